@@ -1,0 +1,264 @@
+"""Plain CPU oracle for the Introspective Strided Decoding (ISD) verify-and-propose step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(``libisd`` and its Python binding) never imports, links or calls it, and this
+module imports nothing from the product path: the two share no code.
+
+Everything here is float64 numpy evaluated on exactly decoded inputs, written
+as the plain definitions, with no blocking, fusion or reordering.
+
+Sources (cited by page title and section):
+
+* "Introspective Diffusion Language Models | Summary" (greeksharifa.github.io),
+  section 2 "Background and Motivation": the introspective acceptance rate
+  alpha is the mean over the L proposed positions of min(1, p_k(x_k)/q_k(x_k)),
+  where q_k is the distribution that generated x_k and p_k is the causal anchor
+  that scores it once the tokens are revealed.
+* same page, section 3.2 "Introspective Strided Decoding (ISD)": each proposal
+  is kept with probability min(1, p_k(x_k)/q_k(x_k)); at the first rejection a
+  replacement is drawn from the normalised residual max(0, p_k - q_k) and every
+  later proposal is dropped; the mask positions of the same forward pass give
+  the proposals of the next step.
+* same page, section 3.3 "I-DLM Serving Stack": the serving stack proposes by
+  argmax and verifies strictly, so the acceptance test must use the law of the
+  proposal mechanism that was actually used (greedy mode below).
+
+Readings where the pages leave a step open (each one is listed in the design doc):
+
+* draws: one uniform per decision, passed in as an input (``ua`` for the
+  accept test, ``ur`` for the residual draw, ``up`` for each proposal draw);
+  a proposal is accepted iff ``ua < r`` (strict), so r = 1 always accepts;
+* the residual and proposal draws are inverse-CDF draws over ascending vocab
+  index: the token is the smallest i with cum_i > u * Z (cumulative of the
+  weights, Z their total), clamped to the last positive weight when rounding
+  pushes the target past the end;
+* the residual uses ``ur[c, j]`` at the first rejected position j;
+* alpha is averaged over all L positions, not only up to the first rejection;
+* if the proposal probability q_k(x_k) is 0 the ratio is 1 when p_k(x_k) > 0
+  and 0 otherwise; if the residual mass Z is 0 the draw falls back to p_k and
+  the sequence is flagged;
+* no bonus token: a step that accepts all L proposals emits exactly L tokens;
+* greedy mode: argmax of the raw anchor logits with ties to the lowest index,
+  a proposal is accepted iff it equals that argmax, the correction is the
+  anchor argmax at the first mismatch, alpha is the match fraction, and the
+  next proposals are the argmax of the mask-position logits.
+
+Near-tie flags: a decision whose margin (|u - r| for the accept test, distance
+of u to the two cumulative boundaries of the chosen token for a draw) is below
+``TIE_WINDOW`` is reported so that a comparison can leave it out.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+TIE_WINDOW = 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Input decoding
+# ---------------------------------------------------------------------------
+
+def decode_logits(raw: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of a logits buffer.
+
+    ``dtype`` is ``"bf16"`` (raw holds the uint16 bit patterns) or ``"f32"``.
+    A bf16 value is the upper half of the float32 with the same bits.
+    """
+    if dtype == "bf16":
+        bits = np.asarray(raw, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# Distributions
+# ---------------------------------------------------------------------------
+
+def softmax(logits: np.ndarray, temperature: float = 1.0) -> np.ndarray:
+    """softmax(logits / T) along the last axis, in float64.
+
+    -inf logits get probability 0.  NaN or +inf logits, or a row that is all
+    -inf, have no defined distribution and raise ``ValueError``.
+    """
+    a = np.asarray(logits, dtype=np.float64) / float(temperature)
+    if np.isnan(a).any() or np.isposinf(a).any():
+        raise ValueError("logits contain NaN or +inf")
+    m = a.max(axis=-1, keepdims=True)
+    if np.isneginf(m).any():
+        raise ValueError("a logits row is entirely -inf")
+    e = np.exp(a - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def inverse_cdf(weights: np.ndarray, u: np.ndarray):
+    """Inverse-CDF draw over ascending index, batched over leading axes.
+
+    Returns ``(index, margin, total)``: ``index`` is the smallest i with
+    cum_i > u * Z where cum is the running sum of ``weights`` and Z its total;
+    when no such i exists (rounding), the last index with positive weight.
+    ``margin`` is min(|cum_{i-1}/Z - u|, |cum_i/Z - u|) with cum_{-1} = 0.
+    Rows whose total is 0 get index -1 and margin 0.
+    """
+    w = np.asarray(weights, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    cum = np.cumsum(w, axis=-1)
+    total = cum[..., -1]
+    target = u * total
+    idx = np.sum(cum <= target[..., None], axis=-1)
+    V = w.shape[-1]
+    positive = w > 0
+    last_pos = V - 1 - np.argmax(positive[..., ::-1], axis=-1)
+    idx = np.where(idx >= V, last_pos, idx)
+    safe_total = np.where(total > 0, total, 1.0)
+    i_clip = np.clip(idx, 0, V - 1)
+    cum_i = np.take_along_axis(cum, i_clip[..., None], axis=-1)[..., 0]
+    prev = np.take_along_axis(cum, np.clip(i_clip - 1, 0, V - 1)[..., None], axis=-1)[..., 0]
+    prev = np.where(i_clip == 0, 0.0, prev)
+    margin = np.minimum(np.abs(prev / safe_total - u), np.abs(cum_i / safe_total - u))
+    idx = np.where(total > 0, idx, -1)
+    margin = np.where(total > 0, margin, 0.0)
+    return idx.astype(np.int64), margin, total
+
+
+def accept_ratio(px: np.ndarray, qx: np.ndarray) -> np.ndarray:
+    """min(1, px/qx), with the q(x) = 0 convention (1 if px > 0 else 0)."""
+    px = np.asarray(px, dtype=np.float64)
+    qx = np.asarray(qx, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.minimum(1.0, px / np.where(qx > 0, qx, 1.0))
+    return np.where(qx > 0, r, np.where(px > 0, 1.0, 0.0))
+
+
+# ---------------------------------------------------------------------------
+# Sample mode
+# ---------------------------------------------------------------------------
+
+def verify_sample(p, q, x, ua, ur, temperature=1.0):
+    """ISD verification of proposals ``x`` against the anchor, batched.
+
+    p, q: [B, L, V] logits (anchor rows, proposal rows that generated x);
+    x: [B, L] int proposals; ua, ur: [B, L] uniforms in [0, 1).
+    Returns a dict of per-sequence arrays:
+      accept_len [B], out_tokens [B, L] (-1 padded), n_emitted [B],
+      p_x, q_x, ratio [B, L], alpha [B], decision_margin [B] (smallest
+      |ua - r| over k <= j), resid_margin [B] (inf when nothing was drawn),
+      resid_fallback [B] (residual mass was 0), flagged [B] and
+      resid_flagged [B].
+    """
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    x = np.asarray(x, dtype=np.int64)
+    ua = np.asarray(ua, dtype=np.float64)
+    ur = np.asarray(ur, dtype=np.float64)
+    B, L, V = p.shape
+
+    P = softmax(p, temperature)
+    Q = softmax(q, temperature)
+    px = np.take_along_axis(P, x[..., None], axis=-1)[..., 0]
+    qx = np.take_along_axis(Q, x[..., None], axis=-1)[..., 0]
+    r = accept_ratio(px, qx)
+    alpha = r.mean(axis=-1)
+
+    accepted = ua < r
+    rejected = ~accepted
+    j = np.where(rejected.any(axis=-1), np.argmax(rejected, axis=-1), L)
+
+    ks = np.arange(L)[None, :]
+    considered = ks <= j[:, None]
+    gap = np.where(considered, np.abs(ua - r), np.inf)
+    decision_margin = gap.min(axis=-1)
+
+    out = np.where(ks < j[:, None], x, -1)
+    n_emitted = j + (j < L)
+    resid_margin = np.full(B, np.inf)
+    resid_fallback = np.zeros(B, dtype=bool)
+
+    rows = np.nonzero(j < L)[0]
+    if rows.size:
+        jj = j[rows]
+        Pj = P[rows, jj]
+        Qj = Q[rows, jj]
+        R = np.maximum(0.0, Pj - Qj)
+        Z = R.sum(axis=-1)
+        resid_fallback[rows] = Z == 0
+        W = np.where((Z == 0)[:, None], Pj, R)
+        tok, margin, _ = inverse_cdf(W, ur[rows, jj])
+        out[rows, jj] = tok
+        resid_margin[rows] = np.where(Z == 0, 0.0, margin)
+
+    flagged = decision_margin < TIE_WINDOW
+    resid_flagged = (resid_margin < TIE_WINDOW) | resid_fallback
+    return dict(accept_len=j, out_tokens=out, n_emitted=n_emitted, p_x=px, q_x=qx,
+                ratio=r, alpha=alpha, decision_margin=decision_margin,
+                resid_margin=resid_margin, resid_fallback=resid_fallback,
+                flagged=flagged, resid_flagged=resid_flagged)
+
+
+def propose_sample(qn, up, temperature=1.0):
+    """Draw the next proposals from the mask-position logits, batched.
+
+    qn: [..., V] logits; up: [...] uniforms.  Returns ``(tokens, prob,
+    margin, flagged)`` where prob is softmax(qn/T) at the drawn token.
+    """
+    Qn = softmax(qn, temperature)
+    tok, margin, _ = inverse_cdf(Qn, up)
+    prob = np.take_along_axis(Qn, tok[..., None], axis=-1)[..., 0]
+    return tok, prob, margin, margin < TIE_WINDOW
+
+
+def alpha_sample(p, q, x, temperature=1.0):
+    """Introspective acceptance rate per sequence, [B, L, V] -> [B]."""
+    P = softmax(p, temperature)
+    Q = softmax(q, temperature)
+    x = np.asarray(x, dtype=np.int64)
+    px = np.take_along_axis(P, x[..., None], axis=-1)[..., 0]
+    qx = np.take_along_axis(Q, x[..., None], axis=-1)[..., 0]
+    return accept_ratio(px, qx).mean(axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Greedy (strict, argmax-proposal) mode
+# ---------------------------------------------------------------------------
+
+def argmax_first(logits):
+    """Index of the largest logit along the last axis, lowest index on ties."""
+    return np.argmax(np.asarray(logits, dtype=np.float64), axis=-1).astype(np.int64)
+
+
+def verify_greedy(p, x):
+    """Strict verification: accept x_k iff it equals argmax p_k.
+
+    p: [B, L, V] logits; x: [B, L].  The correction at the first mismatch is
+    the anchor argmax there.  Returns the same keys as ``verify_sample`` for
+    tokens and counts, with ``alpha`` the match fraction.
+    """
+    x = np.asarray(x, dtype=np.int64)
+    B, L, _ = np.shape(p)
+    g = argmax_first(p)
+    match = x == g
+    mismatch = ~match
+    j = np.where(mismatch.any(axis=-1), np.argmax(mismatch, axis=-1), L)
+    ks = np.arange(L)[None, :]
+    out = np.where(ks < j[:, None], x, -1)
+    rows = np.nonzero(j < L)[0]
+    out[rows, j[rows]] = g[rows, j[rows]]
+    return dict(accept_len=j, out_tokens=out, n_emitted=j + (j < L),
+                argmax=g, alpha=match.mean(axis=-1))
+
+
+def propose_greedy(qn):
+    """Next proposals by argmax of the mask-position logits."""
+    return argmax_first(qn)
+
+
+# ---------------------------------------------------------------------------
+# LM head (logits GEMM feeding the step)
+# ---------------------------------------------------------------------------
+
+def lm_head(h, w):
+    """logits = h @ w in float64 on exactly decoded inputs."""
+    return np.asarray(h, dtype=np.float64) @ np.asarray(w, dtype=np.float64)
