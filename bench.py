@@ -1,0 +1,236 @@
+"""Benchmark of the fused ISD verify-and-propose step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one isd_step launch over one batch: verification of C*L proposals
+(anchor rows p and proposal rows q) plus the draw of the next C*L proposals
+(mask rows qn).  The serving workload (C=64, L=8, V=151936, bf16 logits, T=1)
+is the default.  Inputs are resident in HBM before timing; steps cycle over
+`--sets` distinct logits sets (each larger than the 256 MB Infinity Cache)
+with fresh uniforms every step.  Prints one JSON line.
+
+Reported:
+  value      verified positions per second = C*L / wall-clock time per step
+  roofline   the step kernel against the HBM peak: algorithmic bytes per
+             launch (every logit read once: 3*C*L*V*2 B) over the kernel's
+             mean duration, timed with events on its stream
+  cpu_baseline  the CPU oracle on a bounded sample of the same inputs,
+             across the host's cores (process pool), in positions per second
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_isd_step_serving.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "speculative_verification_amd", "csrc", f)
+                  for f in ("isd_step.hip", "isd_internal.h", "isd_api.hip")]
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 5])
+    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU oracle sample")
+    ap.add_argument("--segments", type=int, default=0)
+    ap.add_argument("--resid-segments", type=int, default=0)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (forked workers share the host inputs copy-on-write)
+# ---------------------------------------------------------------------------
+
+_HOST = {}
+
+
+def _oracle_seq(args):
+    os.environ["OMP_NUM_THREADS"] = "1"
+    from oracle import isd_oracle as O
+    s, c, dtype, mode, T = args
+    d = _HOST["sets"][s]
+    p = O.decode_logits(d["p"][c:c + 1], dtype)
+    qn = O.decode_logits(d["qn"][c:c + 1], dtype)
+    if mode == "greedy":
+        O.verify_greedy(p, d["x"][c:c + 1])
+        O.propose_greedy(qn)
+    else:
+        q = O.decode_logits(d["q"][c:c + 1], dtype)
+        O.verify_sample(p, q, d["x"][c:c + 1], d["ua"][c:c + 1], d["ur"][c:c + 1], T)
+        O.propose_sample(qn, d["up"][c:c + 1], T)
+    return 1
+
+
+def cpu_baseline(host_sets, cfg, target_s):
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    _HOST["sets"] = host_sets
+    C, L = cfg["C"], cfg["L"]
+    jobs_all = [(s, c, cfg["dtype"], cfg["mode"], cfg["T"])
+                for s in range(len(host_sets)) for c in range(C)]
+    # calibrate on one sequence, then size the sample to about target_s of wall time
+    t0 = time.perf_counter()
+    _oracle_seq(jobs_all[0])
+    per_seq = time.perf_counter() - t0
+    n = int(max(cores, min(len(jobs_all) * 4, target_s * cores / max(per_seq, 1e-6))))
+    jobs = [jobs_all[i % len(jobs_all)] for i in range(n)]
+    with mp.get_context("fork").Pool(cores) as pool:
+        t0 = time.perf_counter()
+        done = sum(pool.imap_unordered(_oracle_seq, jobs, chunksize=1))
+        wall = time.perf_counter() - t0
+    return dict(value=round(done * L / wall, 3), unit="positions/s", cores=cores, kind="oracle",
+                sample=f"{done} sequences ({done * L} positions) of the timed workload's "
+                       f"resident input sets, fp64 numpy oracle, one process per core, "
+                       f"{wall:.1f} s wall")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps(dict(error="this build runs on one GPU: the ISD step is measured "
+                                    "on a single MI355X; multi-GPU runs are not supported",
+                              n_gpus=args.gpus)))
+        sys.exit(2)
+
+    import torch
+
+    import speculative_verification_amd as isd
+    from isd_inputs import CONFIGS, gen_step, gen_uniforms
+
+    cfg = CONFIGS[args.config]
+    C, L, V, mode, T = cfg["C"], cfg["L"], cfg["V"], cfg["mode"], cfg["T"]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    isd.set_tuning(args.segments, args.resid_segments, 0)
+
+    nsets = max(1, args.sets)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    t_gen = time.perf_counter()
+    host_sets, dev_sets = [], []
+    for s in range(nsets):
+        d = gen_step(args.config, s, workers=workers)
+        host_sets.append(d)
+        t = {}
+        for key in ("p", "q", "qn"):
+            t[key] = torch.from_numpy(d[key].view(np.int16)).to(dev).view(torch.bfloat16)
+        t["x"] = torch.from_numpy(d["x"]).to(dev)
+        dev_sets.append(t)
+    total = args.warmup + args.steps
+    uni = torch.from_numpy(gen_uniforms(args.config, total)).to(dev)   # [steps, 3, C, L]
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+    print(f"# inputs ready: {nsets} sets x {3 * C * L * V * 2 / 1e6:.1f} MB, {gen_s:.1f} s",
+          file=sys.stderr, flush=True)
+
+    d0 = dev_sets[0]
+    call = isd.StepCall(d0["p"], d0["q"], d0["x"], uni[0, 0], uni[0, 1], d0["qn"], uni[0, 2],
+                        mode=mode, temperature=T)
+
+    def bind(i):
+        t = dev_sets[i % nsets]
+        call.bind(t["p"], t["q"], t["x"], uni[i, 0], uni[i, 1], t["qn"], uni[i, 2])
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        bind(i)
+        call()
+    torch.cuda.synchronize()
+    isd.check_device_error(call.ws)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    accept = torch.empty((args.steps, C), dtype=torch.int32, device=dev)
+    alphas = torch.empty((args.steps, C), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        bind(args.warmup + i)
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+        accept[i].copy_(call.out["accept_len"], non_blocking=True)
+        alphas[i].copy_(call.out["alpha"], non_blocking=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    isd.check_device_error(call.ws)
+
+    kernel_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = wall * 1e3 / args.steps
+    positions = C * L
+    bytes_alg = 3 * C * L * V * 2
+    kernel_mean_s = float(kernel_ms.mean()) * 1e-3
+    achieved = bytes_alg / kernel_mean_s / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_digest") == kernel_digest() and tr.get("config") == args.config:
+            traffic = tr.get("bytes_per_launch")
+
+    acc = accept.cpu().numpy()
+    result = dict(
+        metric="ISD verified positions/sec at C=64,L=8,V=151936 bf16; achieved HBM GB/s"
+        if args.config == 2 else f"ISD verified positions/sec ({cfg['name']} workload)",
+        value=round(positions / (ms_per_step * 1e-3), 1),
+        unit="positions/s",
+        n_gpus=1,
+        steps=args.steps,
+        warmup=args.warmup,
+        ms_per_step=round(ms_per_step, 5),
+        higher_is_better=True,
+        scaling="weak",
+        vs_baseline=None,
+        dtype="f32",
+        data="synthetic",
+        config=dict(workload=f"{cfg['name']} ISD step: C={C}, L={L}, V={V}, bf16 logits, "
+                             f"{'greedy' if mode == 'greedy' else f'T={T}'}",
+                    C=C, L=L, V=V, logits_dtype="bf16", mode=mode, input_sets=nsets,
+                    parallelism="single GPU"),
+        roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic),
+        hbm_gbs_wall=round(bytes_alg / (ms_per_step * 1e-3) / 1e9, 1),
+        kernel_us=dict(mean=round(float(kernel_ms.mean()) * 1e3, 2),
+                       median=round(float(np.median(kernel_ms)) * 1e3, 2),
+                       min=round(float(kernel_ms.min()) * 1e3, 2)),
+        bytes_per_step=bytes_alg,
+        accept_len_mean=round(float(acc.mean()), 4),
+        alpha_mean=round(float(alphas.mean().item()), 5),
+    )
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(host_sets, cfg, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * libisd -- Introspective Strided Decoding (ISD) verify-and-propose step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The step follows "Introspective Diffusion Language Models | Summary"
+ * (greeksharifa.github.io):
+ *   - section 2 (Background and Motivation) defines the introspective
+ *     acceptance rate alpha: the mean over the L proposed positions of
+ *     min(1, p_k(x_k) / q_k(x_k)), with q_k the law that generated x_k and
+ *     p_k the causal anchor that scores it;
+ *   - section 3.2 (Introspective Strided Decoding) keeps each proposal with
+ *     probability min(1, p_k(x_k)/q_k(x_k)), replaces the first rejected one by
+ *     a draw from normalize(max(0, p_k - q_k)), drops every later proposal, and
+ *     takes the next proposals from the mask positions of the same forward;
+ *   - section 3.3 (I-DLM Serving Stack) proposes by argmax and verifies
+ *     strictly (ISD_MODE_GREEDY).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Logits are row-major [C, L, V] with V innermost and `ld` elements
+ *   between consecutive rows (ld >= V); row (c, k) starts at element
+ *   (c*L + k)*ld.  Token and uniform arrays are dense [C, L] (row-major).
+ *   p_logits[c, k] is the anchor row that scores proposal x[c, k] (the
+ *   next-token logit shift is applied by the caller); q_logits[c, k] is the
+ *   proposal row that generated x[c, k]; qnext_logits[c, k] is the mask row
+ *   whose draw becomes the next proposal at position k.
+ * Memory.  Every pointer argument except `s` is device memory owned by the
+ *   caller; the library never allocates, frees or keeps a pointer.  `s` is a
+ *   host pointer read synchronously.
+ * Workspace.  Size it with isd_workspace_bytes() for the same shape.  It must
+ *   be zero-filled before its first use; every call leaves it zero-filled
+ *   again once its kernels have finished (it holds work counters and
+ *   per-row partial results).  One workspace serves one call at a time:
+ *   calls that share a workspace must be ordered on one stream.
+ * Asynchrony.  Every call validates its arguments on the host, enqueues its
+ *   kernels on `stream` (a hipStream_t; NULL is the null stream) and returns;
+ *   outputs are valid once the stream has reached that point.
+ * Draws.  Randomness is passed in: one uniform in [0, 1) per decision.  A
+ *   proposal is kept iff u_accept < min(1, P(x)/Q(x)).  The residual and the
+ *   proposals are inverse-CDF draws over ascending vocab index: the token is
+ *   the smallest i whose running weight sum exceeds u * (total weight).
+ * Precision.  Streaming sums are fp32 per 32-element lane block, accumulated
+ *   in fp64; decisions use fp64 ratios.  Results match an exact fp64
+ *   evaluation up to ~1e-7 relative, so only draws within ~1e-6 of a
+ *   decision boundary can come out differently.
+ * Errors.  On a non-OK status nothing has been enqueued and no output or
+ *   workspace byte is touched; isd_last_error() then describes the problem.
+ *     ISD_ERR_ARG          bad shape (C < 1, L not in [1, 64], V < 1, ld < V),
+ *                          a required NULL pointer, a base not aligned to its
+ *                          element size, or T <= 0 / non-finite in sample mode
+ *     ISD_ERR_UNSUPPORTED  unknown dtype or mode
+ *     ISD_ERR_WORKSPACE    ws_bytes smaller than isd_workspace_bytes()
+ *     ISD_ERR_DEVICE       a HIP call failed (text in isd_last_error())
+ *   Out-of-range proposal ids and NaN/+inf logits are undefined input; the
+ *   kernels never read out of bounds because of them, and record them in a
+ *   device error word that isd_check_device_error() reports.
+ */
+#ifndef ISD_H
+#define ISD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ISD_OK = 0,
+    ISD_ERR_ARG = 1,
+    ISD_ERR_UNSUPPORTED = 2,
+    ISD_ERR_WORKSPACE = 3,
+    ISD_ERR_DEVICE = 4
+} isd_status_t;
+
+typedef enum { ISD_DTYPE_BF16 = 0, ISD_DTYPE_F32 = 1 } isd_dtype_t;
+
+/* ISD_MODE_SAMPLE: probabilistic acceptance with residual correction
+ * (section 3.2).  ISD_MODE_GREEDY: argmax proposals verified strictly
+ * (section 3.3): x_k is kept iff it equals argmax p_k (ties to the lowest
+ * index, raw logits, temperature ignored), the correction is that argmax,
+ * alpha is the match fraction, proposals are argmax of the mask rows, and
+ * q_logits and all uniforms are ignored (may be NULL). */
+typedef enum { ISD_MODE_SAMPLE = 0, ISD_MODE_GREEDY = 1 } isd_mode_t;
+
+typedef struct {
+    int32_t C;           /* concurrent sequences, >= 1 */
+    int32_t L;           /* strided positions per step, 1..64 */
+    int32_t V;           /* vocabulary size, >= 1 */
+    int64_t ld;          /* elements between consecutive logits rows, >= V */
+    int32_t dtype;       /* isd_dtype_t of every logits tensor */
+    int32_t mode;        /* isd_mode_t */
+    float temperature;   /* softmax temperature T > 0 (sample mode) */
+} isd_shape_t;
+
+/* Workspace bytes needed by any call on shape `s`; 0 if `s` is invalid. */
+size_t isd_workspace_bytes(const isd_shape_t *s);
+
+/* Verification of the previous step's proposals (section 3.2; strict
+ * variant section 3.3).
+ *   p_logits, q_logits  [C, L, V] logits (q ignored in greedy mode)
+ *   proposals           [C, L] int32 proposal ids x, in [0, V)
+ *   u_accept, u_resid   [C, L] fp32 uniforms; the residual draw uses
+ *                       u_resid[c, j] at the first rejected position j
+ * outputs (device):
+ *   accept_len [C]      j = number of leading proposals kept (L if none fails)
+ *   out_tokens [C, L]   x[c, 0..j-1], then the correction at j when j < L,
+ *                       then -1
+ *   n_emitted  [C]      j + (j < L); no bonus token is drawn after a full accept
+ *   p_x, q_x   [C, L]   P_k(x_k), Q_k(x_k) (greedy: 1 if x_k matches else 0,
+ *                       and 1); may be NULL
+ *   alpha      [C]      per-sequence alpha over all L positions; may be NULL */
+isd_status_t isd_verify_step(const isd_shape_t *s,
+                             const void *p_logits, const void *q_logits,
+                             const int32_t *proposals,
+                             const float *u_accept, const float *u_resid,
+                             int32_t *accept_len, int32_t *out_tokens, int32_t *n_emitted,
+                             float *p_x, float *q_x, float *alpha,
+                             void *workspace, size_t ws_bytes, void *stream);
+
+/* Next proposals from the mask-position logits (section 3.2, Algorithm 1's
+ * mask positions; greedy: argmax, section 3.3).  All C*L draws are made; a
+ * caller whose step rejected (accept_len < L) discards them.
+ *   qnext_logits [C, L, V]; u_propose [C, L] fp32 (ignored in greedy mode)
+ *   next_tokens  [C, L] int32 out; qnext_x [C, L] fp32 out: the proposal's
+ *   probability under softmax(qnext/T) (greedy: 1); may be NULL */
+isd_status_t isd_propose(const isd_shape_t *s,
+                         const void *qnext_logits, const float *u_propose,
+                         int32_t *next_tokens, float *qnext_x,
+                         void *workspace, size_t ws_bytes, void *stream);
+
+/* The introspective acceptance rate alone (section 2): alpha[c] is the mean
+ * over k of min(1, P_k(x_k)/Q_k(x_k)) (greedy: the match fraction);
+ * alpha_mean [1] is the mean over sequences (may be NULL). */
+isd_status_t isd_alpha(const isd_shape_t *s,
+                       const void *p_logits, const void *q_logits,
+                       const int32_t *proposals,
+                       float *alpha, float *alpha_mean,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/* One fused ISD step: isd_verify_step and isd_propose in one launch, as the
+ * single forward of section 3.2 yields both the anchor rows that verify the
+ * previous proposals and the mask rows that propose the next ones.  Arguments
+ * and outputs are those of the two calls; results are identical to calling
+ * isd_verify_step then isd_propose. */
+isd_status_t isd_step(const isd_shape_t *s,
+                      const void *p_logits, const void *q_logits,
+                      const int32_t *proposals,
+                      const float *u_accept, const float *u_resid,
+                      const void *qnext_logits, const float *u_propose,
+                      int32_t *accept_len, int32_t *out_tokens, int32_t *n_emitted,
+                      float *p_x, float *q_x, float *alpha,
+                      int32_t *next_tokens, float *qnext_x,
+                      void *workspace, size_t ws_bytes, void *stream);
+
+/* Logits projection ahead of the step (the LM head that produces every p and
+ * mask row of the extend forward, section 3.3): logits[M, N] = h[M, K] @
+ * w[K, N], bf16 inputs, fp32 accumulation on the matrix cores, rounded to
+ * bf16 (nearest-even).  All three matrices are dense row-major; requires
+ * K % 64 == 0; M, N >= 1.  No workspace is used (pass NULL, 0). */
+isd_status_t isd_lm_head(const void *h, const void *w, int32_t M, int32_t K, int32_t N,
+                         void *logits, void *workspace, size_t ws_bytes, void *stream);
+
+/* Waits for `stream`, then reads and clears the device error word of
+ * `workspace`.  Returns ISD_OK if no kernel flagged undefined input or an
+ * expired internal wait since the last check, else ISD_ERR_DEVICE with the
+ * flags described by isd_last_error().  After ISD_ERR_DEVICE the workspace
+ * must be zero-filled again before reuse. */
+isd_status_t isd_check_device_error(void *workspace, size_t ws_bytes, void *stream);
+
+/* Tuning knobs, process-wide; 0 restores the automatic choice.
+ *   segments        workgroups sharing one logits row (1..32)
+ *   resid_segments  workgroups sharing one residual row pair (1..64)
+ *   spin_limit      bound on the polls of an internal cross-workgroup wait
+ *                   before it gives up and flags the device error word */
+isd_status_t isd_set_tuning(int32_t segments, int32_t resid_segments, int64_t spin_limit);
+
+/* Thread-local description of the last non-OK status of this thread. */
+const char *isd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISD_H */

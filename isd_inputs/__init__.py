@@ -14,5 +14,6 @@ from .gen import (  # noqa: F401
     gen_head_weights,
     gen_sequence,
     gen_step,
+    gen_uniforms,
     host_bytes_per_step,
 )

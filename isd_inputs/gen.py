@@ -178,6 +178,18 @@ def gen_hidden(cfg_id: int, step: int, cfg: dict | None = None) -> np.ndarray:
                             rng.standard_normal((M, H), dtype=np.float32))
 
 
+def gen_uniforms(cfg_id: int, steps: int, first_step: int = 0, cfg: dict | None = None) -> np.ndarray:
+    """Fresh accept/residual/proposal uniforms for a run of steps that reuse a
+    few resident logits sets: float32 [steps, 3, C, L] in [0, 1), seeded per
+    step with SeedSequence([0x15D, config, step, 0xA11])."""
+    cfg = CONFIGS[cfg_id] if cfg is None else cfg
+    out = np.empty((steps, 3, cfg["C"], cfg["L"]), dtype=np.float32)
+    for i in range(steps):
+        rng = _rng(cfg_id, first_step + i, 0xA11)
+        out[i] = rng.random((3, cfg["C"], cfg["L"]), dtype=np.float32)
+    return out
+
+
 def host_bytes_per_step(cfg_id: int, cfg: dict | None = None) -> int:
     """Bytes of the three logits tensors of one step."""
     cfg = CONFIGS[cfg_id] if cfg is None else cfg

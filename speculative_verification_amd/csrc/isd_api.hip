@@ -1,0 +1,378 @@
+// C-ABI entry points of libisd: argument validation, workspace layout, work
+// decomposition and kernel launches.  Declarations and the contract are in
+// include/isd.h.
+
+#include "isd.h"
+#include "isd_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+namespace isd {
+namespace {
+
+thread_local char g_err[512] = "";
+
+isd_status_t fail(isd_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+std::atomic<int> g_segments{0};
+std::atomic<int> g_resid_segments{0};
+std::atomic<long long> g_spin_limit{0};
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+isd_status_t check_shape(const isd_shape_t *s, bool need_temperature) {
+    if (!s) return fail(ISD_ERR_ARG, "shape pointer is NULL");
+    if (s->dtype != ISD_DTYPE_BF16 && s->dtype != ISD_DTYPE_F32)
+        return fail(ISD_ERR_UNSUPPORTED, "unknown dtype %d", (int)s->dtype);
+    if (s->mode != ISD_MODE_SAMPLE && s->mode != ISD_MODE_GREEDY)
+        return fail(ISD_ERR_UNSUPPORTED, "unknown mode %d", (int)s->mode);
+    if (s->C < 1) return fail(ISD_ERR_ARG, "C must be >= 1 (got %d)", (int)s->C);
+    if (s->L < 1 || s->L > kMaxL) return fail(ISD_ERR_ARG, "L must be in [1, 64] (got %d)", (int)s->L);
+    if (s->V < 1) return fail(ISD_ERR_ARG, "V must be >= 1 (got %d)", (int)s->V);
+    if (s->ld < (int64_t)s->V) return fail(ISD_ERR_ARG, "ld (%lld) must be >= V (%d)", (long long)s->ld, (int)s->V);
+    const long long rows = (long long)s->C * s->L;
+    if (rows > (1LL << 24)) return fail(ISD_ERR_ARG, "C*L too large (%lld)", rows);
+    if (need_temperature && s->mode == ISD_MODE_SAMPLE &&
+        !(isfinite(s->temperature) && s->temperature > 0.0f))
+        return fail(ISD_ERR_ARG, "temperature must be finite and > 0 in sample mode");
+    return ISD_OK;
+}
+
+size_t elem_size(const isd_shape_t *s) { return s->dtype == ISD_DTYPE_BF16 ? 2 : 4; }
+
+isd_status_t check_ptr(const void *p, const char *name, size_t align) {
+    if (!p) return fail(ISD_ERR_ARG, "%s is NULL", name);
+    if (((uintptr_t)p) % align) return fail(ISD_ERR_ARG, "%s is not %zu-byte aligned", name, align);
+    return ISD_OK;
+}
+
+#define ISD_TRY(expr)                      \
+    do {                                   \
+        isd_status_t st_ = (expr);         \
+        if (st_ != ISD_OK) return st_;     \
+    } while (0)
+
+bool vec_ok(const isd_shape_t *s, const void *a, const void *b, const void *c) {
+    const size_t es = elem_size(s);
+    if (((size_t)s->ld * es) % 16) return false;
+    for (const void *p : {a, b, c})
+        if (p && ((uintptr_t)p) % 16) return false;
+    return true;
+}
+
+struct Plan {
+    bool verify = false, propose = false, residual = false, verify_outputs = false;
+};
+
+isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *workspace,
+                 size_t ws_bytes, void *stream) {
+    const WorkspaceLayout lay = workspace_layout(s->C, s->L, s->V);
+    if (!workspace) return fail(ISD_ERR_ARG, "workspace is NULL");
+    if (((uintptr_t)workspace) % 256) return fail(ISD_ERR_ARG, "workspace is not 256-byte aligned");
+    if (ws_bytes < lay.total)
+        return fail(ISD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, lay.total);
+
+    const int C = s->C, L = s->L, V = s->V;
+    const bool greedy = s->mode == ISD_MODE_GREEDY;
+    a.C = C;
+    a.L = L;
+    a.V = V;
+    a.ld = (long long)s->ld;
+    a.k2 = greedy ? 1.0f : (float)(1.4426950408889634 / (double)s->temperature);
+    a.ws = workspace_at(workspace, lay);
+    a.tiles_row = ceil_div(V, kTileElems);
+
+    // rows streamed in this launch
+    const long long rows = (plan.verify ? (long long)C * L * (greedy ? 1 : 2) : 0) +
+                           (plan.propose ? (long long)C * L : 0);
+    int S = g_segments.load();
+    if (S <= 0) {
+        // enough workgroups to keep every CU streaming several rows at once
+        const long long want = 8LL * cu_count();
+        S = (int)((want + rows - 1) / rows);
+    }
+    S = max(1, min(S, min(lay.smax, a.tiles_row)));
+    a.tps = ceil_div(a.tiles_row, S);
+    a.S = ceil_div(a.tiles_row, a.tps);
+
+    int Sr = g_resid_segments.load();
+    if (Sr <= 0) Sr = ceil_div(a.tiles_row, 2 * kWavesPerGroup);
+    Sr = max(1, min(Sr, min(kMaxResidSegments, a.tiles_row)));
+    a.tpsr = ceil_div(a.tiles_row, Sr);
+    a.Sr = ceil_div(a.tiles_row, a.tpsr);
+
+    a.rows_pq = plan.verify ? (greedy ? L : 2 * L) : 0;
+    a.n_pq = C * a.rows_pq * a.S;
+    a.q_blk = plan.propose ? L * a.S : 0;
+    a.r_blk = (plan.residual && !greedy) ? a.Sr : 0;
+    const long long n_items = (long long)a.n_pq + (long long)C * (a.q_blk + a.r_blk);
+    if (n_items <= 0 || n_items >= (1LL << 31))
+        return fail(ISD_ERR_ARG, "work decomposition out of range (%lld items)", n_items);
+    a.n_items = (int)n_items;
+    a.verify_outputs = plan.verify_outputs ? 1 : 0;
+    const long long spin = g_spin_limit.load();
+    a.spin_limit = spin > 0 ? (uint32_t)(spin < (long long)UINT32_MAX ? spin : (long long)UINT32_MAX)
+                            : kDefaultSpinLimit;
+
+    const bool vec = vec_ok(s, a.p, a.q, a.qn);
+    const hipError_t e = launch_step(a, s->dtype, s->mode, vec, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return ISD_OK;
+}
+
+StepArgs blank_args() {
+    StepArgs a;
+    memset(&a, 0, sizeof(a));
+    return a;
+}
+
+}  // namespace
+
+WorkspaceLayout workspace_layout(int C, int L, int V) {
+    WorkspaceLayout lay;
+    const size_t CL = (size_t)C * L;
+    const int tiles_row = ceil_div(V, kTileElems);
+    lay.smax = min(kMaxSegments, tiles_row);
+    size_t off = align256(sizeof(Control));
+    const size_t cs = sizeof(uint32_t) * kCounterStride;
+    lay.off_seq_cnt = off;
+    off = align256(off + cs * C);
+    lay.off_res_cnt = off;
+    off = align256(off + cs * C);
+    lay.off_flag = off;
+    off = align256(off + cs * C);
+    lay.off_row_cnt = off;
+    off = align256(off + cs * CL);
+    lay.off_seg = off;
+    off = align256(off + sizeof(SegRec) * 2 * CL * lay.smax);
+    lay.off_tiles = off;
+    off = align256(off + sizeof(TileRec) * CL * tiles_row);
+    lay.off_rtiles = off;
+    off = align256(off + sizeof(ResTile) * (size_t)C * tiles_row);
+    lay.off_info = off;
+    off = align256(off + sizeof(SeqInfo) * C);
+    lay.total = off;
+    return lay;
+}
+
+Workspace workspace_at(void *base, const WorkspaceLayout &lay) {
+    char *b = static_cast<char *>(base);
+    Workspace w;
+    w.ctl = reinterpret_cast<Control *>(b);
+    w.seq_cnt = reinterpret_cast<uint32_t *>(b + lay.off_seq_cnt);
+    w.res_cnt = reinterpret_cast<uint32_t *>(b + lay.off_res_cnt);
+    w.flag = reinterpret_cast<uint32_t *>(b + lay.off_flag);
+    w.row_cnt = reinterpret_cast<uint32_t *>(b + lay.off_row_cnt);
+    w.seg = reinterpret_cast<SegRec *>(b + lay.off_seg);
+    w.arg = reinterpret_cast<ArgRec *>(b + lay.off_seg);
+    w.tiles = reinterpret_cast<TileRec *>(b + lay.off_tiles);
+    w.rtiles = reinterpret_cast<ResTile *>(b + lay.off_rtiles);
+    w.info = reinterpret_cast<SeqInfo *>(b + lay.off_info);
+    return w;
+}
+
+}  // namespace isd
+
+using namespace isd;
+
+extern "C" {
+
+size_t isd_workspace_bytes(const isd_shape_t *s) {
+    if (check_shape(s, false) != ISD_OK) return 0;
+    return workspace_layout(s->C, s->L, s->V).total;
+}
+
+isd_status_t isd_verify_step(const isd_shape_t *s, const void *p_logits, const void *q_logits,
+                             const int32_t *proposals, const float *u_accept, const float *u_resid,
+                             int32_t *accept_len, int32_t *out_tokens, int32_t *n_emitted,
+                             float *p_x, float *q_x, float *alpha, void *workspace,
+                             size_t ws_bytes, void *stream) {
+    ISD_TRY(check_shape(s, true));
+    const size_t es = elem_size(s);
+    const bool sample = s->mode == ISD_MODE_SAMPLE;
+    ISD_TRY(check_ptr(p_logits, "p_logits", es));
+    if (sample) {
+        ISD_TRY(check_ptr(q_logits, "q_logits", es));
+        ISD_TRY(check_ptr(u_accept, "u_accept", 4));
+        ISD_TRY(check_ptr(u_resid, "u_resid", 4));
+    }
+    ISD_TRY(check_ptr(proposals, "proposals", 4));
+    ISD_TRY(check_ptr(accept_len, "accept_len", 4));
+    ISD_TRY(check_ptr(out_tokens, "out_tokens", 4));
+    ISD_TRY(check_ptr(n_emitted, "n_emitted", 4));
+    StepArgs a = blank_args();
+    a.p = p_logits;
+    a.q = sample ? q_logits : nullptr;
+    a.x = proposals;
+    a.ua = sample ? u_accept : nullptr;
+    a.ur = sample ? u_resid : nullptr;
+    a.accept_len = accept_len;
+    a.out_tokens = out_tokens;
+    a.n_emitted = n_emitted;
+    a.p_x = p_x;
+    a.q_x = q_x;
+    a.alpha = alpha;
+    Plan plan;
+    plan.verify = plan.residual = plan.verify_outputs = true;
+    return run(s, plan, a, workspace, ws_bytes, stream);
+}
+
+isd_status_t isd_propose(const isd_shape_t *s, const void *qnext_logits, const float *u_propose,
+                         int32_t *next_tokens, float *qnext_x, void *workspace, size_t ws_bytes,
+                         void *stream) {
+    ISD_TRY(check_shape(s, true));
+    const bool sample = s->mode == ISD_MODE_SAMPLE;
+    ISD_TRY(check_ptr(qnext_logits, "qnext_logits", elem_size(s)));
+    if (sample) ISD_TRY(check_ptr(u_propose, "u_propose", 4));
+    ISD_TRY(check_ptr(next_tokens, "next_tokens", 4));
+    StepArgs a = blank_args();
+    a.qn = qnext_logits;
+    a.up = sample ? u_propose : nullptr;
+    a.next_tokens = next_tokens;
+    a.qnext_x = qnext_x;
+    Plan plan;
+    plan.propose = true;
+    return run(s, plan, a, workspace, ws_bytes, stream);
+}
+
+isd_status_t isd_alpha(const isd_shape_t *s, const void *p_logits, const void *q_logits,
+                       const int32_t *proposals, float *alpha, float *alpha_mean, void *workspace,
+                       size_t ws_bytes, void *stream) {
+    ISD_TRY(check_shape(s, true));
+    const bool sample = s->mode == ISD_MODE_SAMPLE;
+    ISD_TRY(check_ptr(p_logits, "p_logits", elem_size(s)));
+    if (sample) ISD_TRY(check_ptr(q_logits, "q_logits", elem_size(s)));
+    ISD_TRY(check_ptr(proposals, "proposals", 4));
+    ISD_TRY(check_ptr(alpha, "alpha", 4));
+    StepArgs a = blank_args();
+    a.p = p_logits;
+    a.q = sample ? q_logits : nullptr;
+    a.x = proposals;
+    a.alpha = alpha;
+    a.alpha_mean = alpha_mean;
+    Plan plan;
+    plan.verify = true;
+    return run(s, plan, a, workspace, ws_bytes, stream);
+}
+
+isd_status_t isd_step(const isd_shape_t *s, const void *p_logits, const void *q_logits,
+                      const int32_t *proposals, const float *u_accept, const float *u_resid,
+                      const void *qnext_logits, const float *u_propose, int32_t *accept_len,
+                      int32_t *out_tokens, int32_t *n_emitted, float *p_x, float *q_x,
+                      float *alpha, int32_t *next_tokens, float *qnext_x, void *workspace,
+                      size_t ws_bytes, void *stream) {
+    ISD_TRY(check_shape(s, true));
+    const size_t es = elem_size(s);
+    const bool sample = s->mode == ISD_MODE_SAMPLE;
+    ISD_TRY(check_ptr(p_logits, "p_logits", es));
+    ISD_TRY(check_ptr(qnext_logits, "qnext_logits", es));
+    if (sample) {
+        ISD_TRY(check_ptr(q_logits, "q_logits", es));
+        ISD_TRY(check_ptr(u_accept, "u_accept", 4));
+        ISD_TRY(check_ptr(u_resid, "u_resid", 4));
+        ISD_TRY(check_ptr(u_propose, "u_propose", 4));
+    }
+    ISD_TRY(check_ptr(proposals, "proposals", 4));
+    ISD_TRY(check_ptr(accept_len, "accept_len", 4));
+    ISD_TRY(check_ptr(out_tokens, "out_tokens", 4));
+    ISD_TRY(check_ptr(n_emitted, "n_emitted", 4));
+    ISD_TRY(check_ptr(next_tokens, "next_tokens", 4));
+    StepArgs a = blank_args();
+    a.p = p_logits;
+    a.q = sample ? q_logits : nullptr;
+    a.qn = qnext_logits;
+    a.x = proposals;
+    a.ua = sample ? u_accept : nullptr;
+    a.ur = sample ? u_resid : nullptr;
+    a.up = sample ? u_propose : nullptr;
+    a.accept_len = accept_len;
+    a.out_tokens = out_tokens;
+    a.n_emitted = n_emitted;
+    a.p_x = p_x;
+    a.q_x = q_x;
+    a.alpha = alpha;
+    a.next_tokens = next_tokens;
+    a.qnext_x = qnext_x;
+    Plan plan;
+    plan.verify = plan.propose = plan.residual = plan.verify_outputs = true;
+    return run(s, plan, a, workspace, ws_bytes, stream);
+}
+
+isd_status_t isd_lm_head(const void *h, const void *w, int32_t M, int32_t K, int32_t N,
+                         void *logits, void *workspace, size_t ws_bytes, void *stream) {
+    (void)workspace;
+    (void)ws_bytes;
+    ISD_TRY(check_ptr(h, "h", 16));
+    ISD_TRY(check_ptr(w, "w", 16));
+    ISD_TRY(check_ptr(logits, "logits", 16));
+    if (M < 1 || N < 1 || K < 1) return fail(ISD_ERR_ARG, "M, K, N must be >= 1");
+    if (K % 64) return fail(ISD_ERR_ARG, "K must be a multiple of 64 (got %d)", (int)K);
+    if (N % 8) return fail(ISD_ERR_ARG, "N must be a multiple of 8 (got %d)", (int)N);
+    const hipError_t e = launch_lm_head(static_cast<const uint16_t *>(h),
+                                        static_cast<const uint16_t *>(w), M, K, N,
+                                        static_cast<uint16_t *>(logits), (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "lm_head launch failed: %s", hipGetErrorString(e));
+    return ISD_OK;
+}
+
+isd_status_t isd_check_device_error(void *workspace, size_t ws_bytes, void *stream) {
+    if (!workspace) return fail(ISD_ERR_ARG, "workspace is NULL");
+    if (ws_bytes < sizeof(Control)) return fail(ISD_ERR_WORKSPACE, "workspace too small");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "stream sync failed: %s", hipGetErrorString(e));
+    Control *ctl = static_cast<Control *>(workspace);
+    uint32_t err = 0;
+    e = hipMemcpy(&err, &ctl->error, sizeof(err), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "reading the error word failed: %s", hipGetErrorString(e));
+    if (!err) return ISD_OK;
+    const uint32_t zero = 0;
+    e = hipMemcpy(&ctl->error, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "clearing the error word failed: %s", hipGetErrorString(e));
+    return fail(ISD_ERR_DEVICE, "device error word 0x%x:%s%s%s", err,
+                (err & kErrBadToken) ? " proposal id out of range;" : "",
+                (err & kErrEmptyRow) ? " logits row without a finite value;" : "",
+                (err & kErrWaitExpired) ? " cross-workgroup wait expired;" : "");
+}
+
+isd_status_t isd_set_tuning(int32_t segments, int32_t resid_segments, int64_t spin_limit) {
+    if (segments < 0 || segments > kMaxSegments)
+        return fail(ISD_ERR_ARG, "segments must be in [0, %d]", kMaxSegments);
+    if (resid_segments < 0 || resid_segments > kMaxResidSegments)
+        return fail(ISD_ERR_ARG, "resid_segments must be in [0, %d]", kMaxResidSegments);
+    if (spin_limit < 0) return fail(ISD_ERR_ARG, "spin_limit must be >= 0");
+    g_segments.store(segments);
+    g_resid_segments.store(resid_segments);
+    g_spin_limit.store(spin_limit);
+    return ISD_OK;
+}
+
+const char *isd_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Internal declarations shared by the ISD step kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace isd {
+
+// Work decomposition.  A "tile" is the contiguous span one wavefront streams
+// per iteration: 4 groups of 64 lanes x 8 elements, group-major, so lane l
+// holds elements g*512 + l*8 + e of the tile.  Each 8-element group is one
+// 16-byte load per lane for bf16 (two for fp32): every wavefront load
+// instruction covers 1 KiB (bf16) of consecutive bytes.
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = kWave * kWavesPerGroup;
+constexpr int kGroupElems = 8;
+constexpr int kGroupsPerTile = 4;
+constexpr int kLaneElems = kGroupElems * kGroupsPerTile;       // 32
+constexpr int kTileElems = kWave * kLaneElems;                 // 2048
+constexpr int kMaxL = 64;
+constexpr int kMaxSegments = 32;
+constexpr int kMaxResidSegments = 64;
+// Completion counters and flags each own a 128-byte line: atomics that share
+// a line serialise at the memory side.
+constexpr int kCounterStride = 32;   // uint32 words
+
+// Device error word bits.
+constexpr uint32_t kErrBadToken = 1u << 0;     // proposal id outside [0, V)
+constexpr uint32_t kErrEmptyRow = 1u << 1;     // a row with no finite logit
+constexpr uint32_t kErrWaitExpired = 1u << 2;  // a cross-workgroup wait gave up
+
+// Workspace records.  Counters and flags return to zero at the end of the
+// launch that uses them.
+struct Control {               // 256 B at offset 0
+    uint32_t reserved[2];
+    uint32_t seq_done;         // sequences whose decision is done (alpha mean)
+    uint32_t error;            // kErr* bits, cleared by isd_check_device_error
+    uint32_t pad[60];
+};
+
+struct SegRec {                // softmax partial of one row segment
+    float ref;                 // integer reference e: terms are 2^(x*k2 - e)
+    float pad;
+    double sum;                // sum of the segment's terms
+};
+
+struct ArgRec {                // argmax partial of one row segment
+    float val;
+    int32_t idx;
+};
+
+struct TileRec {               // mass of one 2048-element tile of a mask row
+    float ref;
+    float sum;                 // sum of 2^(x*k2 - ref) over the tile
+};
+
+struct ResTile {               // masses of one tile of a residual row pair
+    float r;                   // sum of max(0, P - Q)
+    float p;                   // sum of P (used only if the residual is empty)
+};
+
+struct SeqInfo {               // per-sequence decision, read by residual items
+    int32_t j;                 // first rejected position (L if none)
+    float u;                   // u_resid[c, j]
+    float cp, cq;              // references of rows p[c, j], q[c, j]
+    float inv_sp, inv_sq;      // 1 / softmax denominators of those rows
+    float alpha;
+    float pad;
+};
+
+struct Workspace {
+    Control *ctl;
+    uint32_t *seq_cnt;         // [C]     pq items finished per sequence      (strided)
+    uint32_t *res_cnt;         // [C]     residual items finished per sequence (strided)
+    uint32_t *flag;            // [C]     decision published (1) for sequence c (strided)
+    uint32_t *row_cnt;         // [C*L]   mask-row items finished per row      (strided)
+    SegRec *seg;               // [2*C*L*Smax] sample: p rows then q rows
+    ArgRec *arg;               // [2*C*L*Smax] greedy: p rows then mask rows (aliases seg)
+    TileRec *tiles;            // [C*L*tiles_row] mask rows
+    ResTile *rtiles;           // [C*tiles_row]  residual rows
+    SeqInfo *info;             // [C]
+};
+
+struct WorkspaceLayout {
+    size_t off_seq_cnt, off_res_cnt, off_flag, off_row_cnt, off_seg, off_tiles,
+        off_rtiles, off_info, total;
+    int smax;
+};
+
+WorkspaceLayout workspace_layout(int C, int L, int V);
+Workspace workspace_at(void *base, const WorkspaceLayout &lay);
+
+// Everything one launch of the step kernel needs (passed by value).
+struct StepArgs {
+    int C, L, V;
+    long long ld;
+    float k2;                  // log2(e) / T
+    // inputs
+    const void *p, *q, *qn;
+    const int32_t *x;
+    const float *ua, *ur, *up;
+    // outputs (NULL when not requested)
+    int32_t *accept_len, *out_tokens, *n_emitted;
+    float *p_x, *q_x, *alpha, *alpha_mean;
+    int32_t *next_tokens;
+    float *qnext_x;
+    Workspace ws;
+    // decomposition
+    int tiles_row;             // ceil(V / kTileElems)
+    int S, tps;                // segments per streamed row, tiles per segment
+    int Sr, tpsr;              // segments per residual row pair, tiles per segment
+    int rows_pq;               // verify rows per sequence (2L sample, L greedy, 0 none)
+    int n_pq;                  // C * rows_pq * S
+    int q_blk;                 // mask-row items per sequence (L*S or 0)
+    int r_blk;                 // residual items per sequence (Sr or 0)
+    int n_items;
+    int verify_outputs;        // write tokens / counts (0: alpha only)
+    uint32_t spin_limit;
+};
+
+enum Dtype { kBf16 = 0, kF32 = 1 };
+enum Mode { kSample = 0, kGreedy = 1 };
+
+// Launches the step kernel for `a` (dtype/mode select the instantiation).
+hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStream_t stream);
+
+// LM-head GEMM (bf16 in, fp32 accumulate, bf16 out).
+hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, int N,
+                          uint16_t *out, hipStream_t stream);
+
+}  // namespace isd

@@ -1,0 +1,987 @@
+// ISD verify-and-propose step kernels for gfx950.
+//
+// One kernel does the whole step ("Introspective Diffusion Language Models |
+// Summary", section 3.2: verification of the previous proposals and the draw
+// of the next ones come out of one forward).  Workgroup b does work item b,
+// in this order:
+//
+//   [pq items]      for each sequence c, each verify row (anchor p_k and, in
+//                   sample mode, proposal q_k) and each row segment: stream
+//                   the segment once and write its softmax partial (sample)
+//                   or argmax partial (greedy).  The workgroup that finishes
+//                   the last pq item of sequence c takes the decision for c:
+//                   ratios min(1, P(x)/Q(x)) in fp64, the accept test, the
+//                   first rejection j by a wavefront ballot, alpha, and the
+//                   outputs; it then publishes (j, row-j constants).
+//   per sequence c: [mask-row items]  stream a segment of row qn[c, k] and
+//                   record the mass of each 2048-element tile; the last
+//                   segment of the row merges the tile masses, finds the tile
+//                   where the running mass crosses u * S, re-reads that tile
+//                   and picks the token (inverse CDF).
+//                   [residual items]  wait until c's decision is published,
+//                   then stream a segment of rows p[c, j], q[c, j] computing
+//                   max(0, P - Q) per tile; the last one does the inverse-CDF
+//                   draw over the residual the same way.
+//
+// A residual item only waits on pq items, which have smaller workgroup
+// indices.  Each XCD dispatches its share of the grid in increasing index
+// order, so by the time a residual workgroup is resident on an XCD every pq
+// workgroup of that XCD has been dispatched; pq workgroups never wait, so all
+// of them finish and every wait ends.  The wait is still bounded (spin_limit
+// polls) and flags the device error word if it ever gives up.  No global
+// atomic is taken per workgroup: completion is counted per row or sequence.
+//
+// Softmax partials use an integer reference e per wavefront so that
+// rescaling is an exact power of two: terms are 2^(x*k2 - e) with
+// k2 = log2(e)/T, summed in fp32 over each lane's 32 elements of a tile and
+// accumulated in fp64.
+
+#include "isd_internal.h"
+
+#include <math.h>
+
+namespace isd {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// Wavefront primitives
+// ---------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// row_ror:n rotates within each row of 16 lanes; four rotations give every
+// lane its row's result, two cross-row exchanges finish the wavefront.  All
+// lanes end with bitwise-identical results.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0x128>(v));
+    v = fmaxf(v, dpp<0x124>(v));
+    v = fmaxf(v, dpp<0x122>(v));
+    v = fmaxf(v, dpp<0x121>(v));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0x128>(v);
+    v += dpp<0x124>(v);
+    v += dpp<0x122>(v);
+    v += dpp<0x121>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        double n = __shfl_up(v, o);
+        if (lane >= o) v += n;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_first(unsigned long long mask) {
+    return __ffsll((long long)mask) - 1;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 2^n for an integer-valued float n, saturating far below the fp64 range.
+__device__ __forceinline__ double pow2_int(float n) {
+    return ldexp(1.0, (int)fmaxf(n, -2000.0f));
+}
+
+// ---------------------------------------------------------------------------
+// Tile loads
+// ---------------------------------------------------------------------------
+
+template <typename T>
+struct TileRaw {
+    static constexpr int kWords = kLaneElems * (int)sizeof(T) / 4;
+    uint32_t w[kWords];
+};
+
+template <typename T>
+__device__ __forceinline__ uint32_t neg_inf_bits();
+template <>
+__device__ __forceinline__ uint32_t neg_inf_bits<uint16_t>() { return 0xFF80u; }
+template <>
+__device__ __forceinline__ uint32_t neg_inf_bits<float>() { return 0xFF800000u; }
+
+template <typename T>
+__device__ __forceinline__ uint32_t load_bits(const T *p) {
+    if constexpr (sizeof(T) == 2) return (uint32_t)(*reinterpret_cast<const uint16_t *>(p));
+    else return *reinterpret_cast<const uint32_t *>(p);
+}
+
+// Lane `lane`'s 32 elements of tile `tile` of `row`; elements at or past V
+// read as -inf and are never loaded.
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_tile(const T *__restrict__ row, int tile, int V, int lane,
+                                          TileRaw<T> &r) {
+    const long long base = (long long)tile * kTileElems + lane * kGroupElems;
+    const bool full = (long long)(tile + 1) * kTileElems <= (long long)V;
+    if (VEC && full) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(row + base);
+        constexpr int kVecPerGroup = kGroupElems * (int)sizeof(T) / 16;  // 1 (bf16) or 2 (fp32)
+        constexpr int kGroupStride = kWave * kGroupElems * (int)sizeof(T) / 16;
+#pragma unroll
+        for (int g = 0; g < kGroupsPerTile; ++g) {
+#pragma unroll
+            for (int h = 0; h < kVecPerGroup; ++h) {
+                uint4 v = src[g * kGroupStride + h];
+                const int w0 = (g * kVecPerGroup + h) * 4;
+                r.w[w0 + 0] = v.x;
+                r.w[w0 + 1] = v.y;
+                r.w[w0 + 2] = v.z;
+                r.w[w0 + 3] = v.w;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < kGroupsPerTile; ++g) {
+#pragma unroll
+            for (int e = 0; e < kGroupElems; ++e) {
+                const long long i = base + g * (kWave * kGroupElems) + e;
+                const uint32_t b = (i < (long long)V) ? load_bits<T>(row + i) : neg_inf_bits<T>();
+                const int idx = g * kGroupElems + e;
+                if constexpr (sizeof(T) == 2) {
+                    if (idx & 1) r.w[idx >> 1] |= b << 16;
+                    else r.w[idx >> 1] = b;
+                } else {
+                    r.w[idx] = b;
+                }
+            }
+        }
+    }
+}
+
+// Element idx (0..31, group-major) of a lane's tile as fp32.
+template <typename T>
+__device__ __forceinline__ float elem(const TileRaw<T> &r, int idx) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w = r.w[idx >> 1];
+        return (idx & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    } else {
+        return __uint_as_float(r.w[idx]);
+    }
+}
+
+// Vocab index of element idx of lane `lane` in tile `tile`.
+__device__ __forceinline__ long long elem_index(int tile, int lane, int idx) {
+    return (long long)tile * kTileElems + (idx / kGroupElems) * (kWave * kGroupElems) +
+           lane * kGroupElems + (idx % kGroupElems);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_value(const T *row, long long i) {
+    const uint32_t b = load_bits<T>(row + i);
+    if constexpr (sizeof(T) == 2) return __uint_as_float(b << 16);
+    else return __uint_as_float(b);
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack(const TileRaw<T> &r, float (&v)[kLaneElems]) {
+#pragma unroll
+    for (int i = 0; i < kLaneElems; ++i) v[i] = elem<T>(r, i);
+}
+
+__device__ __forceinline__ float max32(const float (&v)[kLaneElems]) {
+    float m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m[i] = fmaxf(v[i], v[i + 16]);
+#pragma unroll
+    for (int s = 8; s >= 1; s >>= 1)
+#pragma unroll
+        for (int i = 0; i < s; ++i) m[i] = fmaxf(m[i], m[i + s]);
+    return m[0];
+}
+
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&e)[N]) {
+#pragma unroll
+    for (int s = N / 2; s >= 1; s >>= 1)
+#pragma unroll
+        for (int i = 0; i < s; ++i) e[i] += e[i + s];
+    return e[0];
+}
+
+// Streams tiles tile_begin + wave, + kWavesPerGroup, ... < tile_end of `row`,
+// keeping the next tile's loads in flight while `f` consumes the current one.
+template <typename T, bool VEC, typename F>
+__device__ __forceinline__ void stream_row(const T *__restrict__ row, int tile_begin, int tile_end,
+                                           int V, int wave, int lane, F &&f) {
+    int t = tile_begin + wave;
+    if (t >= tile_end) return;
+    TileRaw<T> cur;
+    load_tile<T, VEC>(row, t, V, lane, cur);
+    for (;;) {
+        const int tn = t + kWavesPerGroup;
+        const bool more = tn < tile_end;
+        TileRaw<T> nxt;
+        if (more) load_tile<T, VEC>(row, tn, V, lane, nxt);
+        f(cur, t);
+        if (!more) break;
+        cur = nxt;
+        t = tn;
+    }
+}
+
+// Streams the same tiles of two rows together (one tile of each in flight).
+template <typename T, bool VEC, typename F>
+__device__ __forceinline__ void stream_rows2(const T *__restrict__ ra, const T *__restrict__ rb,
+                                             int tile_begin, int tile_end, int V, int wave,
+                                             int lane, F &&f) {
+    for (int t = tile_begin + wave; t < tile_end; t += kWavesPerGroup) {
+        TileRaw<T> ca, cb;
+        load_tile<T, VEC>(ra, t, V, lane, ca);
+        load_tile<T, VEC>(rb, t, V, lane, cb);
+        f(ca, cb, t);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Data exchanged between workgroups of one launch
+// ---------------------------------------------------------------------------
+//
+// Records that one workgroup writes and another reads in the same launch
+// (segment partials, tile masses, the per-sequence decision) are written and
+// read with agent-scope atomic stores and loads, which are coherent across
+// the XCDs and never served from a stale per-XCD L2 line.  Each wave waits
+// for its own record stores to complete (s_waitcnt) before the workgroup
+// barrier; thread 0 then counts the workgroup with one relaxed atomic on a
+// counter that has a 128-byte line to itself.  No agent-scope fence is
+// issued: on this part such a fence writes back or invalidates the L2 and,
+// issued by thousands of workgroups, serialises the launch.
+
+__device__ __forceinline__ void st32(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st64(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld32(const uint32_t *p) {
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld64(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
+    return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+}
+__device__ __forceinline__ uint64_t pack2(float lo, int hi) {
+    return (uint64_t)__float_as_uint(lo) | ((uint64_t)(uint32_t)hi << 32);
+}
+__device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
+__device__ __forceinline__ int hi_i(uint64_t v) { return (int)(uint32_t)(v >> 32); }
+
+__device__ __forceinline__ void st_seg(SegRec *r, float ref, double sum) {
+    st64(reinterpret_cast<uint64_t *>(r), pack2(ref, 0.0f));
+    st64(reinterpret_cast<uint64_t *>(r) + 1, (uint64_t)__double_as_longlong(sum));
+}
+__device__ __forceinline__ void ld_seg(const SegRec *r, float &ref, double &sum) {
+    ref = lo_f(ld64(reinterpret_cast<const uint64_t *>(r)));
+    sum = __longlong_as_double((long long)ld64(reinterpret_cast<const uint64_t *>(r) + 1));
+}
+__device__ __forceinline__ void st_pair(void *r, uint64_t v) { st64(static_cast<uint64_t *>(r), v); }
+__device__ __forceinline__ uint64_t ld_pair(const void *r) {
+    return ld64(static_cast<const uint64_t *>(r));
+}
+
+// Completes this workgroup's share of a unit counted by `counter` (total
+// arrivals `total`).  All threads call it after their record stores; it
+// returns, to every thread, whether this was the last arrival.  The last one
+// resets the counter for the next launch.
+__device__ bool arrive(uint32_t *counter, uint32_t total, int *s_flag) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev + 1 == total;
+        if (last) st32(counter, 0u);
+        *s_flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    const bool last = *s_flag != 0;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return last;
+}
+
+// ---------------------------------------------------------------------------
+// Softmax and argmax partials
+// ---------------------------------------------------------------------------
+
+struct LaneSoftmax {
+    float ref = kNegInf;   // wavefront-uniform
+    double acc = 0.0;      // lane sum relative to 2^ref
+
+    // Folds one tile; returns the lane's fp32 tile sum (0 if nothing finite yet).
+    __device__ __forceinline__ float add(const float (&v)[kLaneElems], float k2) {
+        const float lm = max32(v);
+        if (__ballot(lm * k2 > ref)) {
+            const float nref = ceilf(wave_max(lm) * k2);
+            if (ref != kNegInf) acc *= pow2_int(ref - nref);
+            ref = nref;
+        }
+        if (ref == kNegInf) return 0.0f;
+        float e[kLaneElems];
+#pragma unroll
+        for (int i = 0; i < kLaneElems; ++i) e[i] = fast_exp2(fmaf(v[i], k2, -ref));
+        const float s = tree_sum(e);
+        acc += (double)s;
+        return s;
+    }
+};
+
+// Merges (ref, sum) pairs in index order: ref = max ref, sum rescaled to it.
+__device__ __forceinline__ void merge_refsum(const float *refs, const double *sums, int n,
+                                             float &ref, double &sum) {
+    ref = kNegInf;
+    for (int i = 0; i < n; ++i) ref = fmaxf(ref, refs[i]);
+    sum = 0.0;
+    if (ref == kNegInf) return;
+    for (int i = 0; i < n; ++i)
+        if (refs[i] != kNegInf) sum += sums[i] * pow2_int(refs[i] - ref);
+}
+
+// Merges the n segment records of one row and clears them.
+__device__ __forceinline__ void take_segrecs(SegRec *rec, int n, float &ref, double &sum) {
+    ref = kNegInf;
+    sum = 0.0;
+    for (int i = 0; i < n; ++i) {
+        float r;
+        double s;
+        ld_seg(&rec[i], r, s);
+        if (r == kNegInf) continue;
+        if (r > ref) {
+            if (ref != kNegInf) sum *= pow2_int(ref - r);
+            ref = r;
+        }
+        sum += s * pow2_int(r - ref);
+    }
+    for (int i = 0; i < n; ++i) st_seg(&rec[i], 0.0f, 0.0);
+}
+
+__device__ __forceinline__ bool arg_better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ void wave_argmax(float &bv, int &bi) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (arg_better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+}
+
+// Merges the n argmax records of one row (ties to the lowest index) and clears them.
+__device__ __forceinline__ int take_argrecs(ArgRec *rec, int n) {
+    float bv = kNegInf;
+    int bi = INT_MAX;
+    for (int i = 0; i < n; ++i) {
+        const uint64_t v = ld_pair(&rec[i]);
+        if (arg_better(lo_f(v), hi_i(v), bv, bi)) {
+            bv = lo_f(v);
+            bi = hi_i(v);
+        }
+    }
+    for (int i = 0; i < n; ++i) st_pair(&rec[i], 0);
+    return bi == INT_MAX ? 0 : bi;   // a row of -inf only: index 0, like numpy argmax
+}
+
+// Per-lane running argmax over the tiles a wavefront streams in vocab order;
+// strict '>' keeps the first index of equal maxima.
+template <typename T>
+__device__ __forceinline__ void argmax_tile(const TileRaw<T> &r, int tile, int lane, float &bv,
+                                            int &bi) {
+    float v[kLaneElems];
+    unpack<T>(r, v);
+    const float lm = max32(v);
+    if (__ballot(lm > bv)) {
+        if (lm > bv) {
+            int fi = 0;
+#pragma unroll
+            for (int i = kLaneElems - 1; i >= 0; --i) fi = (v[i] == lm) ? i : fi;
+            bv = lm;
+            bi = (int)elem_index(tile, lane, fi);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Inverse-CDF search (one wavefront)
+// ---------------------------------------------------------------------------
+
+// Finds the first tile whose running mass exceeds `target`, masses given by
+// `mass(t)` for t < n.  Returns the tile and the mass before it, or -1.
+template <typename M>
+__device__ __forceinline__ int find_tile(int n, double target, int lane, M &&mass, double &before) {
+    double base = 0.0;
+    for (int t0 = 0; t0 < n; t0 += kWave) {
+        const int t = t0 + lane;
+        const double m = t < n ? mass(t) : 0.0;
+        const double inc = wave_incl_scan_d(m, lane);
+        const unsigned long long hit = __ballot(t < n && base + inc > target);
+        if (hit) {
+            const int l = wave_first(hit);
+            before = base + __shfl(inc - m, l);
+            return t0 + l;
+        }
+        base += __shfl(inc, kWave - 1);
+    }
+    return -1;
+}
+
+template <typename M>
+__device__ __forceinline__ double total_mass(int n, int lane, M &&mass) {
+    double base = 0.0;
+    for (int t0 = 0; t0 < n; t0 += kWave) {
+        const int t = t0 + lane;
+        const double m = t < n ? mass(t) : 0.0;
+        base += __shfl(wave_incl_scan_d(m, lane), kWave - 1);
+    }
+    return base;
+}
+
+template <typename M>
+__device__ __forceinline__ int last_positive_tile(int n, int lane, M &&mass) {
+    int best = -1;
+    for (int t0 = 0; t0 < n; t0 += kWave) {
+        const int t = t0 + lane;
+        const unsigned long long pos = __ballot(t < n && mass(t) > 0.0);
+        if (pos) best = t0 + 63 - __clzll((long long)pos);
+    }
+    return best;
+}
+
+// Within one tile, finds the first vocab index where before + running weight
+// exceeds target.  weight(i) returns the weight of vocab index i (0 past the
+// end of the row), reading the element from memory: the tile was just
+// streamed, so these are cache hits, and nothing tile-sized stays in
+// registers.  If rounding leaves the target unreached, returns the last index
+// with positive weight (-1 if none).
+template <typename W>
+__device__ __forceinline__ long long search_tile(W &&weight, int tile, int lane, double before,
+                                                 double target) {
+    double run = before;
+#pragma unroll 1
+    for (int g = 0; g < kGroupsPerTile; ++g) {
+        const long long i0 = elem_index(tile, lane, g * kGroupElems);
+        double w[kGroupElems];
+        double lsum = 0.0;
+#pragma unroll
+        for (int e = 0; e < kGroupElems; ++e) {
+            w[e] = weight(i0 + e);
+            lsum += w[e];
+        }
+        const double inc = wave_incl_scan_d(lsum, lane);
+        // each lane finds its own first crossing element
+        double c = run + (inc - lsum);
+        int first = -1;
+#pragma unroll
+        for (int e = 0; e < kGroupElems; ++e) {
+            c += w[e];
+            if (first < 0 && c > target) first = e;
+        }
+        const unsigned long long hit = __ballot(first >= 0);
+        if (hit) {
+            const int l = wave_first(hit);
+            const int e = __shfl(first, l);
+            return elem_index(tile, l, g * kGroupElems + e);
+        }
+        run += __shfl(inc, kWave - 1);
+    }
+    long long last = -1;
+#pragma unroll 1
+    for (int g = 0; g < kGroupsPerTile; ++g) {
+        const long long i0 = elem_index(tile, lane, g * kGroupElems);
+#pragma unroll
+        for (int e = 0; e < kGroupElems; ++e)
+            if (weight(i0 + e) > 0.0) last = i0 + e > last ? i0 + e : last;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const long long ol = __shfl_xor(last, o);
+        last = ol > last ? ol : last;
+    }
+    return last;
+}
+
+// ---------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------
+
+struct Shared {
+    int flag;
+    float refs[kWavesPerGroup];
+    double sums[kWavesPerGroup];
+    float vals[kWavesPerGroup];
+    int idxs[kWavesPerGroup];
+    SeqInfo info;
+};
+
+__device__ __forceinline__ uint32_t *counter(uint32_t *base, int i) {
+    return base + (size_t)i * kCounterStride;
+}
+
+// Decision for sequence c from its merged verify rows (wavefront 0 of the
+// workgroup that finished the sequence's last verify segment).
+template <typename T, int MODE>
+__device__ void decide(const StepArgs &a, int c, int lane) {
+    const int L = a.L;
+    const int CL = a.C * L;
+    const bool valid = lane < L;
+    const int kk = valid ? lane : 0;
+    const int xk = valid ? a.x[c * L + kk] : 0;
+    const bool bad = valid && (xk < 0 || xk >= a.V);
+    if (bad) atomicOr(&a.ws.ctl->error, kErrBadToken);
+    float alpha;
+
+    if (MODE == kSample) {
+        float cp = kNegInf, cq = kNegInf;
+        double sp = 0.0, sq = 0.0;
+        double px = 0.0, qx = 0.0;
+        if (valid) {
+            take_segrecs(&a.ws.seg[((size_t)c * L + kk) * a.S], a.S, cp, sp);
+            take_segrecs(&a.ws.seg[((size_t)CL + (size_t)c * L + kk) * a.S], a.S, cq, sq);
+            if (sp <= 0.0 || sq <= 0.0) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
+            if (!bad) {
+                const long long off = (long long)(c * L + kk) * a.ld + xk;
+                const float lp = load_value<T>(static_cast<const T *>(a.p), off);
+                const float lq = load_value<T>(static_cast<const T *>(a.q), off);
+                const double k2 = (double)a.k2;
+                if (sp > 0.0) px = exp2((double)lp * k2 - (double)cp) / sp;
+                if (sq > 0.0) qx = exp2((double)lq * k2 - (double)cq) / sq;
+            }
+        }
+        // min(1, P(x)/Q(x)); Q(x) = 0 gives 1 if P(x) > 0, else 0
+        const double r = qx > 0.0 ? fmin(1.0, px / qx) : (px > 0.0 ? 1.0 : 0.0);
+        const bool accepted = !valid || (a.ua == nullptr || (double)a.ua[c * L + kk] < r);
+        const unsigned long long rej = __ballot(!accepted);
+        const int j = rej ? wave_first(rej) : L;
+        alpha = (float)(wave_sum_d(valid ? r : 0.0) / (double)L);
+        if (valid) {
+            if (a.p_x) a.p_x[c * L + kk] = (float)px;
+            if (a.q_x) a.q_x[c * L + kk] = (float)qx;
+            // position j (a rejection) is written by the residual draw
+            if (a.verify_outputs && kk != j) a.out_tokens[c * L + kk] = kk < j ? xk : -1;
+        }
+        if (a.r_blk) {
+            // publish the row-j constants, then the flag the residual items poll
+            const int src = j < L ? j : 0;
+            const float jcp = __shfl(cp, src), jcq = __shfl(cq, src);
+            const double jsp = __shfl(sp, src), jsq = __shfl(sq, src);
+            if (lane == 0) {
+                SeqInfo *si = &a.ws.info[c];
+                st32(reinterpret_cast<uint32_t *>(&si->j), (uint32_t)j);
+                st32(reinterpret_cast<uint32_t *>(&si->u),
+                     __float_as_uint((j < L && a.ur) ? a.ur[c * L + j] : 0.0f));
+                st32(reinterpret_cast<uint32_t *>(&si->cp), __float_as_uint(jcp));
+                st32(reinterpret_cast<uint32_t *>(&si->cq), __float_as_uint(jcq));
+                st32(reinterpret_cast<uint32_t *>(&si->inv_sp),
+                     __float_as_uint(jsp > 0.0 ? (float)(1.0 / jsp) : 0.0f));
+                st32(reinterpret_cast<uint32_t *>(&si->inv_sq),
+                     __float_as_uint(jsq > 0.0 ? (float)(1.0 / jsq) : 0.0f));
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_s_waitcnt(0);
+                st32(counter(a.ws.flag, c), 1u);
+            }
+        }
+        if (lane == 0 && a.verify_outputs) {
+            a.accept_len[c] = j;
+            a.n_emitted[c] = j + (j < L ? 1 : 0);
+        }
+    } else {
+        int g = 0;
+        if (valid) g = take_argrecs(&a.ws.arg[((size_t)c * L + kk) * a.S], a.S);
+        const bool match = valid && !bad && xk == g;
+        const unsigned long long mism = __ballot(valid && !match);
+        const unsigned long long hits = __ballot(match);
+        const int j = mism ? wave_first(mism) : L;
+        alpha = (float)__popcll((long long)hits) / (float)L;
+        if (valid) {
+            if (a.p_x) a.p_x[c * L + kk] = match ? 1.0f : 0.0f;
+            if (a.q_x) a.q_x[c * L + kk] = 1.0f;
+            if (a.verify_outputs) a.out_tokens[c * L + kk] = kk < j ? xk : (kk == j ? g : -1);
+        }
+        if (lane == 0 && a.verify_outputs) {
+            a.accept_len[c] = j;
+            a.n_emitted[c] = j + (j < L ? 1 : 0);
+        }
+    }
+    if (lane == 0 && a.alpha) a.alpha[c] = alpha;
+
+    // batch mean of alpha, by the last sequence to be decided
+    if (a.alpha_mean) {
+        int last = 0;
+        if (lane == 0) {
+            st32(reinterpret_cast<uint32_t *>(&a.ws.info[c].alpha), __float_as_uint(alpha));
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_s_waitcnt(0);
+            last = __hip_atomic_fetch_add(&a.ws.ctl->seq_done, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) + 1 == (uint32_t)a.C;
+        }
+        last = __shfl(last, 0);
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            double s = 0.0;
+            for (int c0 = 0; c0 < a.C; c0 += kWave) {
+                const int cc = c0 + lane;
+                uint32_t* ap = reinterpret_cast<uint32_t *>(&a.ws.info[cc < a.C ? cc : 0].alpha);
+                s += wave_sum_d(cc < a.C ? (double)__uint_as_float(ld32(ap)) : 0.0);
+            }
+            for (int cc = lane; cc < a.C; cc += kWave)
+                st32(reinterpret_cast<uint32_t *>(&a.ws.info[cc].alpha), 0u);
+            if (lane == 0) {
+                a.alpha_mean[0] = (float)(s / (double)a.C);
+                st32(&a.ws.ctl->seq_done, 0u);
+            }
+        }
+    }
+}
+
+template <typename T, bool VEC, int MODE>
+__device__ __forceinline__ void pq_item(const StepArgs &a, int t, Shared &sh, int wave, int lane) {
+    const int per_seq = a.rows_pq * a.S;
+    const int c = t / per_seq;
+    const int rem = t - c * per_seq;
+    const int slot = rem / a.S;
+    const int seg = rem - slot * a.S;
+    const int CL = a.C * a.L;
+    const int k = MODE == kSample ? slot >> 1 : slot;
+    const int which = MODE == kSample ? (slot & 1) : 0;
+    const T *row = static_cast<const T *>(which ? a.q : a.p) + (long long)(c * a.L + k) * a.ld;
+    const int tb = seg * a.tps;
+    const int te = min(a.tiles_row, tb + a.tps);
+    const size_t rec = ((size_t)which * CL + (size_t)c * a.L + k) * a.S + seg;
+
+    if (MODE == kSample) {
+        LaneSoftmax sm;
+        stream_row<T, VEC>(row, tb, te, a.V, wave, lane, [&](const TileRaw<T> &r, int) {
+            float v[kLaneElems];
+            unpack<T>(r, v);
+            sm.add(v, a.k2);
+        });
+        const double ws = wave_sum_d(sm.acc);
+        if (lane == 0) {
+            sh.refs[wave] = sm.ref;
+            sh.sums[wave] = ws;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float ref;
+            double sum;
+            merge_refsum(sh.refs, sh.sums, kWavesPerGroup, ref, sum);
+            st_seg(&a.ws.seg[rec], ref, sum);
+        }
+    } else {
+        float bv = kNegInf;
+        int bi = INT_MAX;
+        stream_row<T, VEC>(row, tb, te, a.V, wave, lane, [&](const TileRaw<T> &r, int tile) {
+            argmax_tile<T>(r, tile, lane, bv, bi);
+        });
+        wave_argmax(bv, bi);
+        if (lane == 0) {
+            sh.vals[wave] = bv;
+            sh.idxs[wave] = bi;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float v = kNegInf;
+            int i = INT_MAX;
+            for (int w = 0; w < kWavesPerGroup; ++w)
+                if (arg_better(sh.vals[w], sh.idxs[w], v, i)) {
+                    v = sh.vals[w];
+                    i = sh.idxs[w];
+                }
+            st_pair(&a.ws.arg[rec], pack2(v, i));
+        }
+    }
+
+    if (!arrive(counter(a.ws.seq_cnt, c), (uint32_t)per_seq, &sh.flag)) return;
+    if (wave == 0) decide<T, MODE>(a, c, lane);
+}
+
+template <typename T, bool VEC, int MODE>
+__device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg, Shared &sh,
+                                        int wave, int lane) {
+    const int rowid = c * a.L + k;
+    const T *row = static_cast<const T *>(a.qn) + (long long)rowid * a.ld;
+    const int tb = seg * a.tps;
+    const int te = min(a.tiles_row, tb + a.tps);
+
+    if (MODE == kSample) {
+        TileRec *tr = a.ws.tiles + (size_t)rowid * a.tiles_row;
+        LaneSoftmax sm;
+        stream_row<T, VEC>(row, tb, te, a.V, wave, lane, [&](const TileRaw<T> &r, int tile) {
+            float v[kLaneElems];
+            unpack<T>(r, v);
+            const float s = sm.add(v, a.k2);
+            const float ts = wave_sum(s);
+            if (lane == 0) st_pair(&tr[tile], pack2(sm.ref, ts));
+        });
+        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.S, &sh.flag)) return;
+        if (wave != 0) return;
+
+        // ---- inverse-CDF draw over the whole row ----
+        float cr = kNegInf;
+        for (int t = lane; t < a.tiles_row; t += kWave) cr = fmaxf(cr, lo_f(ld_pair(&tr[t])));
+        cr = wave_max(cr);
+        if (cr == kNegInf) {
+            if (lane == 0) {
+                atomicOr(&a.ws.ctl->error, kErrEmptyRow);
+                a.next_tokens[rowid] = 0;
+                if (a.qnext_x) a.qnext_x[rowid] = 0.0f;
+            }
+            for (int t = lane; t < a.tiles_row; t += kWave) st_pair(&tr[t], 0);
+            return;
+        }
+        auto mass = [&](int t) -> double {
+            const uint64_t rc = ld_pair(&tr[t]);
+            const float ref = lo_f(rc);
+            return ref == kNegInf ? 0.0 : (double)hi_f(rc) * pow2_int(ref - cr);
+        };
+        const double S = total_mass(a.tiles_row, lane, mass);
+        const double target = (double)a.up[rowid] * S;
+        double before = 0.0;
+        double tile_target = target;
+        int tile = find_tile(a.tiles_row, target, lane, mass, before);
+        if (tile < 0) {
+            // rounding left the target unreached: clamp to the last positive weight
+            tile = max(0, last_positive_tile(a.tiles_row, lane, mass));
+            tile_target = __builtin_inf();
+        }
+        const float tref = lo_f(ld_pair(&tr[tile]));
+        const double scale = pow2_int(tref - cr);
+        const float k2 = a.k2;
+        const long long V = a.V;
+        auto weight = [&](long long i) -> double {
+            if (i >= V) return 0.0;
+            return (double)fast_exp2(fmaf(load_value<T>(row, i), k2, -tref)) * scale;
+        };
+        const long long tok = search_tile(weight, tile, lane, before, tile_target);
+        // the tile masses are consumed: return them to zero
+        for (int t = lane; t < a.tiles_row; t += kWave) st_pair(&tr[t], 0);
+        if (lane == 0) {
+            const int token = tok < 0 ? 0 : (int)tok;
+            a.next_tokens[rowid] = token;
+            if (a.qnext_x) {
+                const float lv = load_value<T>(row, token);
+                a.qnext_x[rowid] = (float)(exp2((double)lv * (double)k2 - (double)cr) / S);
+            }
+        }
+    } else {
+        float bv = kNegInf;
+        int bi = INT_MAX;
+        stream_row<T, VEC>(row, tb, te, a.V, wave, lane, [&](const TileRaw<T> &r, int tile) {
+            argmax_tile<T>(r, tile, lane, bv, bi);
+        });
+        wave_argmax(bv, bi);
+        if (lane == 0) {
+            sh.vals[wave] = bv;
+            sh.idxs[wave] = bi;
+        }
+        __syncthreads();
+        ArgRec *recs = &a.ws.arg[((size_t)a.C * a.L + rowid) * a.S];
+        if (threadIdx.x == 0) {
+            float v = kNegInf;
+            int i = INT_MAX;
+            for (int w = 0; w < kWavesPerGroup; ++w)
+                if (arg_better(sh.vals[w], sh.idxs[w], v, i)) {
+                    v = sh.vals[w];
+                    i = sh.idxs[w];
+                }
+            st_pair(&recs[seg], pack2(v, i));
+        }
+        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.S, &sh.flag)) return;
+        if (threadIdx.x == 0) {
+            a.next_tokens[rowid] = take_argrecs(recs, a.S);
+            if (a.qnext_x) a.qnext_x[rowid] = 1.0f;
+        }
+    }
+}
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shared &sh, int wave,
+                                         int lane) {
+    // wait for sequence c's decision
+    if (threadIdx.x == 0) {
+        uint32_t polls = 0;
+        bool ok = true;
+        uint32_t *flag = counter(a.ws.flag, c);
+        while (ld32(flag) == 0u) {
+            __builtin_amdgcn_s_sleep(4);
+            if (++polls > a.spin_limit) {
+                atomicOr(&a.ws.ctl->error, kErrWaitExpired);
+                ok = false;
+                break;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        SeqInfo *si = &a.ws.info[c];
+        sh.info.j = ok ? (int)ld32(reinterpret_cast<uint32_t *>(&si->j)) : a.L;
+        sh.info.u = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->u)));
+        sh.info.cp = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->cp)));
+        sh.info.cq = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->cq)));
+        sh.info.inv_sp = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->inv_sp)));
+        sh.info.inv_sq = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->inv_sq)));
+    }
+    __syncthreads();
+    const SeqInfo inf = sh.info;
+    const int L = a.L;
+    const int j = inf.j;
+    ResTile *rt = a.ws.rtiles + (size_t)c * a.tiles_row;
+    const T *prow = static_cast<const T *>(a.p) + (long long)(c * L + (j < L ? j : 0)) * a.ld;
+    const T *qrow = static_cast<const T *>(a.q) + (long long)(c * L + (j < L ? j : 0)) * a.ld;
+
+    if (j < L) {
+        const int tb = seg * a.tpsr;
+        const int te = min(a.tiles_row, tb + a.tpsr);
+        stream_rows2<T, VEC>(prow, qrow, tb, te, a.V, wave, lane,
+                             [&](const TileRaw<T> &rp, const TileRaw<T> &rq, int tile) {
+            float lr = 0.0f, lp = 0.0f;
+#pragma unroll
+            for (int g = 0; g < kGroupsPerTile; ++g) {
+                float er[kGroupElems], ep[kGroupElems];
+#pragma unroll
+                for (int e = 0; e < kGroupElems; ++e) {
+                    const int i = g * kGroupElems + e;
+                    const float P = fast_exp2(fmaf(elem<T>(rp, i), a.k2, -inf.cp)) * inf.inv_sp;
+                    const float Q = fast_exp2(fmaf(elem<T>(rq, i), a.k2, -inf.cq)) * inf.inv_sq;
+                    er[e] = fmaxf(P - Q, 0.0f);
+                    ep[e] = P;
+                }
+                lr += tree_sum(er);
+                lp += tree_sum(ep);
+            }
+            const float sr = wave_sum(lr);
+            const float spp = wave_sum(lp);
+            if (lane == 0) st_pair(&rt[tile], pack2(sr, spp));
+        });
+    }
+
+    if (!arrive(counter(a.ws.res_cnt, c), (uint32_t)a.r_blk, &sh.flag)) return;
+    if (wave != 0) return;
+    if (j < L) {
+        // ---- inverse-CDF draw over max(0, P - Q) (P if that is empty) ----
+        auto mass_r = [&](int t) -> double { return (double)lo_f(ld_pair(&rt[t])); };
+        auto mass_p = [&](int t) -> double { return (double)hi_f(ld_pair(&rt[t])); };
+        double Z = total_mass(a.tiles_row, lane, mass_r);
+        const bool use_p = !(Z > 0.0);
+        if (use_p) Z = total_mass(a.tiles_row, lane, mass_p);
+        const double target = (double)inf.u * Z;
+        double before = 0.0;
+        double tile_target = target;
+        int tile;
+        if (!use_p) {
+            tile = find_tile(a.tiles_row, target, lane, mass_r, before);
+            if (tile < 0) {
+                tile = last_positive_tile(a.tiles_row, lane, mass_r);
+                tile_target = __builtin_inf();
+            }
+        } else {
+            tile = find_tile(a.tiles_row, target, lane, mass_p, before);
+            if (tile < 0) {
+                tile = last_positive_tile(a.tiles_row, lane, mass_p);
+                tile_target = __builtin_inf();
+            }
+        }
+        long long tok = 0;
+        if (tile >= 0) {
+            const float k2 = a.k2;
+            const long long V = a.V;
+            auto weight = [&](long long i) -> double {
+                if (i >= V) return 0.0;
+                const float P = fast_exp2(fmaf(load_value<T>(prow, i), k2, -inf.cp)) * inf.inv_sp;
+                const float Q = fast_exp2(fmaf(load_value<T>(qrow, i), k2, -inf.cq)) * inf.inv_sq;
+                return use_p ? (double)P : (double)fmaxf(P - Q, 0.0f);
+            };
+            tok = search_tile(weight, tile, lane, before, tile_target);
+            if (tok < 0) tok = 0;
+        }
+        for (int t = lane; t < a.tiles_row; t += kWave) st_pair(&rt[t], 0);
+        if (lane == 0 && a.verify_outputs) a.out_tokens[c * L + j] = (int)tok;
+    }
+    if (lane == 0) {
+        // every residual item of c has read the decision: clear it for the next launch
+        SeqInfo *si = &a.ws.info[c];
+        st32(reinterpret_cast<uint32_t *>(&si->j), 0u);
+        st32(reinterpret_cast<uint32_t *>(&si->u), 0u);
+        st32(reinterpret_cast<uint32_t *>(&si->cp), 0u);
+        st32(reinterpret_cast<uint32_t *>(&si->cq), 0u);
+        st32(reinterpret_cast<uint32_t *>(&si->inv_sp), 0u);
+        st32(reinterpret_cast<uint32_t *>(&si->inv_sq), 0u);
+        st32(counter(a.ws.flag, c), 0u);
+    }
+}
+
+template <typename T, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
+    __shared__ Shared sh;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int t = (int)blockIdx.x;
+
+    if (t < a.n_pq) {
+        pq_item<T, VEC, MODE>(a, t, sh, wave, lane);
+    } else if (t < a.n_items) {
+        const int t2 = t - a.n_pq;
+        const int blk = a.q_blk + a.r_blk;
+        const int c = t2 / blk;
+        const int w = t2 - c * blk;
+        if (w < a.q_blk) {
+            const int k = w / a.S;
+            qn_item<T, VEC, MODE>(a, c, k, w - k * a.S, sh, wave, lane);
+        } else if (MODE == kSample) {
+            res_item<T, VEC>(a, c, w - a.q_blk, sh, wave, lane);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStream_t stream) {
+    const dim3 grid((unsigned)a.n_items), block(kThreads);
+#define ISD_LAUNCH(T, V, M) hipLaunchKernelGGL((step_kernel<T, V, M>), grid, block, 0, stream, a)
+    if (dtype == kBf16) {
+        if (mode == kSample) {
+            if (vec) ISD_LAUNCH(uint16_t, true, kSample);
+            else ISD_LAUNCH(uint16_t, false, kSample);
+        } else {
+            if (vec) ISD_LAUNCH(uint16_t, true, kGreedy);
+            else ISD_LAUNCH(uint16_t, false, kGreedy);
+        }
+    } else {
+        if (mode == kSample) {
+            if (vec) ISD_LAUNCH(float, true, kSample);
+            else ISD_LAUNCH(float, false, kSample);
+        } else {
+            if (vec) ISD_LAUNCH(float, true, kGreedy);
+            else ISD_LAUNCH(float, false, kGreedy);
+        }
+    }
+#undef ISD_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace isd

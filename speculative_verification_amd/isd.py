@@ -1,0 +1,262 @@
+"""ctypes binding of libisd (include/isd.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libisd.  Tensors are torch device tensors; the calls enqueue on
+torch's current stream and return without synchronising.  A missing or
+unloadable library raises immediately; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libisd.so")
+
+ISD_OK, ISD_ERR_ARG, ISD_ERR_UNSUPPORTED, ISD_ERR_WORKSPACE, ISD_ERR_DEVICE = range(5)
+DTYPE_BF16, DTYPE_F32 = 0, 1
+MODE_SAMPLE, MODE_GREEDY = 0, 1
+
+_STATUS_NAMES = {ISD_ERR_ARG: "ISD_ERR_ARG", ISD_ERR_UNSUPPORTED: "ISD_ERR_UNSUPPORTED",
+                 ISD_ERR_WORKSPACE: "ISD_ERR_WORKSPACE", ISD_ERR_DEVICE: "ISD_ERR_DEVICE"}
+
+
+class IsdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("C", ctypes.c_int32), ("L", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("ld", ctypes.c_int64), ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("temperature", ctypes.c_float)]
+
+
+_vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+_SIGS = {
+    "isd_workspace_bytes": (_sz, [ctypes.POINTER(Shape)]),
+    "isd_verify_step": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 11 + [_vp, _sz, _vp]),
+    "isd_propose": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 4 + [_vp, _sz, _vp]),
+    "isd_alpha": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 5 + [_vp, _sz, _vp]),
+    "isd_step": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 15 + [_vp, _sz, _vp]),
+    "isd_lm_head": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "isd_check_device_error": (ctypes.c_int, [_vp, _sz, _vp]),
+    "isd_set_tuning": (ctypes.c_int, [_i32, _i32, _i64]),
+    "isd_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libisd; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(f"{LIB_PATH} is not built: run "
+                                       "`python -m speculative_verification_amd.build`")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in _SIGS.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != ISD_OK:
+        raise IsdError(status, lib().isd_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _logits_layout(t: torch.Tensor):
+    """(C, L, V, ld, dtype code) of a [C, L, V] logits tensor with unit
+    innermost stride and evenly spaced rows."""
+    if t.dim() != 3:
+        raise ValueError("logits must be [C, L, V]")
+    if t.dtype == torch.bfloat16:
+        code = DTYPE_BF16
+    elif t.dtype == torch.float32:
+        code = DTYPE_F32
+    else:
+        raise ValueError(f"unsupported logits dtype {t.dtype}")
+    C, L, V = t.shape
+    if t.stride(2) != 1 and V > 1:
+        raise ValueError("logits rows must be contiguous")
+    ld = t.stride(1) if L > 1 else (t.stride(0) if C > 1 else V)
+    if C > 1 and L > 1 and t.stride(0) != L * ld:
+        raise ValueError("logits rows must be evenly spaced")
+    if C > 1 and L == 1:
+        ld = t.stride(0)
+    return C, L, V, max(int(ld), V), code
+
+
+def make_shape(logits: torch.Tensor, mode: int = MODE_SAMPLE, temperature: float = 1.0) -> Shape:
+    C, L, V, ld, code = _logits_layout(logits)
+    return Shape(C, L, V, ld, code, mode, float(temperature))
+
+
+def _mode_code(mode) -> int:
+    if mode in ("sample", MODE_SAMPLE):
+        return MODE_SAMPLE
+    if mode in ("greedy", MODE_GREEDY):
+        return MODE_GREEDY
+    raise ValueError(f"unknown mode {mode!r}")
+
+
+def workspace_bytes(shape: Shape) -> int:
+    n = lib().isd_workspace_bytes(ctypes.byref(shape))
+    if n == 0:
+        _check(ISD_ERR_ARG)
+    return int(n)
+
+
+_ws_cache: dict = {}
+
+
+def workspace(shape: Shape, device=None) -> torch.Tensor:
+    """A zero-filled workspace for `shape`, cached per device (one per thread of use)."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    need = workspace_bytes(shape)
+    key = (device, threading.get_ident())
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _out(out, key, shape, dtype, device):
+    t = None if out is None else out.get(key)
+    if t is None:
+        t = torch.empty(shape, dtype=dtype, device=device)
+    return t
+
+
+def verify_step(p, q, x, ua, ur, *, mode="sample", temperature=1.0, out=None, ws=None):
+    """Verify proposals x [C, L] against anchor rows p (and proposal rows q)."""
+    m = _mode_code(mode)
+    shape = make_shape(p, m, temperature)
+    C, L, dev = shape.C, shape.L, p.device
+    o = dict(accept_len=_out(out, "accept_len", (C,), torch.int32, dev),
+             out_tokens=_out(out, "out_tokens", (C, L), torch.int32, dev),
+             n_emitted=_out(out, "n_emitted", (C,), torch.int32, dev),
+             p_x=_out(out, "p_x", (C, L), torch.float32, dev),
+             q_x=_out(out, "q_x", (C, L), torch.float32, dev),
+             alpha=_out(out, "alpha", (C,), torch.float32, dev))
+    ws = workspace(shape, dev) if ws is None else ws
+    _check(lib().isd_verify_step(ctypes.byref(shape), _ptr(p), _ptr(q), _ptr(x), _ptr(ua), _ptr(ur),
+                                 _ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o["n_emitted"]),
+                                 _ptr(o["p_x"]), _ptr(o["q_x"]), _ptr(o["alpha"]),
+                                 _ptr(ws), ws.numel(), _stream()))
+    return o
+
+
+def propose(qn, up, *, mode="sample", temperature=1.0, out=None, ws=None):
+    """Draw the next proposals [C, L] from the mask-position rows qn."""
+    m = _mode_code(mode)
+    shape = make_shape(qn, m, temperature)
+    C, L, dev = shape.C, shape.L, qn.device
+    o = dict(next_tokens=_out(out, "next_tokens", (C, L), torch.int32, dev),
+             qnext_x=_out(out, "qnext_x", (C, L), torch.float32, dev))
+    ws = workspace(shape, dev) if ws is None else ws
+    _check(lib().isd_propose(ctypes.byref(shape), _ptr(qn), _ptr(up), _ptr(o["next_tokens"]),
+                             _ptr(o["qnext_x"]), _ptr(ws), ws.numel(), _stream()))
+    return o
+
+
+def alpha(p, q, x, *, mode="sample", temperature=1.0, out=None, ws=None):
+    """Introspective acceptance rate per sequence and its batch mean."""
+    m = _mode_code(mode)
+    shape = make_shape(p, m, temperature)
+    dev = p.device
+    o = dict(alpha=_out(out, "alpha", (shape.C,), torch.float32, dev),
+             alpha_mean=_out(out, "alpha_mean", (1,), torch.float32, dev))
+    ws = workspace(shape, dev) if ws is None else ws
+    _check(lib().isd_alpha(ctypes.byref(shape), _ptr(p), _ptr(q), _ptr(x), _ptr(o["alpha"]),
+                           _ptr(o["alpha_mean"]), _ptr(ws), ws.numel(), _stream()))
+    return o
+
+
+class StepCall:
+    """Pre-marshalled isd_step call: fixed shapes and output buffers, so that a
+    timing loop pays one ctypes call per step."""
+
+    def __init__(self, p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, out=None,
+                 ws=None):
+        m = _mode_code(mode)
+        self.shape = make_shape(p, m, temperature)
+        if make_shape(qn, m, temperature).ld != self.shape.ld or qn.shape != p.shape:
+            raise ValueError("p and qn must share shape and row stride")
+        C, L, dev = self.shape.C, self.shape.L, p.device
+        self.out = dict(accept_len=_out(out, "accept_len", (C,), torch.int32, dev),
+                        out_tokens=_out(out, "out_tokens", (C, L), torch.int32, dev),
+                        n_emitted=_out(out, "n_emitted", (C,), torch.int32, dev),
+                        p_x=_out(out, "p_x", (C, L), torch.float32, dev),
+                        q_x=_out(out, "q_x", (C, L), torch.float32, dev),
+                        alpha=_out(out, "alpha", (C,), torch.float32, dev),
+                        next_tokens=_out(out, "next_tokens", (C, L), torch.int32, dev),
+                        qnext_x=_out(out, "qnext_x", (C, L), torch.float32, dev))
+        self.ws = workspace(self.shape, dev) if ws is None else ws
+        self._fn = lib().isd_step
+        self._shape_ref = ctypes.byref(self.shape)
+        o = self.out
+        self._tail = [_ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o["n_emitted"]),
+                      _ptr(o["p_x"]), _ptr(o["q_x"]), _ptr(o["alpha"]), _ptr(o["next_tokens"]),
+                      _ptr(o["qnext_x"]), _ptr(self.ws), self.ws.numel()]
+        self.bind(p, q, x, ua, ur, qn, up)
+
+    def bind(self, p, q, x, ua, ur, qn, up):
+        """Point the call at new input tensors of the same shapes."""
+        self._head = [_ptr(p), _ptr(q), _ptr(x), _ptr(ua), _ptr(ur), _ptr(qn), _ptr(up)]
+
+    def __call__(self, stream=None):
+        s = _stream() if stream is None else ctypes.c_void_p(stream)
+        _check(self._fn(self._shape_ref, *self._head, *self._tail, s))
+        return self.out
+
+
+def step(p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, out=None, ws=None):
+    """One fused ISD step (verify + propose in one launch)."""
+    return StepCall(p, q, x, ua, ur, qn, up, mode=mode, temperature=temperature, out=out, ws=ws)()
+
+
+def lm_head(h, w, out=None):
+    """logits [M, N] = h [M, K] @ w [K, N] (bf16, fp32 accumulation on MFMA)."""
+    if h.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("lm_head takes bf16 tensors")
+    if not (h.is_contiguous() and w.is_contiguous()):
+        raise ValueError("lm_head takes contiguous tensors")
+    M, K = h.shape
+    K2, N = w.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=h.device)
+    _check(lib().isd_lm_head(_ptr(h), _ptr(w), M, K, N, _ptr(out), None, 0, _stream()))
+    return out
+
+
+def check_device_error(ws: torch.Tensor):
+    """Synchronise and raise IsdError if a kernel flagged undefined input."""
+    _check(lib().isd_check_device_error(_ptr(ws), ws.numel(), _stream()))
+
+
+def set_tuning(segments: int = 0, resid_segments: int = 0, spin_limit: int = 0):
+    _check(lib().isd_set_tuning(segments, resid_segments, spin_limit))

@@ -1,0 +1,149 @@
+"""The C ABI on the host: libisd loads, exports every function include/isd.h
+declares, and rejects bad arguments synchronously with the documented
+status codes.  No call here reaches a kernel launch, so no GPU is needed."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "isd.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced on the host
+
+
+@pytest.fixture(scope="module")
+def isd():
+    import speculative_verification_amd as m
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(isd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("isd_verify_step", "isd_propose", "isd_alpha", "isd_step", "isd_lm_head",
+                     "isd_workspace_bytes", "isd_last_error", "isd_check_device_error",
+                     "isd_set_tuning"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(isd):
+    lib = ctypes.CDLL(isd.isd.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _shape(isd, **kw):
+    base = dict(C=4, L=8, V=151936, ld=151936, dtype=0, mode=0, temperature=1.0)
+    base.update(kw)
+    return isd.Shape(base["C"], base["L"], base["V"], base["ld"], base["dtype"], base["mode"],
+                     base["temperature"])
+
+
+def _verify(isd, shape, ws_bytes=1 << 30, **ptrs):
+    args = dict(p=FAKE, q=FAKE, x=FAKE, ua=FAKE, ur=FAKE, al=FAKE, out=FAKE, ne=FAKE)
+    args.update(ptrs)
+    return isd.lib().isd_verify_step(ctypes.byref(shape), args["p"], args["q"], args["x"],
+                                     args["ua"], args["ur"], args["al"], args["out"], args["ne"],
+                                     None, None, None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(C=0), 1, "C must be"),
+    (dict(L=0), 1, "L must be"),
+    (dict(L=65), 1, "L must be"),
+    (dict(V=0), 1, "V must be"),
+    (dict(ld=100), 1, "ld"),
+    (dict(temperature=0.0), 1, "temperature"),
+    (dict(temperature=float("nan")), 1, "temperature"),
+    (dict(dtype=7), 2, "dtype"),
+    (dict(mode=3), 2, "mode"),
+])
+def test_bad_shapes(isd, kw, status, msg):
+    st = _verify(isd, _shape(isd, **kw))
+    assert st == status
+    assert msg in isd.lib().isd_last_error().decode()
+
+
+@pytest.mark.parametrize("missing", ["p", "q", "x", "ua", "ur", "al", "out", "ne"])
+def test_null_pointers(isd, missing):
+    st = _verify(isd, _shape(isd), **{missing: None})
+    assert st == 1
+    assert "NULL" in isd.lib().isd_last_error().decode()
+
+
+def test_greedy_ignores_q_and_uniforms(isd):
+    # with q/ua/ur NULL in greedy mode the only remaining error is the workspace size
+    st = _verify(isd, _shape(isd, mode=1), ws_bytes=16, q=None, ua=None, ur=None)
+    assert st == 3
+
+
+def test_misaligned_pointer(isd):
+    st = _verify(isd, _shape(isd), p=ctypes.c_void_p(0x10001))
+    assert st == 1 and "aligned" in isd.lib().isd_last_error().decode()
+
+
+def test_workspace_too_small(isd):
+    shape = _shape(isd)
+    need = isd.lib().isd_workspace_bytes(ctypes.byref(shape))
+    assert need > 0
+    st = _verify(isd, shape, ws_bytes=need - 1)
+    assert st == 3 and "workspace" in isd.lib().isd_last_error().decode()
+
+
+def test_workspace_bytes(isd):
+    lib = isd.lib()
+    small = lib.isd_workspace_bytes(ctypes.byref(_shape(isd, C=1, L=4, V=1000, ld=1000)))
+    big = lib.isd_workspace_bytes(ctypes.byref(_shape(isd, C=256, L=16)))
+    assert 0 < small < big
+    assert big % 256 == 0
+    assert lib.isd_workspace_bytes(ctypes.byref(_shape(isd, C=0))) == 0
+    assert lib.isd_workspace_bytes(None) == 0
+
+
+def test_propose_alpha_step_validation(isd):
+    lib = isd.lib()
+    shape = _shape(isd)
+    assert lib.isd_propose(ctypes.byref(shape), None, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.isd_alpha(ctypes.byref(shape), FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, None) == 1
+    args = [FAKE] * 15
+    args[5] = None                                   # qnext_logits
+    assert lib.isd_step(ctypes.byref(shape), *args, FAKE, 1 << 30, None) == 1
+    assert "qnext_logits" in lib.isd_last_error().decode()
+
+
+def test_lm_head_validation(isd):
+    lib = isd.lib()
+    assert lib.isd_lm_head(FAKE, FAKE, 16, 100, 64, FAKE, None, 0, None) == 1
+    assert "multiple of 64" in lib.isd_last_error().decode()
+    assert lib.isd_lm_head(FAKE, FAKE, 0, 64, 64, FAKE, None, 0, None) == 1
+    assert lib.isd_lm_head(None, FAKE, 16, 64, 64, FAKE, None, 0, None) == 1
+
+
+def test_tuning_validation(isd):
+    lib = isd.lib()
+    assert lib.isd_set_tuning(-1, 0, 0) == 1
+    assert lib.isd_set_tuning(0, 1000, 0) == 1
+    assert lib.isd_set_tuning(0, 0, -5) == 1
+    assert lib.isd_set_tuning(4, 8, 100) == 0
+    assert lib.isd_set_tuning(0, 0, 0) == 0
+
+
+def test_binding_layout_checks(isd):
+    import torch
+    t = torch.zeros((2, 3, 10), dtype=torch.bfloat16)
+    s = isd.make_shape(t)
+    assert (s.C, s.L, s.V, s.ld, s.dtype) == (2, 3, 10, 10, 0)
+    padded = torch.zeros((2, 3, 16), dtype=torch.float32)[:, :, :10]
+    s = isd.make_shape(padded)
+    assert (s.V, s.ld, s.dtype) == (10, 16, 1)
+    with pytest.raises(ValueError):
+        isd.make_shape(torch.zeros((2, 3, 10), dtype=torch.float16))
