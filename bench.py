@@ -58,6 +58,7 @@ def parse():
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--resid-segments", type=int, default=0)
+    ap.add_argument("--propose-segments", type=int, default=0)
     return ap.parse_args()
 
 
@@ -128,7 +129,7 @@ def main():
     C, L, V, mode, T = cfg["C"], cfg["L"], cfg["V"], cfg["mode"], cfg["T"]
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    isd.set_tuning(args.segments, args.resid_segments, 0)
+    isd.set_tuning(args.segments, args.resid_segments, 0, args.propose_segments)
 
     nsets = max(1, args.sets)
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -166,8 +167,6 @@ def main():
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    accept = torch.empty((args.steps, C), dtype=torch.int32, device=dev)
-    alphas = torch.empty((args.steps, C), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -175,11 +174,20 @@ def main():
         starts[i].record(stream)
         call()
         ends[i].record(stream)
-        accept[i].copy_(call.out["accept_len"], non_blocking=True)
-        alphas[i].copy_(call.out["alpha"], non_blocking=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     isd.check_device_error(call.ws)
+
+    # untimed pass over the same steps for workload statistics
+    n_stat = min(args.steps, 50)
+    accept = torch.empty((n_stat, C), dtype=torch.int32, device=dev)
+    alphas = torch.empty((n_stat, C), dtype=torch.float32, device=dev)
+    for i in range(n_stat):
+        bind(args.warmup + i)
+        call()
+        accept[i].copy_(call.out["accept_len"])
+        alphas[i].copy_(call.out["alpha"])
+    torch.cuda.synchronize()
 
     kernel_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     ms_per_step = wall * 1e3 / args.steps

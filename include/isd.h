@@ -169,11 +169,13 @@ isd_status_t isd_lm_head(const void *h, const void *w, int32_t M, int32_t K, int
 isd_status_t isd_check_device_error(void *workspace, size_t ws_bytes, void *stream);
 
 /* Tuning knobs, process-wide; 0 restores the automatic choice.
- *   segments        workgroups sharing one logits row (1..32)
- *   resid_segments  workgroups sharing one residual row pair (1..64)
- *   spin_limit      bound on the polls of an internal cross-workgroup wait
- *                   before it gives up and flags the device error word */
-isd_status_t isd_set_tuning(int32_t segments, int32_t resid_segments, int64_t spin_limit);
+ *   segments          workgroups sharing one verify row (1..32)
+ *   propose_segments  workgroups sharing one mask row (1..32)
+ *   resid_segments    workgroups sharing one residual row pair (1..64)
+ *   spin_limit        bound on the polls of an internal cross-workgroup wait
+ *                     before it gives up and flags the device error word */
+isd_status_t isd_set_tuning(int32_t segments, int32_t propose_segments, int32_t resid_segments,
+                            int64_t spin_limit);
 
 /* Thread-local description of the last non-OK status of this thread. */
 const char *isd_last_error(void);

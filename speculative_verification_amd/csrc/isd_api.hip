@@ -26,7 +26,13 @@ isd_status_t fail(isd_status_t st, const char *fmt, ...) {
 }
 
 std::atomic<int> g_segments{0};
+std::atomic<int> g_propose_segments{0};
 std::atomic<int> g_resid_segments{0};
+// default decomposition (tiles of 2048 elements per workgroup segment)
+constexpr int kVerifyTilesPerSeg = 38;
+constexpr int kProposeTilesPerSeg = 19;
+constexpr int kResidTilesPerSeg = 8;
+constexpr int kItemOrder = 0;
 std::atomic<long long> g_spin_limit{0};
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 
@@ -109,28 +115,30 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
     a.ws = workspace_at(workspace, lay);
     a.tiles_row = ceil_div(V, kTileElems);
 
-    // rows streamed in this launch
-    const long long rows = (plan.verify ? (long long)C * L * (greedy ? 1 : 2) : 0) +
-                           (plan.propose ? (long long)C * L : 0);
-    int S = g_segments.load();
-    if (S <= 0) {
-        // enough workgroups to keep every CU streaming several rows at once
-        const long long want = 8LL * cu_count();
-        S = (int)((want + rows - 1) / rows);
-    }
-    S = max(1, min(S, min(lay.smax, a.tiles_row)));
-    a.tps = ceil_div(a.tiles_row, S);
+    // Segments per row.  Verify rows are dispatched first and can be large;
+    // mask rows and residual rows come later and are cut finer so that the
+    // last workgroups of the launch are short.
+    a.smax = lay.smax;
+    auto segs = [&](int want, int tiles_per_seg_target) {
+        int S = want > 0 ? want : ceil_div(a.tiles_row, tiles_per_seg_target);
+        return max(1, min(S, min(lay.smax, a.tiles_row)));
+    };
+    const int Sv = segs(g_segments.load(), kVerifyTilesPerSeg);
+    a.tps = ceil_div(a.tiles_row, Sv);
     a.S = ceil_div(a.tiles_row, a.tps);
-
+    const int Sq = segs(g_propose_segments.load(), kProposeTilesPerSeg);
+    a.tpsq = ceil_div(a.tiles_row, Sq);
+    a.Sq = ceil_div(a.tiles_row, a.tpsq);
     int Sr = g_resid_segments.load();
-    if (Sr <= 0) Sr = ceil_div(a.tiles_row, 2 * kWavesPerGroup);
+    if (Sr <= 0) Sr = ceil_div(a.tiles_row, kResidTilesPerSeg);
     Sr = max(1, min(Sr, min(kMaxResidSegments, a.tiles_row)));
     a.tpsr = ceil_div(a.tiles_row, Sr);
     a.Sr = ceil_div(a.tiles_row, a.tpsr);
+    a.order = kItemOrder;
 
     a.rows_pq = plan.verify ? (greedy ? L : 2 * L) : 0;
     a.n_pq = C * a.rows_pq * a.S;
-    a.q_blk = plan.propose ? L * a.S : 0;
+    a.q_blk = plan.propose ? L * a.Sq : 0;
     a.r_blk = (plan.residual && !greedy) ? a.Sr : 0;
     const long long n_items = (long long)a.n_pq + (long long)C * (a.q_blk + a.r_blk);
     if (n_items <= 0 || n_items >= (1LL << 31))
@@ -361,13 +369,17 @@ isd_status_t isd_check_device_error(void *workspace, size_t ws_bytes, void *stre
                 (err & kErrWaitExpired) ? " cross-workgroup wait expired;" : "");
 }
 
-isd_status_t isd_set_tuning(int32_t segments, int32_t resid_segments, int64_t spin_limit) {
+isd_status_t isd_set_tuning(int32_t segments, int32_t propose_segments, int32_t resid_segments,
+                            int64_t spin_limit) {
     if (segments < 0 || segments > kMaxSegments)
         return fail(ISD_ERR_ARG, "segments must be in [0, %d]", kMaxSegments);
+    if (propose_segments < 0 || propose_segments > kMaxSegments)
+        return fail(ISD_ERR_ARG, "propose_segments must be in [0, %d]", kMaxSegments);
     if (resid_segments < 0 || resid_segments > kMaxResidSegments)
         return fail(ISD_ERR_ARG, "resid_segments must be in [0, %d]", kMaxResidSegments);
     if (spin_limit < 0) return fail(ISD_ERR_ARG, "spin_limit must be >= 0");
     g_segments.store(segments);
+    g_propose_segments.store(propose_segments);
     g_resid_segments.store(resid_segments);
     g_spin_limit.store(spin_limit);
     return ISD_OK;

@@ -109,14 +109,17 @@ struct StepArgs {
     Workspace ws;
     // decomposition
     int tiles_row;             // ceil(V / kTileElems)
-    int S, tps;                // segments per streamed row, tiles per segment
+    int smax;                  // segment records reserved per row in the workspace
+    int S, tps;                // segments per verify row, tiles per segment
+    int Sq, tpsq;              // segments per mask row, tiles per segment
     int Sr, tpsr;              // segments per residual row pair, tiles per segment
     int rows_pq;               // verify rows per sequence (2L sample, L greedy, 0 none)
     int n_pq;                  // C * rows_pq * S
-    int q_blk;                 // mask-row items per sequence (L*S or 0)
+    int q_blk;                 // mask-row items per sequence (L*Sq or 0)
     int r_blk;                 // residual items per sequence (Sr or 0)
     int n_items;
     int verify_outputs;        // write tokens / counts (0: alpha only)
+    int order;                 // 0: per sequence [mask rows, residual]; 1: all mask rows first
     uint32_t spin_limit;
 };
 

@@ -108,6 +108,8 @@ __device__ __forceinline__ double pow2_int(float n) {
 // Tile loads
 // ---------------------------------------------------------------------------
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename T>
 struct TileRaw {
     static constexpr int kWords = kLaneElems * (int)sizeof(T) / 4;
@@ -135,14 +137,16 @@ __device__ __forceinline__ void load_tile(const T *__restrict__ row, int tile, i
     const long long base = (long long)tile * kTileElems + lane * kGroupElems;
     const bool full = (long long)(tile + 1) * kTileElems <= (long long)V;
     if (VEC && full) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(row + base);
+        // streamed once: non-temporal loads keep the logits from displacing
+        // useful cache lines and measurably raise the achieved read rate
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(row + base);
         constexpr int kVecPerGroup = kGroupElems * (int)sizeof(T) / 16;  // 1 (bf16) or 2 (fp32)
         constexpr int kGroupStride = kWave * kGroupElems * (int)sizeof(T) / 16;
 #pragma unroll
         for (int g = 0; g < kGroupsPerTile; ++g) {
 #pragma unroll
             for (int h = 0; h < kVecPerGroup; ++h) {
-                uint4 v = src[g * kGroupStride + h];
+                const u32x4 v = __builtin_nontemporal_load(&src[g * kGroupStride + h]);
                 const int w0 = (g * kVecPerGroup + h) * 4;
                 r.w[w0 + 0] = v.x;
                 r.w[w0 + 1] = v.y;
@@ -306,7 +310,7 @@ __device__ __forceinline__ uint64_t ld_pair(const void *r) {
 // arrivals `total`).  All threads call it after their record stores; it
 // returns, to every thread, whether this was the last arrival.  The last one
 // resets the counter for the next launch.
-__device__ bool arrive(uint32_t *counter, uint32_t total, int *s_flag) {
+__device__ __forceinline__ bool arrive(uint32_t *counter, uint32_t total, int *s_flag) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -360,20 +364,29 @@ __device__ __forceinline__ void merge_refsum(const float *refs, const double *su
         if (refs[i] != kNegInf) sum += sums[i] * pow2_int(refs[i] - ref);
 }
 
-// Merges the n segment records of one row and clears them.
+// Merges the n segment records of one row (loads issued four at a time) and
+// clears them.
 __device__ __forceinline__ void take_segrecs(SegRec *rec, int n, float &ref, double &sum) {
     ref = kNegInf;
     sum = 0.0;
-    for (int i = 0; i < n; ++i) {
-        float r;
-        double s;
-        ld_seg(&rec[i], r, s);
-        if (r == kNegInf) continue;
-        if (r > ref) {
-            if (ref != kNegInf) sum *= pow2_int(ref - r);
-            ref = r;
+    for (int i0 = 0; i0 < n; i0 += 4) {
+        uint64_t lo[4], hi[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            lo[k] = i0 + k < n ? ld64(reinterpret_cast<const uint64_t *>(&rec[i0 + k])) : 0;
+            hi[k] = i0 + k < n ? ld64(reinterpret_cast<const uint64_t *>(&rec[i0 + k]) + 1) : 0;
         }
-        sum += s * pow2_int(r - ref);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (i0 + k >= n) continue;
+            const float r = lo_f(lo[k]);
+            if (r == kNegInf) continue;
+            if (r > ref) {
+                if (ref != kNegInf) sum *= pow2_int(ref - r);
+                ref = r;
+            }
+            sum += __longlong_as_double((long long)hi[k]) * pow2_int(r - ref);
+        }
     }
     for (int i = 0; i < n; ++i) st_seg(&rec[i], 0.0f, 0.0);
 }
@@ -398,12 +411,16 @@ __device__ __forceinline__ void wave_argmax(float &bv, int &bi) {
 __device__ __forceinline__ int take_argrecs(ArgRec *rec, int n) {
     float bv = kNegInf;
     int bi = INT_MAX;
-    for (int i = 0; i < n; ++i) {
-        const uint64_t v = ld_pair(&rec[i]);
-        if (arg_better(lo_f(v), hi_i(v), bv, bi)) {
-            bv = lo_f(v);
-            bi = hi_i(v);
-        }
+    for (int i0 = 0; i0 < n; i0 += 4) {
+        uint64_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = i0 + k < n ? ld_pair(&rec[i0 + k]) : 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (i0 + k < n && arg_better(lo_f(v[k]), hi_i(v[k]), bv, bi)) {
+                bv = lo_f(v[k]);
+                bi = hi_i(v[k]);
+            }
     }
     for (int i = 0; i < n; ++i) st_pair(&rec[i], 0);
     return bi == INT_MAX ? 0 : bi;   // a row of -inf only: index 0, like numpy argmax
@@ -431,71 +448,128 @@ __device__ __forceinline__ void argmax_tile(const TileRaw<T> &r, int tile, int l
 // ---------------------------------------------------------------------------
 // Inverse-CDF search (one wavefront)
 // ---------------------------------------------------------------------------
+//
+// A finisher runs at the tail of the work it completes, so its cost is the
+// number of dependent memory round trips, not bandwidth.  Tile records are
+// visited in chunks of 512 tiles with lane l holding tiles 8l..8l+7 of the
+// chunk (all loaded at once); the crossing tile is loaded once into
+// registers.  A row of up to 512 tiles (V <= 1,048,576) costs two round
+// trips: its records, then its crossing tile.
 
-// Finds the first tile whose running mass exceeds `target`, masses given by
-// `mass(t)` for t < n.  Returns the tile and the mass before it, or -1.
-template <typename M>
-__device__ __forceinline__ int find_tile(int n, double target, int lane, M &&mass, double &before) {
+constexpr int kRecPerLane = 8;
+constexpr int kRecChunk = kWave * kRecPerLane;
+
+struct RecChunk {
+    uint64_t r[kRecPerLane];
+};
+
+__device__ __forceinline__ void load_chunk(const uint64_t *recs, int n, int t0, int lane,
+                                           RecChunk &c) {
+#pragma unroll
+    for (int i = 0; i < kRecPerLane; ++i) {
+        const int t = t0 + lane * kRecPerLane + i;
+        c.r[i] = t < n ? ld64(&recs[t]) : 0;
+    }
+}
+
+// Lane masses of one chunk: m[i] = mass_of(record) for tiles < n, else 0.
+template <typename MassOf>
+__device__ __forceinline__ double chunk_masses(const RecChunk &c, int n, int t0, int lane,
+                                               MassOf &&mass_of, double (&m)[kRecPerLane]) {
+    double ls = 0.0;
+#pragma unroll
+    for (int i = 0; i < kRecPerLane; ++i) {
+        const int t = t0 + lane * kRecPerLane + i;
+        m[i] = t < n ? mass_of(c.r[i]) : 0.0;
+        ls += m[i];
+    }
+    return ls;
+}
+
+template <typename Get, typename MassOf>
+__device__ __forceinline__ double row_total(int n, Get &&get, int lane, MassOf &&mass_of) {
+    double total = 0.0;
+    for (int t0 = 0; t0 < n; t0 += kRecChunk) {
+        RecChunk c;
+        get(t0, c);
+        double m[kRecPerLane];
+        const double ls = chunk_masses(c, n, t0, lane, mass_of, m);
+        total += __shfl(wave_incl_scan_d(ls, lane), kWave - 1);
+    }
+    return total;
+}
+
+// First tile whose running mass exceeds target (and the mass before it), or -1.
+template <typename Get, typename MassOf>
+__device__ __forceinline__ int row_find(int n, Get &&get, int lane, MassOf &&mass_of,
+                                        double target, double &before) {
     double base = 0.0;
-    for (int t0 = 0; t0 < n; t0 += kWave) {
-        const int t = t0 + lane;
-        const double m = t < n ? mass(t) : 0.0;
-        const double inc = wave_incl_scan_d(m, lane);
-        const unsigned long long hit = __ballot(t < n && base + inc > target);
+    for (int t0 = 0; t0 < n; t0 += kRecChunk) {
+        RecChunk c;
+        get(t0, c);
+        double m[kRecPerLane];
+        const double ls = chunk_masses(c, n, t0, lane, mass_of, m);
+        const double inc = wave_incl_scan_d(ls, lane);
+        double run = base + (inc - ls);
+        int first = -1;
+        double fb = 0.0;
+#pragma unroll
+        for (int i = 0; i < kRecPerLane; ++i) {
+            if (first < 0 && run + m[i] > target) {
+                first = i;
+                fb = run;
+            }
+            run += m[i];
+        }
+        const unsigned long long hit = __ballot(first >= 0);
         if (hit) {
             const int l = wave_first(hit);
-            before = base + __shfl(inc - m, l);
-            return t0 + l;
+            before = __shfl(fb, l);
+            return t0 + l * kRecPerLane + __shfl(first, l);
         }
         base += __shfl(inc, kWave - 1);
     }
     return -1;
 }
 
-template <typename M>
-__device__ __forceinline__ double total_mass(int n, int lane, M &&mass) {
-    double base = 0.0;
-    for (int t0 = 0; t0 < n; t0 += kWave) {
-        const int t = t0 + lane;
-        const double m = t < n ? mass(t) : 0.0;
-        base += __shfl(wave_incl_scan_d(m, lane), kWave - 1);
-    }
-    return base;
-}
-
-template <typename M>
-__device__ __forceinline__ int last_positive_tile(int n, int lane, M &&mass) {
+template <typename Get, typename MassOf>
+__device__ __forceinline__ int row_last_positive(int n, Get &&get, int lane, MassOf &&mass_of) {
     int best = -1;
-    for (int t0 = 0; t0 < n; t0 += kWave) {
-        const int t = t0 + lane;
-        const unsigned long long pos = __ballot(t < n && mass(t) > 0.0);
-        if (pos) best = t0 + 63 - __clzll((long long)pos);
+    for (int t0 = 0; t0 < n; t0 += kRecChunk) {
+        RecChunk c;
+        get(t0, c);
+        double m[kRecPerLane];
+        chunk_masses(c, n, t0, lane, mass_of, m);
+        int mine = -1;
+#pragma unroll
+        for (int i = 0; i < kRecPerLane; ++i)
+            if (m[i] > 0.0) mine = t0 + lane * kRecPerLane + i;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mine = max(mine, __shfl_xor(mine, o));
+        if (mine >= 0) best = mine;
     }
     return best;
 }
 
-// Within one tile, finds the first vocab index where before + running weight
-// exceeds target.  weight(i) returns the weight of vocab index i (0 past the
-// end of the row), reading the element from memory: the tile was just
-// streamed, so these are cache hits, and nothing tile-sized stays in
-// registers.  If rounding leaves the target unreached, returns the last index
-// with positive weight (-1 if none).
+// Within one tile held in registers, finds the first vocab index where
+// before + running weight exceeds target; weight(i) is the weight of the
+// lane's element i (group-major, 0..31; 0 past the end of the row).  If
+// rounding leaves the target unreached, returns the last index with positive
+// weight (-1 if none).
 template <typename W>
 __device__ __forceinline__ long long search_tile(W &&weight, int tile, int lane, double before,
                                                  double target) {
     double run = before;
-#pragma unroll 1
+#pragma unroll
     for (int g = 0; g < kGroupsPerTile; ++g) {
-        const long long i0 = elem_index(tile, lane, g * kGroupElems);
         double w[kGroupElems];
         double lsum = 0.0;
 #pragma unroll
         for (int e = 0; e < kGroupElems; ++e) {
-            w[e] = weight(i0 + e);
+            w[e] = weight(g * kGroupElems + e);
             lsum += w[e];
         }
         const double inc = wave_incl_scan_d(lsum, lane);
-        // each lane finds its own first crossing element
         double c = run + (inc - lsum);
         int first = -1;
 #pragma unroll
@@ -506,19 +580,17 @@ __device__ __forceinline__ long long search_tile(W &&weight, int tile, int lane,
         const unsigned long long hit = __ballot(first >= 0);
         if (hit) {
             const int l = wave_first(hit);
-            const int e = __shfl(first, l);
-            return elem_index(tile, l, g * kGroupElems + e);
+            return elem_index(tile, l, g * kGroupElems + __shfl(first, l));
         }
         run += __shfl(inc, kWave - 1);
     }
     long long last = -1;
-#pragma unroll 1
-    for (int g = 0; g < kGroupsPerTile; ++g) {
-        const long long i0 = elem_index(tile, lane, g * kGroupElems);
 #pragma unroll
-        for (int e = 0; e < kGroupElems; ++e)
-            if (weight(i0 + e) > 0.0) last = i0 + e > last ? i0 + e : last;
-    }
+    for (int i = 0; i < kLaneElems; ++i)
+        if (weight(i) > 0.0) {
+            const long long ei = elem_index(tile, lane, i);
+            last = ei > last ? ei : last;
+        }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         const long long ol = __shfl_xor(last, o);
@@ -547,7 +619,7 @@ __device__ __forceinline__ uint32_t *counter(uint32_t *base, int i) {
 // Decision for sequence c from its merged verify rows (wavefront 0 of the
 // workgroup that finished the sequence's last verify segment).
 template <typename T, int MODE>
-__device__ void decide(const StepArgs &a, int c, int lane) {
+__device__ __forceinline__ void decide(const StepArgs &a, int c, int lane) {
     const int L = a.L;
     const int CL = a.C * L;
     const bool valid = lane < L;
@@ -727,8 +799,8 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
                                         int wave, int lane) {
     const int rowid = c * a.L + k;
     const T *row = static_cast<const T *>(a.qn) + (long long)rowid * a.ld;
-    const int tb = seg * a.tps;
-    const int te = min(a.tiles_row, tb + a.tps);
+    const int tb = seg * a.tpsq;
+    const int te = min(a.tiles_row, tb + a.tpsq);
 
     if (MODE == kSample) {
         TileRec *tr = a.ws.tiles + (size_t)rowid * a.tiles_row;
@@ -740,54 +812,72 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
             const float ts = wave_sum(s);
             if (lane == 0) st_pair(&tr[tile], pack2(sm.ref, ts));
         });
-        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.S, &sh.flag)) return;
+        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.Sq, &sh.flag)) return;
         if (wave != 0) return;
 
         // ---- inverse-CDF draw over the whole row ----
+        const uint64_t *recs = reinterpret_cast<const uint64_t *>(tr);
+        const int nt = a.tiles_row;
+        RecChunk first;
+        load_chunk(recs, nt, 0, lane, first);
+        auto get = [&](int t0, RecChunk &c) {
+            if (t0 == 0) c = first;
+            else load_chunk(recs, nt, t0, lane, c);
+        };
         float cr = kNegInf;
-        for (int t = lane; t < a.tiles_row; t += kWave) cr = fmaxf(cr, lo_f(ld_pair(&tr[t])));
-        cr = wave_max(cr);
-        if (cr == kNegInf) {
-            if (lane == 0) {
-                atomicOr(&a.ws.ctl->error, kErrEmptyRow);
-                a.next_tokens[rowid] = 0;
-                if (a.qnext_x) a.qnext_x[rowid] = 0.0f;
-            }
-            for (int t = lane; t < a.tiles_row; t += kWave) st_pair(&tr[t], 0);
-            return;
+        for (int t0 = 0; t0 < nt; t0 += kRecChunk) {
+            RecChunk ch;
+            get(t0, ch);
+#pragma unroll
+            for (int i = 0; i < kRecPerLane; ++i)
+                if (t0 + lane * kRecPerLane + i < nt) cr = fmaxf(cr, lo_f(ch.r[i]));
         }
-        auto mass = [&](int t) -> double {
-            const uint64_t rc = ld_pair(&tr[t]);
+        cr = wave_max(cr);
+        auto mass = [&](uint64_t rc) -> double {
             const float ref = lo_f(rc);
             return ref == kNegInf ? 0.0 : (double)hi_f(rc) * pow2_int(ref - cr);
         };
-        const double S = total_mass(a.tiles_row, lane, mass);
-        const double target = (double)a.up[rowid] * S;
-        double before = 0.0;
-        double tile_target = target;
-        int tile = find_tile(a.tiles_row, target, lane, mass, before);
-        if (tile < 0) {
-            // rounding left the target unreached: clamp to the last positive weight
-            tile = max(0, last_positive_tile(a.tiles_row, lane, mass));
-            tile_target = __builtin_inf();
+        int token = 0;
+        double S = 0.0;
+        if (cr == kNegInf) {
+            if (lane == 0) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
+        } else {
+            S = row_total(nt, get, lane, mass);
+            const double target = (double)a.up[rowid] * S;
+            double before = 0.0;
+            double tile_target = target;
+            int tile = row_find(nt, get, lane, mass, target, before);
+            if (tile < 0) {
+                // rounding left the target unreached: clamp to the last positive weight
+                tile = max(0, row_last_positive(nt, get, lane, mass));
+                tile_target = __builtin_inf();
+            }
+            RecChunk tc;
+            get(tile - tile % kRecChunk, tc);
+            const int owner = (tile % kRecChunk) / kRecPerLane;
+            uint64_t trec = 0;
+#pragma unroll
+            for (int i = 0; i < kRecPerLane; ++i)
+                if (i == tile % kRecPerLane) trec = tc.r[i];
+            const float tref = lo_f(__shfl(trec, owner));
+            const double scale = pow2_int(tref - cr);
+            TileRaw<T> raw;
+            load_tile<T, VEC>(row, tile, a.V, lane, raw);
+            const float k2 = a.k2;
+            auto weight = [&](int i) -> double {
+                return (double)fast_exp2(fmaf(elem<T>(raw, i), k2, -tref)) * scale;
+            };
+            const long long tok = search_tile(weight, tile, lane, before, tile_target);
+            token = tok < 0 ? 0 : (int)tok;
         }
-        const float tref = lo_f(ld_pair(&tr[tile]));
-        const double scale = pow2_int(tref - cr);
-        const float k2 = a.k2;
-        const long long V = a.V;
-        auto weight = [&](long long i) -> double {
-            if (i >= V) return 0.0;
-            return (double)fast_exp2(fmaf(load_value<T>(row, i), k2, -tref)) * scale;
-        };
-        const long long tok = search_tile(weight, tile, lane, before, tile_target);
         // the tile masses are consumed: return them to zero
         for (int t = lane; t < a.tiles_row; t += kWave) st_pair(&tr[t], 0);
         if (lane == 0) {
-            const int token = tok < 0 ? 0 : (int)tok;
             a.next_tokens[rowid] = token;
             if (a.qnext_x) {
                 const float lv = load_value<T>(row, token);
-                a.qnext_x[rowid] = (float)(exp2((double)lv * (double)k2 - (double)cr) / S);
+                a.qnext_x[rowid] =
+                    S > 0.0 ? (float)(exp2((double)lv * (double)a.k2 - (double)cr) / S) : 0.0f;
             }
         }
     } else {
@@ -802,7 +892,7 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
             sh.idxs[wave] = bi;
         }
         __syncthreads();
-        ArgRec *recs = &a.ws.arg[((size_t)a.C * a.L + rowid) * a.S];
+        ArgRec *recs = &a.ws.arg[(size_t)a.C * a.L * a.smax + (size_t)rowid * a.Sq];
         if (threadIdx.x == 0) {
             float v = kNegInf;
             int i = INT_MAX;
@@ -813,9 +903,9 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
                 }
             st_pair(&recs[seg], pack2(v, i));
         }
-        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.S, &sh.flag)) return;
+        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.Sq, &sh.flag)) return;
         if (threadIdx.x == 0) {
-            a.next_tokens[rowid] = take_argrecs(recs, a.S);
+            a.next_tokens[rowid] = take_argrecs(recs, a.Sq);
             if (a.qnext_x) a.qnext_x[rowid] = 1.0f;
         }
     }
@@ -884,36 +974,38 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
     if (wave != 0) return;
     if (j < L) {
         // ---- inverse-CDF draw over max(0, P - Q) (P if that is empty) ----
-        auto mass_r = [&](int t) -> double { return (double)lo_f(ld_pair(&rt[t])); };
-        auto mass_p = [&](int t) -> double { return (double)hi_f(ld_pair(&rt[t])); };
-        double Z = total_mass(a.tiles_row, lane, mass_r);
+        const uint64_t *recs = reinterpret_cast<const uint64_t *>(rt);
+        const int nt = a.tiles_row;
+        RecChunk first;
+        load_chunk(recs, nt, 0, lane, first);
+        auto get = [&](int t0, RecChunk &c) {
+            if (t0 == 0) c = first;
+            else load_chunk(recs, nt, t0, lane, c);
+        };
+        auto mass_r = [&](uint64_t rc) -> double { return (double)lo_f(rc); };
+        auto mass_p = [&](uint64_t rc) -> double { return (double)hi_f(rc); };
+        double Z = row_total(nt, get, lane, mass_r);
         const bool use_p = !(Z > 0.0);
-        if (use_p) Z = total_mass(a.tiles_row, lane, mass_p);
+        if (use_p) Z = row_total(nt, get, lane, mass_p);
         const double target = (double)inf.u * Z;
         double before = 0.0;
         double tile_target = target;
-        int tile;
-        if (!use_p) {
-            tile = find_tile(a.tiles_row, target, lane, mass_r, before);
-            if (tile < 0) {
-                tile = last_positive_tile(a.tiles_row, lane, mass_r);
-                tile_target = __builtin_inf();
-            }
-        } else {
-            tile = find_tile(a.tiles_row, target, lane, mass_p, before);
-            if (tile < 0) {
-                tile = last_positive_tile(a.tiles_row, lane, mass_p);
-                tile_target = __builtin_inf();
-            }
+        int tile = use_p ? row_find(nt, get, lane, mass_p, target, before)
+                         : row_find(nt, get, lane, mass_r, target, before);
+        if (tile < 0) {
+            tile = use_p ? row_last_positive(nt, get, lane, mass_p)
+                         : row_last_positive(nt, get, lane, mass_r);
+            tile_target = __builtin_inf();
         }
         long long tok = 0;
         if (tile >= 0) {
+            TileRaw<T> rp, rq;
+            load_tile<T, VEC>(prow, tile, a.V, lane, rp);
+            load_tile<T, VEC>(qrow, tile, a.V, lane, rq);
             const float k2 = a.k2;
-            const long long V = a.V;
-            auto weight = [&](long long i) -> double {
-                if (i >= V) return 0.0;
-                const float P = fast_exp2(fmaf(load_value<T>(prow, i), k2, -inf.cp)) * inf.inv_sp;
-                const float Q = fast_exp2(fmaf(load_value<T>(qrow, i), k2, -inf.cq)) * inf.inv_sq;
+            auto weight = [&](int i) -> double {
+                const float P = fast_exp2(fmaf(elem<T>(rp, i), k2, -inf.cp)) * inf.inv_sp;
+                const float Q = fast_exp2(fmaf(elem<T>(rq, i), k2, -inf.cq)) * inf.inv_sq;
                 return use_p ? (double)P : (double)fmaxf(P - Q, 0.0f);
             };
             tok = search_tile(weight, tile, lane, before, tile_target);
@@ -946,12 +1038,26 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
         pq_item<T, VEC, MODE>(a, t, sh, wave, lane);
     } else if (t < a.n_items) {
         const int t2 = t - a.n_pq;
-        const int blk = a.q_blk + a.r_blk;
-        const int c = t2 / blk;
-        const int w = t2 - c * blk;
+        int c, w;
+        if (a.order == 0) {
+            // per sequence: its mask-row items, then its residual items
+            const int blk = a.q_blk + a.r_blk;
+            c = t2 / blk;
+            w = t2 - c * blk;
+        } else {
+            // every mask-row item, then every residual item
+            const int nq = a.C * a.q_blk;
+            if (t2 < nq) {
+                c = t2 / a.q_blk;
+                w = t2 - c * a.q_blk;
+            } else {
+                c = (t2 - nq) / a.r_blk;
+                w = a.q_blk + (t2 - nq) - c * a.r_blk;
+            }
+        }
         if (w < a.q_blk) {
-            const int k = w / a.S;
-            qn_item<T, VEC, MODE>(a, c, k, w - k * a.S, sh, wave, lane);
+            const int k = w / a.Sq;
+            qn_item<T, VEC, MODE>(a, c, k, w - k * a.Sq, sh, wave, lane);
         } else if (MODE == kSample) {
             res_item<T, VEC>(a, c, w - a.q_blk, sh, wave, lane);
         }

@@ -46,7 +46,7 @@ _SIGS = {
     "isd_step": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 15 + [_vp, _sz, _vp]),
     "isd_lm_head": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "isd_check_device_error": (ctypes.c_int, [_vp, _sz, _vp]),
-    "isd_set_tuning": (ctypes.c_int, [_i32, _i32, _i64]),
+    "isd_set_tuning": (ctypes.c_int, [_i32, _i32, _i32, _i64]),
     "isd_last_error": (ctypes.c_char_p, []),
 }
 
@@ -258,5 +258,7 @@ def check_device_error(ws: torch.Tensor):
     _check(lib().isd_check_device_error(_ptr(ws), ws.numel(), _stream()))
 
 
-def set_tuning(segments: int = 0, resid_segments: int = 0, spin_limit: int = 0):
-    _check(lib().isd_set_tuning(segments, resid_segments, spin_limit))
+def set_tuning(segments: int = 0, resid_segments: int = 0, spin_limit: int = 0,
+               propose_segments: int = 0):
+    """Process-wide decomposition knobs (0 = automatic)."""
+    _check(lib().isd_set_tuning(segments, propose_segments, resid_segments, spin_limit))

@@ -130,11 +130,12 @@ def test_lm_head_validation(isd):
 
 def test_tuning_validation(isd):
     lib = isd.lib()
-    assert lib.isd_set_tuning(-1, 0, 0) == 1
-    assert lib.isd_set_tuning(0, 1000, 0) == 1
-    assert lib.isd_set_tuning(0, 0, -5) == 1
-    assert lib.isd_set_tuning(4, 8, 100) == 0
-    assert lib.isd_set_tuning(0, 0, 0) == 0
+    assert lib.isd_set_tuning(-1, 0, 0, 0) == 1
+    assert lib.isd_set_tuning(0, 33, 0, 0) == 1
+    assert lib.isd_set_tuning(0, 0, 1000, 0) == 1
+    assert lib.isd_set_tuning(0, 0, 0, -5) == 1
+    assert lib.isd_set_tuning(4, 2, 8, 100) == 0
+    assert lib.isd_set_tuning(0, 0, 0, 0) == 0
 
 
 def test_binding_layout_checks(isd):
