@@ -13,7 +13,10 @@ Reported:
   value      verified positions per second = C*L / wall-clock time per step
   roofline   the step kernel against the HBM peak: algorithmic bytes per
              launch (every logit read once: 3*C*L*V*2 B) over the kernel's
-             mean duration, timed with events on its stream
+             average duration (two events on its stream around the K
+             back-to-back launches); `traffic` is the HBM bytes per launch
+             from rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated on a plain copy,
+             when profiles/ holds counters for the current kernel source
   cpu_baseline  the CPU oracle on a bounded sample of the same inputs,
              across the host's cores (process pool), in positions per second
 """
@@ -59,7 +62,25 @@ def parse():
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--resid-segments", type=int, default=0)
     ap.add_argument("--propose-segments", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, five times: under rocprofv3
+    counters its FETCH_SIZE and WRITE_SIZE per dispatch calibrate the counters
+    against a known byte count."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_calibration_bytes=n, dispatches=5)), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -99,10 +120,14 @@ def cpu_baseline(host_sets, cfg, target_s):
     per_seq = time.perf_counter() - t0
     n = int(max(cores, min(len(jobs_all) * 4, target_s * cores / max(per_seq, 1e-6))))
     jobs = [jobs_all[i % len(jobs_all)] for i in range(n)]
-    with mp.get_context("fork").Pool(cores) as pool:
+    pool = mp.get_context("fork").Pool(cores)
+    try:
         t0 = time.perf_counter()
         done = sum(pool.imap_unordered(_oracle_seq, jobs, chunksize=1))
         wall = time.perf_counter() - t0
+    finally:
+        pool.close()
+        pool.join()
     return dict(value=round(done * L / wall, 3), unit="positions/s", cores=cores, kind="oracle",
                 sample=f"{done} sequences ({done * L} positions) of the timed workload's "
                        f"resident input sets, fp64 numpy oracle, one process per core, "
@@ -113,6 +138,9 @@ def cpu_baseline(host_sets, cfg, target_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps(dict(error="this build runs on one GPU: the ISD step is measured "
@@ -165,18 +193,20 @@ def main():
     torch.cuda.synchronize()
     isd.check_device_error(call.ws)
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # two events on the launch stream bracket the K back-to-back launches
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
         bind(args.warmup + i)
-        starts[i].record(stream)
         call()
-        ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     isd.check_device_error(call.ws)
+    kernel_avg_ms = ev0.elapsed_time(ev1) / args.steps
 
     # untimed pass over the same steps for workload statistics
     n_stat = min(args.steps, 50)
@@ -189,12 +219,10 @@ def main():
         alphas[i].copy_(call.out["alpha"])
     torch.cuda.synchronize()
 
-    kernel_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     ms_per_step = wall * 1e3 / args.steps
     positions = C * L
     bytes_alg = 3 * C * L * V * 2
-    kernel_mean_s = float(kernel_ms.mean()) * 1e-3
-    achieved = bytes_alg / kernel_mean_s / 1e9
+    achieved = bytes_alg / (kernel_avg_ms * 1e-3) / 1e9
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -225,9 +253,7 @@ def main():
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic),
         hbm_gbs_wall=round(bytes_alg / (ms_per_step * 1e-3) / 1e9, 1),
-        kernel_us=dict(mean=round(float(kernel_ms.mean()) * 1e3, 2),
-                       median=round(float(np.median(kernel_ms)) * 1e3, 2),
-                       min=round(float(kernel_ms.min()) * 1e3, 2)),
+        kernel_us_avg=round(kernel_avg_ms * 1e3, 2),
         bytes_per_step=bytes_alg,
         accept_len_mean=round(float(acc.mean()), 4),
         alpha_mean=round(float(alphas.mean().item()), 5),

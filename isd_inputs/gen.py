@@ -141,11 +141,17 @@ def gen_step(cfg_id: int, step: int, seqs=None, cfg: dict | None = None,
     jobs = [(cfg_id, step, s, cfg) for s in seqs]
     if workers > 1 and n > 1:
         import multiprocessing as mp
-        with mp.get_context("fork").Pool(workers) as pool:
+        # workers exit on their own (close/join): a terminate() would signal
+        # them, which profilers that hook signals in forked children mishandle
+        pool = mp.get_context("fork").Pool(workers)
+        try:
             results = pool.imap(_gen_one, jobs, chunksize=max(1, n // (4 * workers)))
             for i, r in enumerate(results):
                 for key in ("p", "q", "qn", "x", "ua", "ur", "up"):
                     out[key][i] = r[key]
+        finally:
+            pool.close()
+            pool.join()
     else:
         for i, job in enumerate(jobs):
             r = _gen_one(job)
