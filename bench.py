@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -136,10 +136,106 @@ def cpu_baseline(host_sets, cfg, target_s):
 
 # ---------------------------------------------------------------------------
 
+def lm_head_workload(args):
+    """LM-head + ISD chain: per step, logits [C*2L, V] = h @ W on the matrix
+    cores, then one fused step that verifies the previous step's proposals
+    (q = the previous step's mask rows) against this step's anchor rows and
+    draws the next proposals from this step's mask rows."""
+    import torch
+
+    import speculative_verification_amd as isd
+    from isd_inputs import CONFIGS, gen_head_weights, gen_hidden, gen_uniforms
+
+    cfg = CONFIGS[4]
+    C, L, V, H, T = cfg["C"], cfg["L"], cfg["V"], cfg["H"], cfg["T"]
+    M = C * 2 * L
+    dev = torch.device("cuda", 0)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t_gen = time.perf_counter()
+    W = bf16(gen_head_weights(4))
+    hs = [bf16(gen_hidden(4, s)) for s in range(2)]
+    total = args.warmup + args.steps + 1
+    uni = torch.from_numpy(gen_uniforms(4, total)).to(dev)
+    logits = [torch.empty((M, V), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    xs = [torch.zeros((C, L), dtype=torch.int32, device=dev) for _ in range(2)]
+    torch.cuda.synchronize()
+    print(f"# W [{H}, {V}] and hidden states ready, {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+
+    def views(i):
+        ext = logits[i % 2].view(C, 2 * L, V)
+        return ext[:, :L], ext[:, L:]
+
+    # step -1: proposal-only bootstrap gives the first q and x
+    isd.lm_head(hs[0], W, out=logits[1])
+    _, qn0 = views(1)
+    isd.propose(qn0, uni[0, 2], temperature=T, out=dict(next_tokens=xs[1]))
+    ws = isd.workspace(isd.make_shape(views(0)[0]))
+    outs = [None, None]
+
+    def step(i):
+        h = hs[i % 2]
+        isd.lm_head(h, W, out=logits[i % 2])
+        p, qn = views(i)
+        _, q = views(i - 1)
+        o = isd.step(p, q, xs[(i - 1) % 2], uni[i + 1, 0], uni[i + 1, 1], qn, uni[i + 1, 2],
+                     temperature=T, ws=ws, out=dict(next_tokens=xs[i % 2]))
+        outs[i % 2] = o
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    isd.check_device_error(ws)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    t0 = time.perf_counter()
+    for n in range(args.steps):
+        i = args.warmup + n
+        h = hs[i % 2]
+        ev[3 * n].record(stream)
+        isd.lm_head(h, W, out=logits[i % 2])
+        ev[3 * n + 1].record(stream)
+        p, qn = views(i)
+        _, q = views(i - 1)
+        outs[i % 2] = isd.step(p, q, xs[(i - 1) % 2], uni[i + 1, 0], uni[i + 1, 1], qn,
+                               uni[i + 1, 2], temperature=T, ws=ws,
+                               out=dict(next_tokens=xs[i % 2]))
+        ev[3 * n + 2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    isd.check_device_error(ws)
+    gemm_ms = np.mean([ev[3 * n].elapsed_time(ev[3 * n + 1]) for n in range(args.steps)])
+    step_ms = np.mean([ev[3 * n + 1].elapsed_time(ev[3 * n + 2]) for n in range(args.steps)])
+    flops = 2.0 * M * H * V
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    step_bytes = 3 * C * L * V * 2
+    ms_per_step = wall * 1e3 / args.steps
+    acc = outs[(args.warmup + args.steps - 1) % 2]["accept_len"].float().mean().item()
+    print(json.dumps(dict(
+        metric="ISD verified positions/sec with the LM-head projection (h @ W on MFMA) in the step",
+        value=round(C * L / (ms_per_step * 1e-3), 1), unit="positions/s", n_gpus=1,
+        steps=args.steps, warmup=args.warmup, ms_per_step=round(ms_per_step, 4),
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload=f"LM head + ISD step: h [{M}, {H}] x W [{H}, {V}] bf16, then "
+                             f"C={C}, L={L} verify/propose", C=C, L=L, V=V, H=H),
+        gemm=dict(ms=round(float(gemm_ms), 4), tflops=round(gemm_tflops, 1),
+                  mfma_util=round(gemm_tflops / 2500.0, 4), peak_tflops=2500.0),
+        step=dict(us=round(float(step_ms) * 1e3, 2),
+                  hbm_gbs=round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+                  frac=round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
+        accept_len_mean_last=round(acc, 3))), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.config == 4:
+        lm_head_workload(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

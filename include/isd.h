@@ -17,9 +17,12 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Layout.  Logits are row-major [C, L, V] with V innermost and `ld` elements
- *   between consecutive rows (ld >= V); row (c, k) starts at element
- *   (c*L + k)*ld.  Token and uniform arrays are dense [C, L] (row-major).
+ * Layout.  Logits rows are V contiguous elements; row (c, k) starts at
+ *   element c*ldc + k*ld of its buffer, with ld >= V and ldc either 0 (which
+ *   means L*ld, a dense [C, L, V] tensor) or >= L*ld.  A [C, 2L, V] extend
+ *   output whose first L rows per sequence are anchors and last L are mask
+ *   rows is passed as p = base, qnext = base + L*ld, ld = V, ldc = 2L*V.
+ *   Token and uniform arrays are dense [C, L] (row-major).
  *   p_logits[c, k] is the anchor row that scores proposal x[c, k] (the
  *   next-token logit shift is applied by the caller); q_logits[c, k] is the
  *   proposal row that generated x[c, k]; qnext_logits[c, k] is the mask row
@@ -45,7 +48,8 @@
  *   decision boundary can come out differently.
  * Errors.  On a non-OK status nothing has been enqueued and no output or
  *   workspace byte is touched; isd_last_error() then describes the problem.
- *     ISD_ERR_ARG          bad shape (C < 1, L not in [1, 64], V < 1, ld < V),
+ *     ISD_ERR_ARG          bad shape (C < 1, L not in [1, 64], V < 1, ld < V,
+ *                          0 < ldc < L*ld),
  *                          a required NULL pointer, a base not aligned to its
  *                          element size, or T <= 0 / non-finite in sample mode
  *     ISD_ERR_UNSUPPORTED  unknown dtype or mode
@@ -91,6 +95,7 @@ typedef struct {
     int32_t dtype;       /* isd_dtype_t of every logits tensor */
     int32_t mode;        /* isd_mode_t */
     float temperature;   /* softmax temperature T > 0 (sample mode) */
+    int64_t ldc;         /* elements between sequences c and c+1 (0: L*ld) */
 } isd_shape_t;
 
 /* Workspace bytes needed by any call on shape `s`; 0 if `s` is invalid. */

@@ -63,6 +63,9 @@ isd_status_t check_shape(const isd_shape_t *s, bool need_temperature) {
     if (s->L < 1 || s->L > kMaxL) return fail(ISD_ERR_ARG, "L must be in [1, 64] (got %d)", (int)s->L);
     if (s->V < 1) return fail(ISD_ERR_ARG, "V must be >= 1 (got %d)", (int)s->V);
     if (s->ld < (int64_t)s->V) return fail(ISD_ERR_ARG, "ld (%lld) must be >= V (%d)", (long long)s->ld, (int)s->V);
+    if (s->ldc != 0 && s->ldc < (int64_t)s->L * s->ld)
+        return fail(ISD_ERR_ARG, "ldc (%lld) must be 0 or >= L*ld (%lld)", (long long)s->ldc,
+                    (long long)s->L * (long long)s->ld);
     const long long rows = (long long)s->C * s->L;
     if (rows > (1LL << 24)) return fail(ISD_ERR_ARG, "C*L too large (%lld)", rows);
     if (need_temperature && s->mode == ISD_MODE_SAMPLE &&
@@ -85,9 +88,12 @@ isd_status_t check_ptr(const void *p, const char *name, size_t align) {
         if (st_ != ISD_OK) return st_;     \
     } while (0)
 
+int64_t seq_stride(const isd_shape_t *s) { return s->ldc ? s->ldc : (int64_t)s->L * s->ld; }
+
 bool vec_ok(const isd_shape_t *s, const void *a, const void *b, const void *c) {
     const size_t es = elem_size(s);
     if (((size_t)s->ld * es) % 16) return false;
+    if (((size_t)seq_stride(s) * es) % 16) return false;
     for (const void *p : {a, b, c})
         if (p && ((uintptr_t)p) % 16) return false;
     return true;
@@ -111,6 +117,7 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
     a.L = L;
     a.V = V;
     a.ld = (long long)s->ld;
+    a.ldc = (long long)seq_stride(s);
     a.k2 = greedy ? 1.0f : (float)(1.4426950408889634 / (double)s->temperature);
     a.ws = workspace_at(workspace, lay);
     a.tiles_row = ceil_div(V, kTileElems);

@@ -95,7 +95,8 @@ Workspace workspace_at(void *base, const WorkspaceLayout &lay);
 // Everything one launch of the step kernel needs (passed by value).
 struct StepArgs {
     int C, L, V;
-    long long ld;
+    long long ld;              // elements between rows (c, k) and (c, k + 1)
+    long long ldc;             // elements between rows (c, k) and (c + 1, k)
     float k2;                  // log2(e) / T
     // inputs
     const void *p, *q, *qn;

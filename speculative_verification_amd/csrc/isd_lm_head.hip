@@ -1,6 +1,166 @@
+// LM-head projection on the matrix cores: logits[M, N] = h[M, K] @ w[K, N].
+//
+// bf16 operands, fp32 accumulation with v_mfma_f32_32x32x16_bf16, bf16 output
+// rounded to nearest even.  The projection produces every anchor and mask
+// row that the ISD step consumes ("Introspective Diffusion Language Models |
+// Summary", section 3.3: one extend forward yields both).
+//
+// Tiling: a 256-thread workgroup owns a 256 x 128 output tile and walks K in
+// steps of 64 through two LDS buffers (the next step's global loads are in
+// flight while the current one is multiplied).  Its four wavefronts form a
+// 2 x 2 grid of 128 x 64 sub-tiles, each 4 x 2 MFMA tiles of 32 x 32.
+//
+// The MFMA operands need 8 consecutive k per lane.  h is k-contiguous; w is
+// n-contiguous, so its tile is transposed on the way into LDS ([n][k]).
+// Tiles are ordered so that one XCD owns a contiguous range of N-tiles with
+// all their M-tiles: the M-tiles that share a w tile read it through the same
+// L2, and w streams from HBM about once.
+
 #include "isd_internal.h"
+
 namespace isd {
-hipError_t launch_lm_head(const uint16_t *, const uint16_t *, int, int, int, uint16_t *, hipStream_t) {
-    return hipErrorNotSupported;
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 256, kBN = 128, kBK = 64;
+constexpr int kLdsPad = 8;              // bf16 of padding per LDS row
+constexpr int kLdA = kBK + kLdsPad;     // A tile row (m) length in LDS
+constexpr int kLdB = kBK + kLdsPad;     // transposed B tile row (n) length in LDS
+constexpr int kXcds = 8;
+constexpr int kThreadsG = 256;
+constexpr int kAVecRow = kBK / 8;                       // 16-byte vectors per A row per step
+constexpr int kAPerThread = kBM * kBK / 8 / kThreadsG;  // A vectors each thread moves per step
+constexpr int kBVecRow = kBN / 8;                       // 16-byte vectors per w row per step
+constexpr int kBPerThread = kBK * kBN / 8 / kThreadsG;  // w vectors each thread moves per step
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
 }
+
+__global__ __launch_bounds__(256) void lm_head_kernel(const uint16_t *__restrict__ h,
+                                                      const uint16_t *__restrict__ w, int M, int K,
+                                                      int N, uint16_t *__restrict__ out,
+                                                      int m_tiles, int total, int per_xcd) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdA];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kLdB];
+
+    const int b = blockIdx.x;
+    const int idx = (b % kXcds) * per_xcd + b / kXcds;
+    if (idx >= total) return;
+    const int m0 = (idx % m_tiles) * kBM;
+    const int n0 = (idx / m_tiles) * kBN;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64;
+    const int wm = wave / 2, wn = wave % 2;
+
+    // global -> register mapping of one K step: A is kBM rows of kAVecRow
+    // vectors of 8 k, w is kBK rows of kBVecRow vectors of 8 n; thread tid
+    // moves vectors tid, tid + 256, ...
+    uint4 ra[kAPerThread], rb[kBPerThread];
+    auto load_step = [&](int k0) {
+#pragma unroll
+        for (int r = 0; r < kAPerThread; ++r) {
+            const int v = tid + kThreadsG * r;
+            const int row = m0 + v / kAVecRow, kk = k0 + (v % kAVecRow) * 8;
+            ra[r] = row < M ? *reinterpret_cast<const uint4 *>(h + (size_t)row * K + kk)
+                            : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < kBPerThread; ++r) {
+            const int v = tid + kThreadsG * r;
+            const int kk = k0 + v / kBVecRow, col = n0 + (v % kBVecRow) * 8;
+            rb[r] = col < N ? *reinterpret_cast<const uint4 *>(w + (size_t)kk * N + col)
+                            : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_step = [&](int s) {
+#pragma unroll
+        for (int r = 0; r < kAPerThread; ++r) {
+            const int v = tid + kThreadsG * r;
+            *reinterpret_cast<uint4 *>(&As[s][(v / kAVecRow) * kLdA + (v % kAVecRow) * 8]) = ra[r];
+        }
+#pragma unroll
+        for (int r = 0; r < kBPerThread; ++r) {
+            const int v = tid + kThreadsG * r;
+            const int kk = v / kBVecRow, nb = (v % kBVecRow) * 8;
+            const uint32_t wd[4] = {rb[r].x, rb[r].y, rb[r].z, rb[r].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                Bs[s][(nb + e) * kLdB + kk] = (uint16_t)(wd[e / 2] >> (16 * (e % 2)));
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+
+    const int nk = K / kBK;
+    load_step(0);
+    store_step(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s = kt & 1;
+        if (kt + 1 < nk) load_step((kt + 1) * kBK);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            const int kk = ks * 16 + 8 * (lane / 32);
+            bf16x8 af[4], bfr[2];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                af[mi] = *reinterpret_cast<const bf16x8 *>(
+                    &As[s][(wm * 128 + mi * 32 + lane % 32) * kLdA + kk]);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                bfr[ni] = *reinterpret_cast<const bf16x8 *>(
+                    &Bs[s][(wn * 64 + ni * 32 + lane % 32) * kLdB + kk]);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+        }
+        if (kt + 1 < nk) store_step(s ^ 1);
+        __syncthreads();
+    }
+
+    // D layout of a 32 x 32 tile: lane holds column lane % 32, rows
+    // 8 * (i / 4) + 4 * (lane / 32) + i % 4 for its 16 values i.
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+            const int col = n0 + wn * 64 + ni * 32 + lane % 32;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * 128 + mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+                if (row < M && col < N) out[(size_t)row * N + col] = bf16_rne(acc[mi][ni][i]);
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, int N, uint16_t *out,
+                          hipStream_t stream) {
+    const int m_tiles = (M + kBM - 1) / kBM;
+    const int n_tiles = (N + kBN - 1) / kBN;
+    const long long total = (long long)m_tiles * n_tiles;
+    if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
+    const int per_xcd = (int)((total + kXcds - 1) / kXcds);
+    hipLaunchKernelGGL(lm_head_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, h,
+                       w, M, K, N, out, m_tiles, (int)total, per_xcd);
+    return hipGetLastError();
+}
+
 }  // namespace isd

@@ -603,6 +603,11 @@ __device__ __forceinline__ long long search_tile(W &&weight, int tile, int lane,
 // The kernel
 // ---------------------------------------------------------------------------
 
+// Element offset of logits row (c, k).
+__device__ __forceinline__ long long row_offset(const StepArgs &a, int c, int k) {
+    return (long long)c * a.ldc + (long long)k * a.ld;
+}
+
 struct Shared {
     int flag;
     float refs[kWavesPerGroup];
@@ -638,7 +643,7 @@ __device__ __forceinline__ void decide(const StepArgs &a, int c, int lane) {
             take_segrecs(&a.ws.seg[((size_t)CL + (size_t)c * L + kk) * a.S], a.S, cq, sq);
             if (sp <= 0.0 || sq <= 0.0) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
             if (!bad) {
-                const long long off = (long long)(c * L + kk) * a.ld + xk;
+                const long long off = row_offset(a, c, kk) + xk;
                 const float lp = load_value<T>(static_cast<const T *>(a.p), off);
                 const float lq = load_value<T>(static_cast<const T *>(a.q), off);
                 const double k2 = (double)a.k2;
@@ -742,7 +747,7 @@ __device__ __forceinline__ void pq_item(const StepArgs &a, int t, Shared &sh, in
     const int CL = a.C * a.L;
     const int k = MODE == kSample ? slot >> 1 : slot;
     const int which = MODE == kSample ? (slot & 1) : 0;
-    const T *row = static_cast<const T *>(which ? a.q : a.p) + (long long)(c * a.L + k) * a.ld;
+    const T *row = static_cast<const T *>(which ? a.q : a.p) + row_offset(a, c, k);
     const int tb = seg * a.tps;
     const int te = min(a.tiles_row, tb + a.tps);
     const size_t rec = ((size_t)which * CL + (size_t)c * a.L + k) * a.S + seg;
@@ -798,7 +803,7 @@ template <typename T, bool VEC, int MODE>
 __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg, Shared &sh,
                                         int wave, int lane) {
     const int rowid = c * a.L + k;
-    const T *row = static_cast<const T *>(a.qn) + (long long)rowid * a.ld;
+    const T *row = static_cast<const T *>(a.qn) + row_offset(a, c, k);
     const int tb = seg * a.tpsq;
     const int te = min(a.tiles_row, tb + a.tpsq);
 
@@ -941,8 +946,8 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
     const int L = a.L;
     const int j = inf.j;
     ResTile *rt = a.ws.rtiles + (size_t)c * a.tiles_row;
-    const T *prow = static_cast<const T *>(a.p) + (long long)(c * L + (j < L ? j : 0)) * a.ld;
-    const T *qrow = static_cast<const T *>(a.q) + (long long)(c * L + (j < L ? j : 0)) * a.ld;
+    const T *prow = static_cast<const T *>(a.p) + row_offset(a, c, j < L ? j : 0);
+    const T *qrow = static_cast<const T *>(a.q) + row_offset(a, c, j < L ? j : 0);
 
     if (j < L) {
         const int tb = seg * a.tpsr;

@@ -34,7 +34,7 @@ class IsdError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("C", ctypes.c_int32), ("L", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("ld", ctypes.c_int64), ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
-                ("temperature", ctypes.c_float)]
+                ("temperature", ctypes.c_float), ("ldc", ctypes.c_int64)]
 
 
 _vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
@@ -86,8 +86,8 @@ def _stream():
 
 
 def _logits_layout(t: torch.Tensor):
-    """(C, L, V, ld, dtype code) of a [C, L, V] logits tensor with unit
-    innermost stride and evenly spaced rows."""
+    """(C, L, V, ld, ldc, dtype code) of a [C, L, V] logits view whose rows are
+    contiguous: row (c, k) starts at element c*stride(0) + k*stride(1)."""
     if t.dim() != 3:
         raise ValueError("logits must be [C, L, V]")
     if t.dtype == torch.bfloat16:
@@ -99,17 +99,26 @@ def _logits_layout(t: torch.Tensor):
     C, L, V = t.shape
     if t.stride(2) != 1 and V > 1:
         raise ValueError("logits rows must be contiguous")
-    ld = t.stride(1) if L > 1 else (t.stride(0) if C > 1 else V)
-    if C > 1 and L > 1 and t.stride(0) != L * ld:
-        raise ValueError("logits rows must be evenly spaced")
-    if C > 1 and L == 1:
-        ld = t.stride(0)
-    return C, L, V, max(int(ld), V), code
+    ld = int(t.stride(1)) if L > 1 else V
+    ld = max(ld, V)
+    ldc = int(t.stride(0)) if C > 1 else L * ld
+    if ldc < L * ld:
+        raise ValueError("sequences of a logits view must not overlap (stride(0) >= L*stride(1))")
+    return C, L, V, ld, ldc, code
 
 
 def make_shape(logits: torch.Tensor, mode: int = MODE_SAMPLE, temperature: float = 1.0) -> Shape:
-    C, L, V, ld, code = _logits_layout(logits)
-    return Shape(C, L, V, ld, code, mode, float(temperature))
+    C, L, V, ld, ldc, code = _logits_layout(logits)
+    return Shape(C, L, V, ld, code, mode, float(temperature), ldc)
+
+
+def _same_layout(ref: Shape, t, name: str, mode: int, temperature: float):
+    """Every logits tensor of a call is read with the layout of the first."""
+    if t is None:
+        return
+    s = make_shape(t, mode, temperature)
+    if (s.C, s.L, s.V, s.ld, s.ldc, s.dtype) != (ref.C, ref.L, ref.V, ref.ld, ref.ldc, ref.dtype):
+        raise ValueError(f"{name} must have the same shape, dtype and strides as the anchor logits")
 
 
 def _mode_code(mode) -> int:
@@ -153,6 +162,8 @@ def verify_step(p, q, x, ua, ur, *, mode="sample", temperature=1.0, out=None, ws
     """Verify proposals x [C, L] against anchor rows p (and proposal rows q)."""
     m = _mode_code(mode)
     shape = make_shape(p, m, temperature)
+    if m == MODE_SAMPLE:
+        _same_layout(shape, q, "q", m, temperature)
     C, L, dev = shape.C, shape.L, p.device
     o = dict(accept_len=_out(out, "accept_len", (C,), torch.int32, dev),
              out_tokens=_out(out, "out_tokens", (C, L), torch.int32, dev),
@@ -185,6 +196,8 @@ def alpha(p, q, x, *, mode="sample", temperature=1.0, out=None, ws=None):
     """Introspective acceptance rate per sequence and its batch mean."""
     m = _mode_code(mode)
     shape = make_shape(p, m, temperature)
+    if m == MODE_SAMPLE:
+        _same_layout(shape, q, "q", m, temperature)
     dev = p.device
     o = dict(alpha=_out(out, "alpha", (shape.C,), torch.float32, dev),
              alpha_mean=_out(out, "alpha_mean", (1,), torch.float32, dev))
@@ -202,8 +215,9 @@ class StepCall:
                  ws=None):
         m = _mode_code(mode)
         self.shape = make_shape(p, m, temperature)
-        if make_shape(qn, m, temperature).ld != self.shape.ld or qn.shape != p.shape:
-            raise ValueError("p and qn must share shape and row stride")
+        _same_layout(self.shape, qn, "qn", m, temperature)
+        if m == MODE_SAMPLE:
+            _same_layout(self.shape, q, "q", m, temperature)
         C, L, dev = self.shape.C, self.shape.L, p.device
         self.out = dict(accept_len=_out(out, "accept_len", (C,), torch.int32, dev),
                         out_tokens=_out(out, "out_tokens", (C, L), torch.int32, dev),

@@ -148,3 +148,19 @@ def test_binding_layout_checks(isd):
     assert (s.V, s.ld, s.dtype) == (10, 16, 1)
     with pytest.raises(ValueError):
         isd.make_shape(torch.zeros((2, 3, 10), dtype=torch.float16))
+
+
+def test_sequence_stride(isd):
+    import torch
+    lib = isd.lib()
+    bad = _shape(isd, C=4, L=8, V=1000, ld=1000)
+    bad.ldc = 7999                      # below L*ld: sequences would overlap
+    assert _verify(isd, bad) == 1 and "ldc" in lib.isd_last_error().decode()
+    ext = torch.zeros((3, 2 * 5, 64), dtype=torch.bfloat16)   # [C, 2L, V] extend output
+    sp, sq = isd.make_shape(ext[:, :5]), isd.make_shape(ext[:, 5:])
+    assert (sp.C, sp.L, sp.V, sp.ld, sp.ldc) == (3, 5, 64, 64, 640)
+    assert (sq.ld, sq.ldc) == (64, 640)
+    dense = torch.zeros((3, 5, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="same shape"):
+        isd.isd._same_layout(sp, dense, "q", 0, 1.0)
+    isd.isd._same_layout(sp, ext[:, 5:], "q", 0, 1.0)

@@ -1,0 +1,88 @@
+"""GPU parity of the LM-head projection (isd_lm_head) against the fp64 oracle.
+
+The kernel accumulates in fp32 and rounds once to bf16 (nearest even).  Each
+output must lie within half a bf16 ulp of the exact product plus the fp32
+accumulation bound K * 2^-24 * sum_k |h_k w_k|, and almost every output must
+equal the exact product rounded to bf16.
+"""
+
+import numpy as np
+import pytest
+
+from isd_inputs import CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, gen_head_weights, gen_hidden
+from oracle import isd_oracle as O
+from tests.isd_testlib import log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def isd():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import speculative_verification_amd as isd_mod
+    isd_mod.lib()
+    return isd_mod
+
+
+def _dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _check(gpu_bits, h_bits, w_bits, rows):
+    """Compare output rows `rows` with the fp64 product."""
+    h = bf16_bits_to_f32(h_bits[rows]).astype(np.float64)
+    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    exact = O.lm_head(h, w)
+    absdot = np.abs(h) @ np.abs(w)
+    got = bf16_bits_to_f32(gpu_bits[rows]).astype(np.float64)
+    rne = bf16_bits_to_f32(f32_to_bf16_bits(exact.astype(np.float32))).astype(np.float64)
+    mag = np.maximum(np.abs(exact), 1e-30)
+    half_ulp = np.exp2(np.floor(np.log2(mag)) - 8)
+    K = h.shape[1]
+    bound = half_ulp + K * 2.0 ** -24 * absdot
+    err = np.abs(got - exact)
+    worst = np.max(err / bound)
+    assert worst <= 1.0, f"max error / bound = {worst}"
+    frac_rne = np.mean(got == rne)
+    assert frac_rne >= 0.999, f"only {frac_rne:.5f} of outputs equal the rounded exact product"
+    return worst, frac_rne
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 256, 1000), (64, 4096, 2048), (257, 128, 136)])
+def test_lm_head_small_shapes(isd, M, K, N):
+    import torch
+    rng = np.random.default_rng(M * 7 + N)
+    h_bits = f32_to_bf16_bits(rng.normal(0, 1, (M, K)).astype(np.float32))
+    w_bits = f32_to_bf16_bits(rng.normal(0, 0.02, (K, N)).astype(np.float32))
+    out = isd.lm_head(_dev_bf16(h_bits), _dev_bf16(w_bits))
+    torch.cuda.synchronize()
+    gpu = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    worst, frac = _check(gpu, h_bits, w_bits, np.arange(M))
+    log(f"lm_head {M}x{K}x{N}: worst err/bound {worst:.3f}, exact-rounded fraction {frac:.5f}")
+
+
+def test_lm_head_full_shape_sampled_rows(isd):
+    """The LM-head workload: h [1024, 4096] x W [4096, 151936]."""
+    import torch
+    cfg = CONFIGS[4]
+    log("lm_head full shape: generating W")
+    w_bits = gen_head_weights(4)
+    h_bits = gen_hidden(4, 0)
+    out = isd.lm_head(_dev_bf16(h_bits), _dev_bf16(w_bits))
+    torch.cuda.synchronize()
+    gpu = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert gpu.shape == (cfg["C"] * 2 * cfg["L"], cfg["V"])
+    rows = np.array([0, 1, 255, 256, 511, 700, 1022, 1023])
+    worst, frac = _check(gpu, h_bits, w_bits, rows)
+    log(f"lm_head full shape, rows {rows.tolist()}: worst err/bound {worst:.3f}, "
+        f"exact-rounded fraction {frac:.5f}")
+
+
+def test_lm_head_rejects_bad_shapes(isd):
+    import torch
+    h = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(isd.IsdError):
+        isd.lm_head(h, w)

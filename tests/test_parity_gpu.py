@@ -375,3 +375,31 @@ def test_workspace_returns_to_zero_across_shapes(isd):
             torch.cuda.synchronize()
             nz = torch.nonzero(ws).flatten()[:8].tolist()
             assert not nz, f"workspace not zero after C={C} L={L} V={V} {mode}: bytes {nz}"
+
+
+def test_extend_layout_matches_dense(isd):
+    """Anchor and mask rows interleaved per sequence ([C, 2L, V], as one extend
+    forward produces them) give bitwise the same results as dense tensors."""
+    import torch
+    rng = np.random.default_rng(31)
+    C, L, V = 6, 8, 20000
+    d, bufs = _make_inputs(rng, C, L, V, "bf16")
+    dense = _device_views(d, bufs, "bf16", V)
+    ext_bits = np.empty((C, 2 * L, V), np.uint16)
+    ext_bits[:, :L] = d["p"]
+    ext_bits[:, L:] = d["qn"]
+    ext = torch.from_numpy(ext_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    prev_bits = np.zeros((C, 2 * L, V), np.uint16)   # the previous extend output's mask rows
+    prev_bits[:, L:] = d["q"]
+    prev = torch.from_numpy(prev_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    a = _run(isd, dense, dict(mode="sample", T=1.0))
+    with pytest.raises(ValueError):
+        isd.step(ext[:, :L], dense["q"], dense["x"], dense["ua"], dense["ur"], ext[:, L:],
+                 dense["up"])
+    o = isd.step(ext[:, :L], prev[:, L:], dense["x"], dense["ua"], dense["ur"], ext[:, L:],
+                 dense["up"])
+    torch.cuda.synchronize()
+    b = to_host(o)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    compare(b, oracle_step(d, "bf16", "sample", 1.0), label="extend layout")
