@@ -129,47 +129,54 @@ __device__ __forceinline__ uint32_t load_bits(const T *p) {
     else return *reinterpret_cast<const uint32_t *>(p);
 }
 
-// Lane `lane`'s 32 elements of tile `tile` of `row`; elements at or past V
-// read as -inf and are never loaded.
+// One lane's 8-element group at element offset i of `row` (8 consecutive
+// elements); elements at or past V read as -inf and are never loaded.  With
+// VEC the group is one or two 16-byte non-temporal loads when it lies wholly
+// below V: the logits are streamed once, and non-temporal loads keep them
+// from displacing useful cache lines and measurably raise the read rate.
 template <typename T, bool VEC>
-__device__ __forceinline__ void load_tile(const T *__restrict__ row, int tile, int V, int lane,
-                                          TileRaw<T> &r) {
-    const long long base = (long long)tile * kTileElems + lane * kGroupElems;
-    const bool full = (long long)(tile + 1) * kTileElems <= (long long)V;
-    if (VEC && full) {
-        // streamed once: non-temporal loads keep the logits from displacing
-        // useful cache lines and measurably raise the achieved read rate
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(row + base);
-        constexpr int kVecPerGroup = kGroupElems * (int)sizeof(T) / 16;  // 1 (bf16) or 2 (fp32)
-        constexpr int kGroupStride = kWave * kGroupElems * (int)sizeof(T) / 16;
+__device__ __forceinline__ void load_group(const T *__restrict__ row, long long i, int V, bool whole,
+                                           uint32_t *w) {
+    constexpr int kVecPerGroup = kGroupElems * (int)sizeof(T) / 16;   // 1 (bf16) or 2 (fp32)
+    if (VEC && whole) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(row + i);
 #pragma unroll
-        for (int g = 0; g < kGroupsPerTile; ++g) {
-#pragma unroll
-            for (int h = 0; h < kVecPerGroup; ++h) {
-                const u32x4 v = __builtin_nontemporal_load(&src[g * kGroupStride + h]);
-                const int w0 = (g * kVecPerGroup + h) * 4;
-                r.w[w0 + 0] = v.x;
-                r.w[w0 + 1] = v.y;
-                r.w[w0 + 2] = v.z;
-                r.w[w0 + 3] = v.w;
-            }
+        for (int h = 0; h < kVecPerGroup; ++h) {
+            const u32x4 v = __builtin_nontemporal_load(&src[h]);
+            w[h * 4 + 0] = v.x;
+            w[h * 4 + 1] = v.y;
+            w[h * 4 + 2] = v.z;
+            w[h * 4 + 3] = v.w;
         }
     } else {
 #pragma unroll
-        for (int g = 0; g < kGroupsPerTile; ++g) {
-#pragma unroll
-            for (int e = 0; e < kGroupElems; ++e) {
-                const long long i = base + g * (kWave * kGroupElems) + e;
-                const uint32_t b = (i < (long long)V) ? load_bits<T>(row + i) : neg_inf_bits<T>();
-                const int idx = g * kGroupElems + e;
-                if constexpr (sizeof(T) == 2) {
-                    if (idx & 1) r.w[idx >> 1] |= b << 16;
-                    else r.w[idx >> 1] = b;
-                } else {
-                    r.w[idx] = b;
-                }
+        for (int e = 0; e < kGroupElems; ++e) {
+            const uint32_t b = (i + e < (long long)V) ? load_bits<T>(row + i + e) : neg_inf_bits<T>();
+            if constexpr (sizeof(T) == 2) {
+                if (e & 1) w[e >> 1] |= b << 16;
+                else w[e >> 1] = b;
+            } else {
+                w[e] = b;
             }
         }
+    }
+}
+
+// Lane `lane`'s 32 elements of tile `tile` of `row`; elements at or past V
+// read as -inf and are never loaded.  In the last, partial tile of a row the
+// groups wholly below V still take the vector path, so that tile costs about
+// what a full one does.
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_tile(const T *__restrict__ row, int tile, int V, int lane,
+                                          TileRaw<T> &r) {
+    constexpr int kWordsPerGroup = kGroupElems * (int)sizeof(T) / 4;
+    const long long base = (long long)tile * kTileElems + lane * kGroupElems;
+    const bool full = (long long)(tile + 1) * kTileElems <= (long long)V;
+#pragma unroll
+    for (int g = 0; g < kGroupsPerTile; ++g) {
+        const long long i = base + g * (kWave * kGroupElems);
+        load_group<T, VEC>(row, i, V, full || i + kGroupElems <= (long long)V,
+                           &r.w[g * kWordsPerGroup]);
     }
 }
 
