@@ -158,6 +158,65 @@ isd_status_t isd_step(const isd_shape_t *s,
                       int32_t *next_tokens, float *qnext_x,
                       void *workspace, size_t ws_bytes, void *stream);
 
+/* ---- The multi-step decoding loop (section 3.2) ----------------------------
+ * After every proposal passes, one more token is drawn from the final causal
+ * anchor (the bonus); after a rejection the next step only proposes (a
+ * recovery step that draws one token from the anchor of the last clean
+ * position).  A sequence is in state 0 (recovery) or 1 (verify).  One loop
+ * step for a batch with rows p [C, L+1, V] (rows 0..L-1 verify, row L is the
+ * bonus anchor, row 0 is the anchor of a recovering sequence), q, qn [C, L, V]:
+ *   1. isd_step_masked with verify_mask = state (recovering sequences verify
+ *      nothing) and propose_mask NULL;
+ *   2. isd_decode_masks: bonus_mask = state == 1 && accept_len == L,
+ *      anchor_mask = state == 0;
+ *   3. isd_propose_masked on rows p[:, L] (shape L = 1) with bonus_mask, and
+ *      on rows p[:, 0] with anchor_mask;
+ *   4. isd_decode_commit: appends the emitted tokens, counts tokens and
+ *      forwards, and moves each sequence to its next state. */
+
+/* isd_step with per-sequence masks (int32 [C], nonzero = active; NULL = all).
+ * A sequence outside verify_mask reads no p, q or x row and gets
+ * accept_len -1, n_emitted 0, out_tokens -1, p_x = q_x = alpha = 0.  A
+ * sequence outside propose_mask reads no qn row and gets next_tokens -1 and
+ * qnext_x 0.  Other sequences get exactly what isd_step gives them. */
+isd_status_t isd_step_masked(const isd_shape_t *s,
+                             const void *p_logits, const void *q_logits,
+                             const int32_t *proposals,
+                             const float *u_accept, const float *u_resid,
+                             const void *qnext_logits, const float *u_propose,
+                             const int32_t *verify_mask, const int32_t *propose_mask,
+                             int32_t *accept_len, int32_t *out_tokens, int32_t *n_emitted,
+                             float *p_x, float *q_x, float *alpha,
+                             int32_t *next_tokens, float *qnext_x,
+                             void *workspace, size_t ws_bytes, void *stream);
+
+/* isd_propose with a per-sequence mask (int32 [C], nonzero = draw; NULL =
+ * all); masked-out sequences read no row and get next_tokens -1. */
+isd_status_t isd_propose_masked(const isd_shape_t *s,
+                                const void *qnext_logits, const float *u_propose,
+                                const int32_t *mask,
+                                int32_t *next_tokens, float *qnext_x,
+                                void *workspace, size_t ws_bytes, void *stream);
+
+/* Draw masks of one loop step from the state before it and the step's
+ * accept_len (all int32 [C]). */
+isd_status_t isd_decode_masks(int32_t C, int32_t L, const int32_t *state,
+                              const int32_t *accept_len, int32_t *bonus_mask,
+                              int32_t *anchor_mask, void *stream);
+
+/* Closes one loop step.  A verifying sequence emits out_tokens[c, 0..j]
+ * (j + 1 tokens) when it rejected at j < L and moves to recovery, or
+ * out_tokens[c, 0..L-1] and bonus[c] (L + 1 tokens) and stays verifying; a
+ * recovering sequence emits anchor[c] and moves to verify.  The tokens are
+ * appended to history [C, hist_cap] (int32; those past hist_cap are dropped;
+ * history may be NULL when hist_cap is 0), tokens [C] (int64) counts every
+ * emitted token, forwards [C] (int64) the steps; state [C] is updated in
+ * place. */
+isd_status_t isd_decode_commit(int32_t C, int32_t L, int32_t *state, const int32_t *accept_len,
+                               const int32_t *out_tokens, const int32_t *bonus,
+                               const int32_t *anchor, int32_t *history, int64_t hist_cap,
+                               int64_t *tokens, int64_t *forwards, void *stream);
+
 /* Logits projection ahead of the step (the LM head that produces every p and
  * mask row of the extend forward, section 3.3): logits[M, N] = h[M, K] @
  * w[K, N], bf16 inputs, fp32 accumulation on the matrix cores, rounded to

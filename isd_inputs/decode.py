@@ -30,7 +30,7 @@ DECODE_CONFIGS = {
     # GPU parity of the chained loop
     "gpu_chain": dict(C=16, L=4, V=5000, a=0.75, sigma=2.0, T=1.0, steps=24),
     # GPU Monte Carlo of tokens per forward, stride N = L + 1 = 8
-    "gpu_tpf": dict(C=64, L=7, V=4096, a=0.8, sigma=2.0, T=1.0, steps=120),
+    "gpu_tpf": dict(C=64, L=7, V=4096, a=0.8, sigma=2.0, T=1.0, steps=100),
 }
 
 
@@ -48,8 +48,23 @@ def _log_normalised(logits64: np.ndarray, support: np.ndarray) -> np.ndarray:
     return out
 
 
+_pair_cache: dict = {}
+
+
 def pair(step: int, cfg: dict):
-    """(P logits, Q logits) of the verify positions of `step`: float32 [C, L, V]."""
+    """(P logits, Q logits) of the verify positions of `step`: float32 [C, L, V].
+    The last few pairs are kept, since consecutive steps share one."""
+    key = (int(step),) + tuple(sorted((k, cfg[k]) for k in ("C", "L", "V", "a", "sigma")))
+    hit = _pair_cache.get(key)
+    if hit is None:
+        hit = _make_pair(step, cfg)
+        if len(_pair_cache) >= 4:
+            _pair_cache.pop(next(iter(_pair_cache)))
+        _pair_cache[key] = hit
+    return hit[0].copy(), hit[1].copy()
+
+
+def _make_pair(step: int, cfg: dict):
     C, L, V, a, s = cfg["C"], cfg["L"], cfg["V"], cfg["a"], cfg["sigma"]
     P = np.empty((C, L, V), dtype=np.float32)
     Q = np.empty((C, L, V), dtype=np.float32)

@@ -11,15 +11,20 @@ from .isd import (  # noqa: F401
     MODE_SAMPLE,
     IsdError,
     Shape,
+    Decoder,
     StepCall,
     alpha,
     check_device_error,
+    decode_commit,
+    decode_masks,
     lib,
     lm_head,
     make_shape,
     propose,
+    propose_masked,
     set_tuning,
     step,
+    step_masked,
     verify_step,
     workspace,
     workspace_bytes,

@@ -262,7 +262,16 @@ isd_status_t isd_verify_step(const isd_shape_t *s, const void *p_logits, const v
 isd_status_t isd_propose(const isd_shape_t *s, const void *qnext_logits, const float *u_propose,
                          int32_t *next_tokens, float *qnext_x, void *workspace, size_t ws_bytes,
                          void *stream) {
+    return isd_propose_masked(s, qnext_logits, u_propose, nullptr, next_tokens, qnext_x, workspace,
+                              ws_bytes, stream);
+}
+
+isd_status_t isd_propose_masked(const isd_shape_t *s, const void *qnext_logits,
+                                const float *u_propose, const int32_t *mask,
+                                int32_t *next_tokens, float *qnext_x, void *workspace,
+                                size_t ws_bytes, void *stream) {
     ISD_TRY(check_shape(s, true));
+    if (mask) ISD_TRY(check_ptr(mask, "mask", 4));
     const bool sample = s->mode == ISD_MODE_SAMPLE;
     ISD_TRY(check_ptr(qnext_logits, "qnext_logits", elem_size(s)));
     if (sample) ISD_TRY(check_ptr(u_propose, "u_propose", 4));
@@ -272,6 +281,7 @@ isd_status_t isd_propose(const isd_shape_t *s, const void *qnext_logits, const f
     a.up = sample ? u_propose : nullptr;
     a.next_tokens = next_tokens;
     a.qnext_x = qnext_x;
+    a.pmask = mask;
     Plan plan;
     plan.propose = true;
     return run(s, plan, a, workspace, ws_bytes, stream);
@@ -303,7 +313,22 @@ isd_status_t isd_step(const isd_shape_t *s, const void *p_logits, const void *q_
                       int32_t *out_tokens, int32_t *n_emitted, float *p_x, float *q_x,
                       float *alpha, int32_t *next_tokens, float *qnext_x, void *workspace,
                       size_t ws_bytes, void *stream) {
+    return isd_step_masked(s, p_logits, q_logits, proposals, u_accept, u_resid, qnext_logits,
+                           u_propose, nullptr, nullptr, accept_len, out_tokens, n_emitted, p_x,
+                           q_x, alpha, next_tokens, qnext_x, workspace, ws_bytes, stream);
+}
+
+isd_status_t isd_step_masked(const isd_shape_t *s, const void *p_logits, const void *q_logits,
+                             const int32_t *proposals, const float *u_accept,
+                             const float *u_resid, const void *qnext_logits,
+                             const float *u_propose, const int32_t *verify_mask,
+                             const int32_t *propose_mask, int32_t *accept_len,
+                             int32_t *out_tokens, int32_t *n_emitted, float *p_x, float *q_x,
+                             float *alpha, int32_t *next_tokens, float *qnext_x, void *workspace,
+                             size_t ws_bytes, void *stream) {
     ISD_TRY(check_shape(s, true));
+    if (verify_mask) ISD_TRY(check_ptr(verify_mask, "verify_mask", 4));
+    if (propose_mask) ISD_TRY(check_ptr(propose_mask, "propose_mask", 4));
     const size_t es = elem_size(s);
     const bool sample = s->mode == ISD_MODE_SAMPLE;
     ISD_TRY(check_ptr(p_logits, "p_logits", es));
@@ -335,6 +360,8 @@ isd_status_t isd_step(const isd_shape_t *s, const void *p_logits, const void *q_
     a.alpha = alpha;
     a.next_tokens = next_tokens;
     a.qnext_x = qnext_x;
+    a.vmask = verify_mask;
+    a.pmask = propose_mask;
     Plan plan;
     plan.verify = plan.propose = plan.residual = plan.verify_outputs = true;
     return run(s, plan, a, workspace, ws_bytes, stream);
@@ -354,6 +381,43 @@ isd_status_t isd_lm_head(const void *h, const void *w, int32_t M, int32_t K, int
                                         static_cast<const uint16_t *>(w), M, K, N,
                                         static_cast<uint16_t *>(logits), (hipStream_t)stream);
     if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "lm_head launch failed: %s", hipGetErrorString(e));
+    return ISD_OK;
+}
+
+isd_status_t isd_decode_masks(int32_t C, int32_t L, const int32_t *state,
+                              const int32_t *accept_len, int32_t *bonus_mask,
+                              int32_t *anchor_mask, void *stream) {
+    if (C < 1) return fail(ISD_ERR_ARG, "C must be >= 1 (got %d)", (int)C);
+    if (L < 1 || L > kMaxL) return fail(ISD_ERR_ARG, "L must be in [1, 64] (got %d)", (int)L);
+    ISD_TRY(check_ptr(state, "state", 4));
+    ISD_TRY(check_ptr(accept_len, "accept_len", 4));
+    ISD_TRY(check_ptr(bonus_mask, "bonus_mask", 4));
+    ISD_TRY(check_ptr(anchor_mask, "anchor_mask", 4));
+    const hipError_t e = launch_decode_masks(C, L, state, accept_len, bonus_mask, anchor_mask,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return ISD_OK;
+}
+
+isd_status_t isd_decode_commit(int32_t C, int32_t L, int32_t *state, const int32_t *accept_len,
+                               const int32_t *out_tokens, const int32_t *bonus,
+                               const int32_t *anchor, int32_t *history, int64_t hist_cap,
+                               int64_t *tokens, int64_t *forwards, void *stream) {
+    if (C < 1) return fail(ISD_ERR_ARG, "C must be >= 1 (got %d)", (int)C);
+    if (L < 1 || L > kMaxL) return fail(ISD_ERR_ARG, "L must be in [1, 64] (got %d)", (int)L);
+    ISD_TRY(check_ptr(state, "state", 4));
+    ISD_TRY(check_ptr(accept_len, "accept_len", 4));
+    ISD_TRY(check_ptr(out_tokens, "out_tokens", 4));
+    ISD_TRY(check_ptr(bonus, "bonus", 4));
+    ISD_TRY(check_ptr(anchor, "anchor", 4));
+    ISD_TRY(check_ptr(tokens, "tokens", 8));
+    ISD_TRY(check_ptr(forwards, "forwards", 8));
+    if (hist_cap < 0) return fail(ISD_ERR_ARG, "hist_cap must be >= 0");
+    if (hist_cap > 0) ISD_TRY(check_ptr(history, "history", 4));
+    const hipError_t e = launch_decode_commit(C, L, state, accept_len, out_tokens, bonus, anchor,
+                                              hist_cap > 0 ? history : nullptr, hist_cap, tokens,
+                                              forwards, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ISD_OK;
 }
 

@@ -102,6 +102,7 @@ struct StepArgs {
     const void *p, *q, *qn;
     const int32_t *x;
     const float *ua, *ur, *up;
+    const int32_t *vmask, *pmask;   // per-sequence verify / propose masks (NULL: all)
     // outputs (NULL when not requested)
     int32_t *accept_len, *out_tokens, *n_emitted;
     float *p_x, *q_x, *alpha, *alpha_mean;
@@ -129,6 +130,14 @@ enum Mode { kSample = 0, kGreedy = 1 };
 
 // Launches the step kernel for `a` (dtype/mode select the instantiation).
 hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStream_t stream);
+
+// Bookkeeping kernels of the multi-step decoding loop.
+hipError_t launch_decode_masks(int C, int L, const int32_t *state, const int32_t *accept_len,
+                               int32_t *bonus_mask, int32_t *anchor_mask, hipStream_t stream);
+hipError_t launch_decode_commit(int C, int L, int32_t *state, const int32_t *accept_len,
+                                const int32_t *out_tokens, const int32_t *bonus,
+                                const int32_t *anchor, int32_t *history, int64_t hist_cap,
+                                int64_t *tokens, int64_t *forwards, hipStream_t stream);
 
 // LM-head GEMM (bf16 in, fp32 accumulate, bf16 out).
 hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, int N,

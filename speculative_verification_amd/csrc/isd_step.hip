@@ -231,7 +231,8 @@ __device__ __forceinline__ float tree_sum(float (&e)[N]) {
 }
 
 // Streams tiles tile_begin + wave, + kWavesPerGroup, ... < tile_end of `row`,
-// keeping the next tile's loads in flight while `f` consumes the current one.
+// keeping the loads of the next AHEAD tiles in flight while `f` consumes the
+// current one.
 template <typename T, bool VEC, typename F>
 __device__ __forceinline__ void stream_row(const T *__restrict__ row, int tile_begin, int tile_end,
                                            int V, int wave, int lane, F &&f) {
@@ -248,6 +249,30 @@ __device__ __forceinline__ void stream_row(const T *__restrict__ row, int tile_b
         if (!more) break;
         cur = nxt;
         t = tn;
+    }
+}
+
+// stream_row with the next two tiles of each wavefront in flight.
+template <typename T, bool VEC, typename F>
+__device__ __forceinline__ void stream_row_deep(const T *__restrict__ row, int tile_begin,
+                                                int tile_end, int V, int wave, int lane, F &&f) {
+    int t = tile_begin + wave;
+    if (t >= tile_end) return;
+    TileRaw<T> cur, nx1;
+    load_tile<T, VEC>(row, t, V, lane, cur);
+    bool has1 = t + kWavesPerGroup < tile_end;
+    if (has1) load_tile<T, VEC>(row, t + kWavesPerGroup, V, lane, nx1);
+    for (;;) {
+        const int t2 = t + 2 * kWavesPerGroup;
+        const bool has2 = t2 < tile_end;
+        TileRaw<T> nx2;
+        if (has2) load_tile<T, VEC>(row, t2, V, lane, nx2);
+        f(cur, t);
+        if (!has1) break;
+        cur = nx1;
+        nx1 = nx2;
+        has1 = has2;
+        t += kWavesPerGroup;
     }
 }
 
@@ -744,6 +769,23 @@ __device__ __forceinline__ void decide(const StepArgs &a, int c, int lane) {
     }
 }
 
+// Outputs of a sequence that verifies nothing in a masked step.
+__device__ __forceinline__ void write_idle_verify(const StepArgs &a, int c) {
+    const int L = a.L;
+    for (int k = threadIdx.x; k < L; k += kThreads) {
+        if (a.verify_outputs) a.out_tokens[c * L + k] = -1;
+        if (a.p_x) a.p_x[c * L + k] = 0.0f;
+        if (a.q_x) a.q_x[c * L + k] = 0.0f;
+    }
+    if (threadIdx.x == 0) {
+        if (a.verify_outputs) {
+            a.accept_len[c] = -1;
+            a.n_emitted[c] = 0;
+        }
+        if (a.alpha) a.alpha[c] = 0.0f;
+    }
+}
+
 template <typename T, bool VEC, int MODE>
 __device__ __forceinline__ void pq_item(const StepArgs &a, int t, Shared &sh, int wave, int lane) {
     const int per_seq = a.rows_pq * a.S;
@@ -758,6 +800,13 @@ __device__ __forceinline__ void pq_item(const StepArgs &a, int t, Shared &sh, in
     const int tb = seg * a.tps;
     const int te = min(a.tiles_row, tb + a.tps);
     const size_t rec = ((size_t)which * CL + (size_t)c * a.L + k) * a.S + seg;
+
+    if (a.vmask && a.vmask[c] == 0) {
+        // sequence c verifies nothing this step: its first item writes the
+        // defined outputs of an idle sequence, and no other item of c runs
+        if (slot == 0 && seg == 0) write_idle_verify(a, c);
+        return;
+    }
 
     if (MODE == kSample) {
         LaneSoftmax sm;
@@ -813,6 +862,14 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
     const T *row = static_cast<const T *>(a.qn) + row_offset(a, c, k);
     const int tb = seg * a.tpsq;
     const int te = min(a.tiles_row, tb + a.tpsq);
+    if (a.pmask && a.pmask[c] == 0) {
+        // no proposal for sequence c this step; its row is not read
+        if (seg == 0 && threadIdx.x == 0) {
+            a.next_tokens[rowid] = -1;
+            if (a.qnext_x) a.qnext_x[rowid] = 0.0f;
+        }
+        return;
+    }
 
     if (MODE == kSample) {
         TileRec *tr = a.ws.tiles + (size_t)rowid * a.tiles_row;
@@ -926,6 +983,7 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
 template <typename T, bool VEC>
 __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shared &sh, int wave,
                                          int lane) {
+    if (a.vmask && a.vmask[c] == 0) return;   // no decision is taken for c
     // wait for sequence c's decision
     if (threadIdx.x == 0) {
         uint32_t polls = 0;

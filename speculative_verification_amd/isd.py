@@ -44,6 +44,10 @@ _SIGS = {
     "isd_propose": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 4 + [_vp, _sz, _vp]),
     "isd_alpha": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 5 + [_vp, _sz, _vp]),
     "isd_step": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 15 + [_vp, _sz, _vp]),
+    "isd_step_masked": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 17 + [_vp, _sz, _vp]),
+    "isd_propose_masked": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 5 + [_vp, _sz, _vp]),
+    "isd_decode_masks": (ctypes.c_int, [_i32, _i32] + [_vp] * 4 + [_vp]),
+    "isd_decode_commit": (ctypes.c_int, [_i32, _i32] + [_vp] * 6 + [_i64, _vp, _vp, _vp]),
     "isd_lm_head": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "isd_check_device_error": (ctypes.c_int, [_vp, _sz, _vp]),
     "isd_set_tuning": (ctypes.c_int, [_i32, _i32, _i32, _i64]),
@@ -249,6 +253,101 @@ class StepCall:
 def step(p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, out=None, ws=None):
     """One fused ISD step (verify + propose in one launch)."""
     return StepCall(p, q, x, ua, ur, qn, up, mode=mode, temperature=temperature, out=out, ws=ws)()
+
+
+def step_masked(p, q, x, ua, ur, qn, up, verify_mask=None, propose_mask=None, *, mode="sample",
+                temperature=1.0, out=None, ws=None):
+    """isd_step with per-sequence verify / propose masks (int32 [C]; None = all)."""
+    m = _mode_code(mode)
+    shape = make_shape(p, m, temperature)
+    _same_layout(shape, qn, "qn", m, temperature)
+    if m == MODE_SAMPLE:
+        _same_layout(shape, q, "q", m, temperature)
+    C, L, dev = shape.C, shape.L, p.device
+    o = dict(accept_len=_out(out, "accept_len", (C,), torch.int32, dev),
+             out_tokens=_out(out, "out_tokens", (C, L), torch.int32, dev),
+             n_emitted=_out(out, "n_emitted", (C,), torch.int32, dev),
+             p_x=_out(out, "p_x", (C, L), torch.float32, dev),
+             q_x=_out(out, "q_x", (C, L), torch.float32, dev),
+             alpha=_out(out, "alpha", (C,), torch.float32, dev),
+             next_tokens=_out(out, "next_tokens", (C, L), torch.int32, dev),
+             qnext_x=_out(out, "qnext_x", (C, L), torch.float32, dev))
+    ws = workspace(shape, dev) if ws is None else ws
+    _check(lib().isd_step_masked(
+        ctypes.byref(shape), _ptr(p), _ptr(q), _ptr(x), _ptr(ua), _ptr(ur), _ptr(qn), _ptr(up),
+        _ptr(verify_mask), _ptr(propose_mask), _ptr(o["accept_len"]), _ptr(o["out_tokens"]),
+        _ptr(o["n_emitted"]), _ptr(o["p_x"]), _ptr(o["q_x"]), _ptr(o["alpha"]),
+        _ptr(o["next_tokens"]), _ptr(o["qnext_x"]), _ptr(ws), ws.numel(), _stream()))
+    return o
+
+
+def propose_masked(rows, u, mask=None, *, mode="sample", temperature=1.0, out=None, ws=None):
+    """isd_propose with a per-sequence mask (int32 [C]; None = all)."""
+    m = _mode_code(mode)
+    shape = make_shape(rows, m, temperature)
+    C, L, dev = shape.C, shape.L, rows.device
+    o = dict(next_tokens=_out(out, "next_tokens", (C, L), torch.int32, dev),
+             qnext_x=_out(out, "qnext_x", (C, L), torch.float32, dev))
+    ws = workspace(shape, dev) if ws is None else ws
+    _check(lib().isd_propose_masked(ctypes.byref(shape), _ptr(rows), _ptr(u), _ptr(mask),
+                                    _ptr(o["next_tokens"]), _ptr(o["qnext_x"]), _ptr(ws),
+                                    ws.numel(), _stream()))
+    return o
+
+
+def decode_masks(L, state, accept_len, bonus_mask, anchor_mask):
+    """Bonus and anchor draw masks of one decoding-loop step."""
+    _check(lib().isd_decode_masks(state.numel(), L, _ptr(state), _ptr(accept_len),
+                                  _ptr(bonus_mask), _ptr(anchor_mask), _stream()))
+
+
+def decode_commit(L, state, accept_len, out_tokens, bonus, anchor, tokens, forwards,
+                  history=None):
+    """Close one decoding-loop step: append tokens, count, advance the state."""
+    cap = 0 if history is None else history.shape[1]
+    _check(lib().isd_decode_commit(state.numel(), L, _ptr(state), _ptr(accept_len),
+                                   _ptr(out_tokens), _ptr(bonus), _ptr(anchor), _ptr(history),
+                                   cap, _ptr(tokens), _ptr(forwards), _stream()))
+
+
+class Decoder:
+    """Device-resident state of the multi-step decoding loop for C sequences
+    with L proposals per step (stride L + 1).
+
+    Every sequence starts in recovery (state 0).  ``step`` takes one
+    forward's rows, all shaped [C, L + 1, V] with one layout: p (rows 0..L-1
+    verify, row L is the bonus anchor, row 0 the anchor of a recovering
+    sequence), q and qn (rows 0..L-1 used); and the uniforms ua, ur, up
+    [C, L], ub, uz [C].  Each step is five library calls on the current
+    stream and never synchronises."""
+
+    def __init__(self, C, L, device, *, history=0, mode="sample", temperature=1.0):
+        self.C, self.L, self.mode, self.temperature = C, L, mode, temperature
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
+        self.state = z((C,), torch.int32)
+        self.x = z((C, L), torch.int32)
+        self.tokens = z((C,), torch.int64)
+        self.forwards = z((C,), torch.int64)
+        self.history = z((C, history), torch.int32) if history else None
+        self.bonus_mask = z((C,), torch.int32)
+        self.anchor_mask = z((C,), torch.int32)
+        self.last = None
+
+    def step(self, p, q, qn, ua, ur, up, ub, uz):
+        L, C = self.L, self.C
+        kw = dict(mode=self.mode, temperature=self.temperature)
+        o = step_masked(p[:, :L], q[:, :L], self.x, ua, ur, qn[:, :L], up,
+                        verify_mask=self.state, **kw)
+        state_before = self.state.clone()
+        decode_masks(L, self.state, o["accept_len"], self.bonus_mask, self.anchor_mask)
+        b = propose_masked(p[:, L:L + 1], ub.view(C, 1), self.bonus_mask, **kw)
+        a = propose_masked(p[:, 0:1], uz.view(C, 1), self.anchor_mask, **kw)
+        decode_commit(L, self.state, o["accept_len"], o["out_tokens"], b["next_tokens"],
+                      a["next_tokens"], self.tokens, self.forwards, self.history)
+        self.x.copy_(o["next_tokens"])
+        self.last = dict(o, state_before=state_before, bonus=b["next_tokens"][:, 0],
+                         anchor=a["next_tokens"][:, 0])
+        return self.last
 
 
 def lm_head(h, w, out=None):

@@ -164,3 +164,26 @@ def test_sequence_stride(isd):
     with pytest.raises(ValueError, match="same shape"):
         isd.isd._same_layout(sp, dense, "q", 0, 1.0)
     isd.isd._same_layout(sp, ext[:, 5:], "q", 0, 1.0)
+
+
+def test_masked_and_loop_validation(isd):
+    lib = isd.lib()
+    shape = _shape(isd)
+    # a misaligned mask is rejected before any launch
+    args = [FAKE] * 15
+    st = lib.isd_step_masked(ctypes.byref(shape), *args[:7], ctypes.c_void_p(0x10002), None,
+                             *args[7:], FAKE, 1 << 30, None)
+    assert st == 1 and "verify_mask" in lib.isd_last_error().decode()
+    st = lib.isd_propose_masked(ctypes.byref(shape), FAKE, FAKE, ctypes.c_void_p(0x10001), FAKE,
+                                None, FAKE, 1 << 30, None)
+    assert st == 1 and "mask" in lib.isd_last_error().decode()
+    assert lib.isd_decode_masks(0, 4, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.isd_decode_masks(4, 65, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.isd_decode_masks(4, 4, None, FAKE, FAKE, FAKE, None) == 1
+    assert lib.isd_decode_commit(4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, 8, FAKE, FAKE,
+                                 None) == 1
+    assert "history" in lib.isd_last_error().decode()
+    assert lib.isd_decode_commit(4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, -1, FAKE, FAKE,
+                                 None) == 1
+    assert lib.isd_decode_commit(4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                 ctypes.c_void_p(0x10004), FAKE, None) == 1
