@@ -137,11 +137,19 @@ def accept_ratio(px: np.ndarray, qx: np.ndarray) -> np.ndarray:
 # Sample mode
 # ---------------------------------------------------------------------------
 
-def verify_sample(p, q, x, ua, ur, temperature=1.0):
+def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False):
     """ISD verification of proposals ``x`` against the anchor, batched.
 
     p, q: [B, L, V] logits (anchor rows, proposal rows that generated x);
     x: [B, L] int proposals; ua, ur: [B, L] uniforms in [0, 1).
+
+    Variants ("Introspective Diffusion Language Models | Summary", section 3.3
+    and the relaxed-acceptance ablation of section 4):
+      relax = tau >= 0 accepts with min(1, (1 + tau) P(x)/Q(x)) (tau = 0 is
+        the exact rule); the correction and alpha are unchanged;
+      q_onehot: the proposals were argmax picks, so their law is one-hot at
+        x (q is not read): the ratio is P(x) and the residual is P with x
+        removed.
     Returns a dict of per-sequence arrays:
       accept_len [B], out_tokens [B, L] (-1 padded), n_emitted [B],
       p_x, q_x, ratio [B, L], alpha [B], decision_margin [B] (smallest
@@ -150,26 +158,32 @@ def verify_sample(p, q, x, ua, ur, temperature=1.0):
       resid_flagged [B].
     """
     p = np.asarray(p, dtype=np.float64)
-    q = np.asarray(q, dtype=np.float64)
     x = np.asarray(x, dtype=np.int64)
     ua = np.asarray(ua, dtype=np.float64)
     ur = np.asarray(ur, dtype=np.float64)
     B, L, V = p.shape
+    if relax < 0:
+        raise ValueError("relax must be >= 0")
 
     P = softmax(p, temperature)
-    Q = softmax(q, temperature)
+    if q_onehot:
+        Q = np.zeros_like(P)
+        np.put_along_axis(Q, x[..., None], 1.0, axis=-1)
+    else:
+        Q = softmax(np.asarray(q, dtype=np.float64), temperature)
     px = np.take_along_axis(P, x[..., None], axis=-1)[..., 0]
     qx = np.take_along_axis(Q, x[..., None], axis=-1)[..., 0]
     r = accept_ratio(px, qx)
     alpha = r.mean(axis=-1)
+    r_acc = accept_ratio((1.0 + relax) * px, qx) if relax else r
 
-    accepted = ua < r
+    accepted = ua < r_acc
     rejected = ~accepted
     j = np.where(rejected.any(axis=-1), np.argmax(rejected, axis=-1), L)
 
     ks = np.arange(L)[None, :]
     considered = ks <= j[:, None]
-    gap = np.where(considered, np.abs(ua - r), np.inf)
+    gap = np.where(considered, np.abs(ua - r_acc), np.inf)
     decision_margin = gap.min(axis=-1)
 
     out = np.where(ks < j[:, None], x, -1)

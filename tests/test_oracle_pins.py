@@ -154,7 +154,7 @@ def _step_measures(f, V):
         u, cur = b, f(b)
 
 
-def _emitted_law(P_rows, Q_rows, xs_weight, pos):
+def _emitted_law(P_rows, Q_rows, xs_weight, pos, **variant):
     """Exact law of the token emitted at position ``pos`` given every earlier
     position accepted, by bisecting the oracle's decisions as a black box.
 
@@ -175,7 +175,7 @@ def _emitted_law(P_rows, Q_rows, xs_weight, pos):
 
         def accepted(u):
             ua[0, pos] = u
-            o = O.verify_sample(p, q, x, ua, ur)
+            o = O.verify_sample(p, q, x, ua, ur, **variant)
             return int(o["accept_len"][0] > pos)
 
         # earlier positions must accept at u = 0, i.e. their ratio must be > 0
@@ -185,7 +185,7 @@ def _emitted_law(P_rows, Q_rows, xs_weight, pos):
 
         def corrected(u):
             ur[0, pos] = u
-            o = O.verify_sample(p, q, x, ua, ur)
+            o = O.verify_sample(p, q, x, ua, ur, **variant)
             return int(o["out_tokens"][0, pos])
 
         if acc_measure < 1.0:
