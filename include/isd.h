@@ -96,6 +96,13 @@ typedef struct {
     int32_t mode;        /* isd_mode_t */
     float temperature;   /* softmax temperature T > 0 (sample mode) */
     int64_t ldc;         /* elements between sequences c and c+1 (0: L*ld) */
+    float relax;         /* tau >= 0 (sample mode): accept with min(1, (1 + tau) P(x)/Q(x)),
+                            the relaxed acceptance of the pages' ablation (section 4); 0 is
+                            the exact rule.  alpha and the correction are unchanged. */
+    int32_t q_onehot;    /* 1 (sample mode): the proposals were argmax picks, so their law
+                            is one-hot at x (section 3.3 with a sampled anchor): q_logits
+                            is not read (may be NULL), the ratio is P(x), and the
+                            correction draws from P with x removed.  0: q_logits as given */
 } isd_shape_t;
 
 /* Workspace bytes needed by any call on shape `s`; 0 if `s` is invalid. */

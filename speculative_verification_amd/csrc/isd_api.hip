@@ -71,6 +71,9 @@ isd_status_t check_shape(const isd_shape_t *s, bool need_temperature) {
     if (need_temperature && s->mode == ISD_MODE_SAMPLE &&
         !(isfinite(s->temperature) && s->temperature > 0.0f))
         return fail(ISD_ERR_ARG, "temperature must be finite and > 0 in sample mode");
+    if (!(isfinite(s->relax) && s->relax >= 0.0f))
+        return fail(ISD_ERR_ARG, "relax must be finite and >= 0");
+    if (s->q_onehot != 0 && s->q_onehot != 1) return fail(ISD_ERR_ARG, "q_onehot must be 0 or 1");
     return ISD_OK;
 }
 
@@ -143,7 +146,9 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
     a.Sr = ceil_div(a.tiles_row, a.tpsr);
     a.order = kItemOrder;
 
-    a.rows_pq = plan.verify ? (greedy ? L : 2 * L) : 0;
+    a.q_onehot = (!greedy && s->q_onehot) ? 1 : 0;
+    a.relax1p = greedy ? 1.0 : 1.0 + (double)s->relax;
+    a.rows_pq = plan.verify ? ((greedy || a.q_onehot) ? L : 2 * L) : 0;
     a.n_pq = C * a.rows_pq * a.S;
     a.q_blk = plan.propose ? L * a.Sq : 0;
     a.r_blk = (plan.residual && !greedy) ? a.Sr : 0;
@@ -234,7 +239,7 @@ isd_status_t isd_verify_step(const isd_shape_t *s, const void *p_logits, const v
     const bool sample = s->mode == ISD_MODE_SAMPLE;
     ISD_TRY(check_ptr(p_logits, "p_logits", es));
     if (sample) {
-        ISD_TRY(check_ptr(q_logits, "q_logits", es));
+        if (!s->q_onehot) ISD_TRY(check_ptr(q_logits, "q_logits", es));
         ISD_TRY(check_ptr(u_accept, "u_accept", 4));
         ISD_TRY(check_ptr(u_resid, "u_resid", 4));
     }
@@ -244,7 +249,7 @@ isd_status_t isd_verify_step(const isd_shape_t *s, const void *p_logits, const v
     ISD_TRY(check_ptr(n_emitted, "n_emitted", 4));
     StepArgs a = blank_args();
     a.p = p_logits;
-    a.q = sample ? q_logits : nullptr;
+    a.q = (sample && !s->q_onehot) ? q_logits : nullptr;
     a.x = proposals;
     a.ua = sample ? u_accept : nullptr;
     a.ur = sample ? u_resid : nullptr;
@@ -293,12 +298,12 @@ isd_status_t isd_alpha(const isd_shape_t *s, const void *p_logits, const void *q
     ISD_TRY(check_shape(s, true));
     const bool sample = s->mode == ISD_MODE_SAMPLE;
     ISD_TRY(check_ptr(p_logits, "p_logits", elem_size(s)));
-    if (sample) ISD_TRY(check_ptr(q_logits, "q_logits", elem_size(s)));
+    if (sample && !s->q_onehot) ISD_TRY(check_ptr(q_logits, "q_logits", elem_size(s)));
     ISD_TRY(check_ptr(proposals, "proposals", 4));
     ISD_TRY(check_ptr(alpha, "alpha", 4));
     StepArgs a = blank_args();
     a.p = p_logits;
-    a.q = sample ? q_logits : nullptr;
+    a.q = (sample && !s->q_onehot) ? q_logits : nullptr;
     a.x = proposals;
     a.alpha = alpha;
     a.alpha_mean = alpha_mean;
@@ -334,7 +339,7 @@ isd_status_t isd_step_masked(const isd_shape_t *s, const void *p_logits, const v
     ISD_TRY(check_ptr(p_logits, "p_logits", es));
     ISD_TRY(check_ptr(qnext_logits, "qnext_logits", es));
     if (sample) {
-        ISD_TRY(check_ptr(q_logits, "q_logits", es));
+        if (!s->q_onehot) ISD_TRY(check_ptr(q_logits, "q_logits", es));
         ISD_TRY(check_ptr(u_accept, "u_accept", 4));
         ISD_TRY(check_ptr(u_resid, "u_resid", 4));
         ISD_TRY(check_ptr(u_propose, "u_propose", 4));
@@ -346,7 +351,7 @@ isd_status_t isd_step_masked(const isd_shape_t *s, const void *p_logits, const v
     ISD_TRY(check_ptr(next_tokens, "next_tokens", 4));
     StepArgs a = blank_args();
     a.p = p_logits;
-    a.q = sample ? q_logits : nullptr;
+    a.q = (sample && !s->q_onehot) ? q_logits : nullptr;
     a.qn = qnext_logits;
     a.x = proposals;
     a.ua = sample ? u_accept : nullptr;

@@ -67,7 +67,7 @@ struct SeqInfo {               // per-sequence decision, read by residual items
     float cp, cq;              // references of rows p[c, j], q[c, j]
     float inv_sp, inv_sq;      // 1 / softmax denominators of those rows
     float alpha;
-    float pad;
+    int32_t xj;                // x[c, j] (the argmax pick removed from the residual)
 };
 
 struct Workspace {
@@ -103,6 +103,8 @@ struct StepArgs {
     const int32_t *x;
     const float *ua, *ur, *up;
     const int32_t *vmask, *pmask;   // per-sequence verify / propose masks (NULL: all)
+    double relax1p;            // 1 + tau: the accept test uses min(1, (1 + tau) P/Q)
+    int q_onehot;              // proposals are argmax picks: Q = onehot(x), q not read
     // outputs (NULL when not requested)
     int32_t *accept_len, *out_tokens, *n_emitted;
     float *p_x, *q_x, *alpha, *alpha_mean;

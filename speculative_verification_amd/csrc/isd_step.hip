@@ -672,20 +672,29 @@ __device__ __forceinline__ void decide(const StepArgs &a, int c, int lane) {
         double px = 0.0, qx = 0.0;
         if (valid) {
             take_segrecs(&a.ws.seg[((size_t)c * L + kk) * a.S], a.S, cp, sp);
-            take_segrecs(&a.ws.seg[((size_t)CL + (size_t)c * L + kk) * a.S], a.S, cq, sq);
-            if (sp <= 0.0 || sq <= 0.0) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
+            if (!a.q_onehot) take_segrecs(&a.ws.seg[((size_t)CL + (size_t)c * L + kk) * a.S], a.S, cq, sq);
+            if (sp <= 0.0 || (!a.q_onehot && sq <= 0.0)) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
             if (!bad) {
                 const long long off = row_offset(a, c, kk) + xk;
                 const float lp = load_value<T>(static_cast<const T *>(a.p), off);
-                const float lq = load_value<T>(static_cast<const T *>(a.q), off);
                 const double k2 = (double)a.k2;
                 if (sp > 0.0) px = exp2((double)lp * k2 - (double)cp) / sp;
-                if (sq > 0.0) qx = exp2((double)lq * k2 - (double)cq) / sq;
+                if (a.q_onehot) {
+                    qx = 1.0;   // the argmax pick's own law
+                } else {
+                    const float lq = load_value<T>(static_cast<const T *>(a.q), off);
+                    if (sq > 0.0) qx = exp2((double)lq * k2 - (double)cq) / sq;
+                }
             }
         }
-        // min(1, P(x)/Q(x)); Q(x) = 0 gives 1 if P(x) > 0, else 0
+        // min(1, P(x)/Q(x)); Q(x) = 0 gives 1 if P(x) > 0, else 0.  The accept
+        // test may use the relaxed ratio min(1, (1 + tau) P(x)/Q(x)); alpha
+        // stays the plain rate.
         const double r = qx > 0.0 ? fmin(1.0, px / qx) : (px > 0.0 ? 1.0 : 0.0);
-        const bool accepted = !valid || (a.ua == nullptr || (double)a.ua[c * L + kk] < r);
+        const double ra = a.relax1p == 1.0
+                              ? r
+                              : (qx > 0.0 ? fmin(1.0, (a.relax1p * px) / qx) : (px > 0.0 ? 1.0 : 0.0));
+        const bool accepted = !valid || (a.ua == nullptr || (double)a.ua[c * L + kk] < ra);
         const unsigned long long rej = __ballot(!accepted);
         const int j = rej ? wave_first(rej) : L;
         alpha = (float)(wave_sum_d(valid ? r : 0.0) / (double)L);
@@ -700,6 +709,7 @@ __device__ __forceinline__ void decide(const StepArgs &a, int c, int lane) {
             const int src = j < L ? j : 0;
             const float jcp = __shfl(cp, src), jcq = __shfl(cq, src);
             const double jsp = __shfl(sp, src), jsq = __shfl(sq, src);
+            const int jx = __shfl(xk, src);
             if (lane == 0) {
                 SeqInfo *si = &a.ws.info[c];
                 st32(reinterpret_cast<uint32_t *>(&si->j), (uint32_t)j);
@@ -711,6 +721,7 @@ __device__ __forceinline__ void decide(const StepArgs &a, int c, int lane) {
                      __float_as_uint(jsp > 0.0 ? (float)(1.0 / jsp) : 0.0f));
                 st32(reinterpret_cast<uint32_t *>(&si->inv_sq),
                      __float_as_uint(jsq > 0.0 ? (float)(1.0 / jsq) : 0.0f));
+                st32(reinterpret_cast<uint32_t *>(&si->xj), (uint32_t)jx);
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 __builtin_amdgcn_s_waitcnt(0);
                 st32(counter(a.ws.flag, c), 1u);
@@ -794,8 +805,11 @@ __device__ __forceinline__ void pq_item(const StepArgs &a, int t, Shared &sh, in
     const int slot = rem / a.S;
     const int seg = rem - slot * a.S;
     const int CL = a.C * a.L;
-    const int k = MODE == kSample ? slot >> 1 : slot;
-    const int which = MODE == kSample ? (slot & 1) : 0;
+    // sample mode verifies (p, q) row pairs, unless the proposals were argmax
+    // picks whose law is one-hot at x (no q row to read)
+    const bool pairs = MODE == kSample && !a.q_onehot;
+    const int k = pairs ? slot >> 1 : slot;
+    const int which = pairs ? (slot & 1) : 0;
     const T *row = static_cast<const T *>(which ? a.q : a.p) + row_offset(a, c, k);
     const int tb = seg * a.tps;
     const int te = min(a.tiles_row, tb + a.tps);
@@ -1005,6 +1019,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         sh.info.cq = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->cq)));
         sh.info.inv_sp = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->inv_sp)));
         sh.info.inv_sq = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->inv_sq)));
+        sh.info.xj = (int)ld32(reinterpret_cast<uint32_t *>(&si->xj));
     }
     __syncthreads();
     const SeqInfo inf = sh.info;
@@ -1014,7 +1029,30 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
     const T *prow = static_cast<const T *>(a.p) + row_offset(a, c, j < L ? j : 0);
     const T *qrow = static_cast<const T *>(a.q) + row_offset(a, c, j < L ? j : 0);
 
-    if (j < L) {
+    if (j < L && a.q_onehot) {
+        // Q is one-hot at x_j: the residual is P with x_j removed
+        const int tb = seg * a.tpsr;
+        const int te = min(a.tiles_row, tb + a.tpsr);
+        stream_row<T, VEC>(prow, tb, te, a.V, wave, lane, [&](const TileRaw<T> &rp, int tile) {
+            float lr = 0.0f, lp = 0.0f;
+#pragma unroll
+            for (int g = 0; g < kGroupsPerTile; ++g) {
+                float er[kGroupElems], ep[kGroupElems];
+#pragma unroll
+                for (int e = 0; e < kGroupElems; ++e) {
+                    const int i = g * kGroupElems + e;
+                    const float P = fast_exp2(fmaf(elem<T>(rp, i), a.k2, -inf.cp)) * inf.inv_sp;
+                    er[e] = elem_index(tile, lane, i) == (long long)inf.xj ? 0.0f : P;
+                    ep[e] = P;
+                }
+                lr += tree_sum(er);
+                lp += tree_sum(ep);
+            }
+            const float sr = wave_sum(lr);
+            const float spp = wave_sum(lp);
+            if (lane == 0) st_pair(&rt[tile], pack2(sr, spp));
+        });
+    } else if (j < L) {
         const int tb = seg * a.tpsr;
         const int te = min(a.tiles_row, tb + a.tpsr);
         stream_rows2<T, VEC>(prow, qrow, tb, te, a.V, wave, lane,
@@ -1071,12 +1109,15 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         if (tile >= 0) {
             TileRaw<T> rp, rq;
             load_tile<T, VEC>(prow, tile, a.V, lane, rp);
-            load_tile<T, VEC>(qrow, tile, a.V, lane, rq);
+            if (!a.q_onehot) load_tile<T, VEC>(qrow, tile, a.V, lane, rq);
             const float k2 = a.k2;
+            const bool onehot = a.q_onehot != 0;
             auto weight = [&](int i) -> double {
                 const float P = fast_exp2(fmaf(elem<T>(rp, i), k2, -inf.cp)) * inf.inv_sp;
+                if (use_p) return (double)P;
+                if (onehot) return elem_index(tile, lane, i) == (long long)inf.xj ? 0.0 : (double)P;
                 const float Q = fast_exp2(fmaf(elem<T>(rq, i), k2, -inf.cq)) * inf.inv_sq;
-                return use_p ? (double)P : (double)fmaxf(P - Q, 0.0f);
+                return (double)fmaxf(P - Q, 0.0f);
             };
             tok = search_tile(weight, tile, lane, before, tile_target);
             if (tok < 0) tok = 0;
@@ -1093,6 +1134,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         st32(reinterpret_cast<uint32_t *>(&si->cq), 0u);
         st32(reinterpret_cast<uint32_t *>(&si->inv_sp), 0u);
         st32(reinterpret_cast<uint32_t *>(&si->inv_sq), 0u);
+        st32(reinterpret_cast<uint32_t *>(&si->xj), 0u);
         st32(counter(a.ws.flag, c), 0u);
     }
 }

@@ -34,7 +34,8 @@ class IsdError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("C", ctypes.c_int32), ("L", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("ld", ctypes.c_int64), ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
-                ("temperature", ctypes.c_float), ("ldc", ctypes.c_int64)]
+                ("temperature", ctypes.c_float), ("ldc", ctypes.c_int64),
+                ("relax", ctypes.c_float), ("q_onehot", ctypes.c_int32)]
 
 
 _vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
@@ -111,9 +112,10 @@ def _logits_layout(t: torch.Tensor):
     return C, L, V, ld, ldc, code
 
 
-def make_shape(logits: torch.Tensor, mode: int = MODE_SAMPLE, temperature: float = 1.0) -> Shape:
+def make_shape(logits: torch.Tensor, mode: int = MODE_SAMPLE, temperature: float = 1.0,
+               relax: float = 0.0, q_onehot: bool = False) -> Shape:
     C, L, V, ld, ldc, code = _logits_layout(logits)
-    return Shape(C, L, V, ld, code, mode, float(temperature), ldc)
+    return Shape(C, L, V, ld, code, mode, float(temperature), ldc, float(relax), int(bool(q_onehot)))
 
 
 def _same_layout(ref: Shape, t, name: str, mode: int, temperature: float):
@@ -162,10 +164,12 @@ def _out(out, key, shape, dtype, device):
     return t
 
 
-def verify_step(p, q, x, ua, ur, *, mode="sample", temperature=1.0, out=None, ws=None):
-    """Verify proposals x [C, L] against anchor rows p (and proposal rows q)."""
+def verify_step(p, q, x, ua, ur, *, mode="sample", temperature=1.0, relax=0.0, q_onehot=False,
+                out=None, ws=None):
+    """Verify proposals x [C, L] against anchor rows p (and proposal rows q;
+    None with q_onehot)."""
     m = _mode_code(mode)
-    shape = make_shape(p, m, temperature)
+    shape = make_shape(p, m, temperature, relax, q_onehot)
     if m == MODE_SAMPLE:
         _same_layout(shape, q, "q", m, temperature)
     C, L, dev = shape.C, shape.L, p.device
@@ -196,10 +200,10 @@ def propose(qn, up, *, mode="sample", temperature=1.0, out=None, ws=None):
     return o
 
 
-def alpha(p, q, x, *, mode="sample", temperature=1.0, out=None, ws=None):
+def alpha(p, q, x, *, mode="sample", temperature=1.0, q_onehot=False, out=None, ws=None):
     """Introspective acceptance rate per sequence and its batch mean."""
     m = _mode_code(mode)
-    shape = make_shape(p, m, temperature)
+    shape = make_shape(p, m, temperature, 0.0, q_onehot)
     if m == MODE_SAMPLE:
         _same_layout(shape, q, "q", m, temperature)
     dev = p.device
@@ -215,10 +219,10 @@ class StepCall:
     """Pre-marshalled isd_step call: fixed shapes and output buffers, so that a
     timing loop pays one ctypes call per step."""
 
-    def __init__(self, p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, out=None,
-                 ws=None):
+    def __init__(self, p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, relax=0.0,
+                 q_onehot=False, out=None, ws=None):
         m = _mode_code(mode)
-        self.shape = make_shape(p, m, temperature)
+        self.shape = make_shape(p, m, temperature, relax, q_onehot)
         _same_layout(self.shape, qn, "qn", m, temperature)
         if m == MODE_SAMPLE:
             _same_layout(self.shape, q, "q", m, temperature)
@@ -250,16 +254,18 @@ class StepCall:
         return self.out
 
 
-def step(p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, out=None, ws=None):
+def step(p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, relax=0.0, q_onehot=False,
+         out=None, ws=None):
     """One fused ISD step (verify + propose in one launch)."""
-    return StepCall(p, q, x, ua, ur, qn, up, mode=mode, temperature=temperature, out=out, ws=ws)()
+    return StepCall(p, q, x, ua, ur, qn, up, mode=mode, temperature=temperature, relax=relax,
+                    q_onehot=q_onehot, out=out, ws=ws)()
 
 
 def step_masked(p, q, x, ua, ur, qn, up, verify_mask=None, propose_mask=None, *, mode="sample",
-                temperature=1.0, out=None, ws=None):
+                temperature=1.0, relax=0.0, q_onehot=False, out=None, ws=None):
     """isd_step with per-sequence verify / propose masks (int32 [C]; None = all)."""
     m = _mode_code(mode)
-    shape = make_shape(p, m, temperature)
+    shape = make_shape(p, m, temperature, relax, q_onehot)
     _same_layout(shape, qn, "qn", m, temperature)
     if m == MODE_SAMPLE:
         _same_layout(shape, q, "q", m, temperature)

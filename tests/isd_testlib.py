@@ -51,8 +51,10 @@ def to_host(o: dict) -> dict:
     return {k: v.detach().cpu().numpy() for k, v in o.items()}
 
 
-def oracle_step(d: dict, dtype: str, mode: str, T: float, chunk: int = 8) -> dict:
-    """Oracle outputs for every sequence in d (chunked to bound memory)."""
+def oracle_step(d: dict, dtype: str, mode: str, T: float, chunk: int = 8, relax: float = 0.0,
+                q_onehot: bool = False) -> dict:
+    """Oracle outputs for every sequence in d (chunked to bound memory);
+    relax and q_onehot select the verification variants (sample mode)."""
     n = d["x"].shape[0]
     parts = []
     for s0 in range(0, n, chunk):
@@ -71,8 +73,9 @@ def oracle_step(d: dict, dtype: str, mode: str, T: float, chunk: int = 8) -> dic
             prob = np.ones(tok.shape)
             pflag = np.zeros(tok.shape, bool)
         else:
-            q = O.decode_logits(d["q"][sl], dtype)
-            v = O.verify_sample(p, q, d["x"][sl], d["ua"][sl], d["ur"][sl], T)
+            q = None if q_onehot else O.decode_logits(d["q"][sl], dtype)
+            v = O.verify_sample(p, q, d["x"][sl], d["ua"][sl], d["ur"][sl], T, relax=relax,
+                                q_onehot=q_onehot)
             tok, prob, _, pflag = O.propose_sample(qn, d["up"][sl], T)
         parts.append(dict(accept_len=v["accept_len"], out_tokens=v["out_tokens"],
                           n_emitted=v["n_emitted"], p_x=v["p_x"], q_x=v["q_x"],

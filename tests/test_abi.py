@@ -187,3 +187,20 @@ def test_masked_and_loop_validation(isd):
                                  None) == 1
     assert lib.isd_decode_commit(4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
                                  ctypes.c_void_p(0x10004), FAKE, None) == 1
+
+
+def test_variant_shape_validation(isd):
+    lib = isd.lib()
+    bad = _shape(isd)
+    bad.relax = -0.5
+    assert _verify(isd, bad) == 1 and "relax" in lib.isd_last_error().decode()
+    bad = _shape(isd)
+    bad.relax = float("inf")
+    assert _verify(isd, bad) == 1
+    bad = _shape(isd)
+    bad.q_onehot = 2
+    assert _verify(isd, bad) == 1 and "q_onehot" in lib.isd_last_error().decode()
+    # with one-hot proposals q may be NULL: the only remaining error is the workspace size
+    ok = _shape(isd)
+    ok.q_onehot = 1
+    assert _verify(isd, ok, ws_bytes=16, q=None) == 3
