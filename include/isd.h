@@ -232,6 +232,17 @@ isd_status_t isd_decode_commit(int32_t C, int32_t L, int32_t *state, const int32
 isd_status_t isd_lm_head(const void *h, const void *w, int32_t M, int32_t K, int32_t N,
                          void *logits, void *workspace, size_t ws_bytes, void *stream);
 
+/* The LM head on a pre-packed head: logits[M, N] = h[M, K] @ wt[N, K]^T,
+ * where wt = w^T is k-contiguous per vocabulary row (isd_lm_head_pack).  Same
+ * arithmetic and rounding as isd_lm_head; K % 64 == 0; h and wt 16-byte
+ * aligned.  No workspace is used (pass NULL, 0). */
+isd_status_t isd_lm_head_packed(const void *h, const void *wt, int32_t M, int32_t K, int32_t N,
+                                void *logits, void *workspace, size_t ws_bytes, void *stream);
+
+/* One-time packing of a head w[K, N] (bf16, row-major) into wt[N, K]
+ * (caller-allocated, 16-byte aligned): a bit-exact transpose. */
+isd_status_t isd_lm_head_pack(const void *w, int32_t K, int32_t N, void *wt, void *stream);
+
 /* Waits for `stream`, then reads and clears the device error word of
  * `workspace`.  Returns ISD_OK if no kernel flagged undefined input or an
  * expired internal wait since the last check, else ISD_ERR_DEVICE with the

@@ -19,6 +19,8 @@ from .isd import (  # noqa: F401
     decode_masks,
     lib,
     lm_head,
+    lm_head_pack,
+    lm_head_packed,
     make_shape,
     propose,
     propose_masked,

@@ -389,6 +389,32 @@ isd_status_t isd_lm_head(const void *h, const void *w, int32_t M, int32_t K, int
     return ISD_OK;
 }
 
+isd_status_t isd_lm_head_pack(const void *w, int32_t K, int32_t N, void *wt, void *stream) {
+    ISD_TRY(check_ptr(w, "w", 2));
+    ISD_TRY(check_ptr(wt, "wt", 16));
+    if (K < 1 || N < 1) return fail(ISD_ERR_ARG, "K, N must be >= 1");
+    const hipError_t e = launch_pack_wt(static_cast<const uint16_t *>(w), static_cast<uint16_t *>(wt),
+                                        K, N, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "pack launch failed: %s", hipGetErrorString(e));
+    return ISD_OK;
+}
+
+isd_status_t isd_lm_head_packed(const void *h, const void *wt, int32_t M, int32_t K, int32_t N,
+                                void *logits, void *workspace, size_t ws_bytes, void *stream) {
+    (void)workspace;
+    (void)ws_bytes;
+    ISD_TRY(check_ptr(h, "h", 16));
+    ISD_TRY(check_ptr(wt, "wt", 16));
+    ISD_TRY(check_ptr(logits, "logits", 2));
+    if (M < 1 || N < 1 || K < 1) return fail(ISD_ERR_ARG, "M, K, N must be >= 1");
+    if (K % 64) return fail(ISD_ERR_ARG, "K must be a multiple of 64 (got %d)", (int)K);
+    const hipError_t e = launch_lm_head_packed(static_cast<const uint16_t *>(h),
+                                               static_cast<const uint16_t *>(wt), M, K, N,
+                                               static_cast<uint16_t *>(logits), (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "lm_head launch failed: %s", hipGetErrorString(e));
+    return ISD_OK;
+}
+
 isd_status_t isd_decode_masks(int32_t C, int32_t L, const int32_t *state,
                               const int32_t *accept_len, int32_t *bonus_mask,
                               int32_t *anchor_mask, void *stream) {

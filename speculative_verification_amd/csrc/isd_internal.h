@@ -141,6 +141,11 @@ hipError_t launch_decode_commit(int C, int L, int32_t *state, const int32_t *acc
                                 const int32_t *anchor, int32_t *history, int64_t hist_cap,
                                 int64_t *tokens, int64_t *forwards, hipStream_t stream);
 
+// LM-head GEMM on a pre-packed head wt = w^T [N, K], and the packing.
+hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
+                                 uint16_t *out, hipStream_t stream);
+hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStream_t stream);
+
 // LM-head GEMM (bf16 in, fp32 accumulate, bf16 out).
 hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, int N,
                           uint16_t *out, hipStream_t stream);

@@ -149,6 +149,138 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const uint16_t *__restrict
         }
 }
 
+// ---------------------------------------------------------------------------
+// Pre-packed head: logits[M, N] = h[M, K] @ wt[N, K]^T
+// ---------------------------------------------------------------------------
+//
+// With the head stored k-contiguous per vocabulary row (wt = w^T, packed
+// once), both MFMA operands are 8 consecutive k of one row: every global
+// load and every LDS store is one 16-byte vector, with no transposition.
+// The workgroup owns a 256 x 128 output tile like the kernel above but keeps
+// a single LDS buffer (55 KB) so that two workgroups share a CU: the next K
+// step's tiles are held in registers while the current one is multiplied,
+// and the two workgroups' barrier phases interleave.
+
+constexpr int kPBM = 256, kPBN = 128, kPBK = 64;
+constexpr int kPLd = kPBK + 8;                              // LDS row length (bf16), padded
+constexpr int kPVecRow = kPBK / 8;                          // 16-byte vectors per row per step
+constexpr int kPAPerThread = kPBM * kPVecRow / kThreadsG;   // 8
+constexpr int kPBPerThread = kPBN * kPVecRow / kThreadsG;   // 4
+
+__global__ __launch_bounds__(256, 2) void lm_head_packed_kernel(
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ wt, int M, int K, int N,
+    uint16_t *__restrict__ out, int m_tiles, int total, int per_xcd) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[kPBM * kPLd];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[kPBN * kPLd];
+
+    const int b = blockIdx.x;
+    const int idx = (b % kXcds) * per_xcd + b / kXcds;
+    if (idx >= total) return;
+    const int m0 = (idx % m_tiles) * kPBM;
+    const int n0 = (idx / m_tiles) * kPBN;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64;
+    const int wm = wave / 2, wn = wave % 2;
+
+    // thread tid moves the 16-byte vectors tid, tid + 256, ... of each tile
+    uint4 ra[kPAPerThread], rb[kPBPerThread];
+    auto load_step = [&](int k0) {
+#pragma unroll
+        for (int r = 0; r < kPAPerThread; ++r) {
+            const int v = tid + kThreadsG * r;
+            const int row = m0 + v / kPVecRow, kk = k0 + (v % kPVecRow) * 8;
+            ra[r] = row < M ? *reinterpret_cast<const uint4 *>(h + (size_t)row * K + kk)
+                            : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < kPBPerThread; ++r) {
+            const int v = tid + kThreadsG * r;
+            const int col = n0 + v / kPVecRow, kk = k0 + (v % kPVecRow) * 8;
+            rb[r] = col < N ? *reinterpret_cast<const uint4 *>(wt + (size_t)col * K + kk)
+                            : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_step = [&]() {
+#pragma unroll
+        for (int r = 0; r < kPAPerThread; ++r) {
+            const int v = tid + kThreadsG * r;
+            *reinterpret_cast<uint4 *>(&As[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = ra[r];
+        }
+#pragma unroll
+        for (int r = 0; r < kPBPerThread; ++r) {
+            const int v = tid + kThreadsG * r;
+            *reinterpret_cast<uint4 *>(&Bs[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = rb[r];
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+
+    const int nk = K / kPBK;
+    load_step(0);
+    for (int kt = 0; kt < nk; ++kt) {
+        store_step();
+        __syncthreads();
+        if (kt + 1 < nk) load_step((kt + 1) * kPBK);
+#pragma unroll
+        for (int ks = 0; ks < kPBK / 16; ++ks) {
+            const int kk = ks * 16 + 8 * (lane / 32);
+            bf16x8 af[4], bfr[2];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                af[mi] = *reinterpret_cast<const bf16x8 *>(
+                    &As[(wm * 128 + mi * 32 + lane % 32) * kPLd + kk]);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                bfr[ni] = *reinterpret_cast<const bf16x8 *>(
+                    &Bs[(wn * 64 + ni * 32 + lane % 32) * kPLd + kk]);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+            const int col = n0 + wn * 64 + ni * 32 + lane % 32;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * 128 + mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+                if (row < M && col < N) out[(size_t)row * N + col] = bf16_rne(acc[mi][ni][i]);
+            }
+        }
+}
+
+// wt[N, K] = w[K, N]^T through 64 x 64 LDS tiles (bit copies).
+__global__ __launch_bounds__(256) void pack_wt_kernel(const uint16_t *__restrict__ w,
+                                                      uint16_t *__restrict__ wt, int K, int N) {
+    __shared__ uint16_t t[64][65];
+    const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int kk = i / 64, nn = i % 64;
+        const int k = k0 + kk, n = n0 + nn;
+        t[kk][nn] = (k < K && n < N) ? w[(size_t)k * N + n] : 0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int nn = i / 64, kk = i % 64;
+        const int k = k0 + kk, n = n0 + nn;
+        if (k < K && n < N) wt[(size_t)n * K + k] = t[kk][nn];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, int N, uint16_t *out,
@@ -160,6 +292,24 @@ hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, in
     const int per_xcd = (int)((total + kXcds - 1) / kXcds);
     hipLaunchKernelGGL(lm_head_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, h,
                        w, M, K, N, out, m_tiles, (int)total, per_xcd);
+    return hipGetLastError();
+}
+
+hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
+                                 uint16_t *out, hipStream_t stream) {
+    const int m_tiles = (M + kPBM - 1) / kPBM;
+    const int n_tiles = (N + kPBN - 1) / kPBN;
+    const long long total = (long long)m_tiles * n_tiles;
+    if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
+    const int per_xcd = (int)((total + kXcds - 1) / kXcds);
+    hipLaunchKernelGGL(lm_head_packed_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0,
+                       stream, h, wt, M, K, N, out, m_tiles, (int)total, per_xcd);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((K + 63) / 64));
+    hipLaunchKernelGGL(pack_wt_kernel, grid, dim3(256), 0, stream, w, wt, K, N);
     return hipGetLastError();
 }
 

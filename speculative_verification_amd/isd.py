@@ -50,6 +50,8 @@ _SIGS = {
     "isd_decode_masks": (ctypes.c_int, [_i32, _i32] + [_vp] * 4 + [_vp]),
     "isd_decode_commit": (ctypes.c_int, [_i32, _i32] + [_vp] * 6 + [_i64, _vp, _vp, _vp]),
     "isd_lm_head": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "isd_lm_head_packed": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "isd_lm_head_pack": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "isd_check_device_error": (ctypes.c_int, [_vp, _sz, _vp]),
     "isd_set_tuning": (ctypes.c_int, [_i32, _i32, _i32, _i64]),
     "isd_last_error": (ctypes.c_char_p, []),
@@ -369,6 +371,32 @@ def lm_head(h, w, out=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=h.device)
     _check(lib().isd_lm_head(_ptr(h), _ptr(w), M, K, N, _ptr(out), None, 0, _stream()))
+    return out
+
+
+def lm_head_pack(w):
+    """wt [N, K] = w [K, N]^T, the head layout of lm_head_packed (a one-time pack)."""
+    if w.dtype != torch.bfloat16 or not w.is_contiguous():
+        raise ValueError("lm_head_pack takes a contiguous bf16 tensor")
+    K, N = w.shape
+    wt = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    _check(lib().isd_lm_head_pack(_ptr(w), K, N, _ptr(wt), _stream()))
+    return wt
+
+
+def lm_head_packed(h, wt, out=None):
+    """logits [M, N] = h [M, K] @ wt [N, K]^T (bf16, fp32 accumulation on MFMA)."""
+    if h.dtype != torch.bfloat16 or wt.dtype != torch.bfloat16:
+        raise ValueError("lm_head_packed takes bf16 tensors")
+    if not (h.is_contiguous() and wt.is_contiguous()):
+        raise ValueError("lm_head_packed takes contiguous tensors")
+    M, K = h.shape
+    N, K2 = wt.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=h.device)
+    _check(lib().isd_lm_head_packed(_ptr(h), _ptr(wt), M, K, N, _ptr(out), None, 0, _stream()))
     return out
 
 

@@ -86,3 +86,38 @@ def test_lm_head_rejects_bad_shapes(isd):
     w = torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(isd.IsdError):
         isd.lm_head(h, w)
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 256, 1000), (64, 4096, 2048), (257, 128, 136), (5, 64, 7)])
+def test_lm_head_packed_small_shapes(isd, M, K, N):
+    """The pre-packed head: the pack is a bit-exact transpose, and the GEMM
+    meets the same bound as the unpacked one."""
+    import torch
+    rng = np.random.default_rng(M * 11 + N)
+    h_bits = f32_to_bf16_bits(rng.normal(0, 1, (M, K)).astype(np.float32))
+    w_bits = f32_to_bf16_bits(rng.normal(0, 0.02, (K, N)).astype(np.float32))
+    w = _dev_bf16(w_bits)
+    wt = isd.lm_head_pack(w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(wt.view(torch.int16).cpu().numpy().view(np.uint16), w_bits.T)
+    out = isd.lm_head_packed(_dev_bf16(h_bits), wt)
+    torch.cuda.synchronize()
+    gpu = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    worst, frac = _check(gpu, h_bits, w_bits, np.arange(M))
+    log(f"lm_head_packed {M}x{K}x{N}: worst err/bound {worst:.3f}, exact-rounded fraction {frac:.5f}")
+
+
+def test_lm_head_packed_full_shape_sampled_rows(isd):
+    import torch
+    cfg = CONFIGS[4]
+    w_bits = gen_head_weights(4)
+    h_bits = gen_hidden(4, 1)
+    wt = isd.lm_head_pack(_dev_bf16(w_bits))
+    out = isd.lm_head_packed(_dev_bf16(h_bits), wt)
+    torch.cuda.synchronize()
+    gpu = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert gpu.shape == (cfg["C"] * 2 * cfg["L"], cfg["V"])
+    rows = np.array([0, 3, 255, 256, 600, 1023])
+    worst, frac = _check(gpu, h_bits, w_bits, rows)
+    log(f"lm_head_packed full shape, rows {rows.tolist()}: worst err/bound {worst:.3f}, "
+        f"exact-rounded fraction {frac:.5f}")
