@@ -54,6 +54,8 @@ from __future__ import annotations
 import numpy as np
 
 TIE_WINDOW = 1e-6
+# Gumbel-max draws are flagged when the best two perturbed log-weights are this close.
+GUMBEL_WINDOW = 1e-4
 
 
 # ---------------------------------------------------------------------------
@@ -124,6 +126,68 @@ def inverse_cdf(weights: np.ndarray, u: np.ndarray):
     return idx.astype(np.int64), margin, total
 
 
+# ---------------------------------------------------------------------------
+# Gumbel-max draws driven by a counter-based generator
+# ---------------------------------------------------------------------------
+#
+# The correction of the pages' serving kernel is a Gumbel-max draw
+# ("Introspective Diffusion Language Models | Summary", section 3.3): the
+# token is argmax_i (ln w_i + G_i) with independent standard Gumbel noise G_i,
+# which selects i with probability w_i / sum(w).  The noise of vocabulary
+# entry i comes from Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+# random numbers: as easy as 1, 2, 3", SC 2011), written here from its
+# published definition: ten rounds of two 32x32->64 multiplications by
+# 0xD2511F53 and 0xCD9E8D57 with the key bumped by the Weyl constants
+# 0x9E3779B9 and 0xBB67AE85 between rounds.
+#
+# Reading (listed in the design doc): for sequence c with first rejection j the key
+# is (bits of the float32 u_resid[c, j], c) and entry i takes 32-bit word i % 4
+# of the block with counter (i // 4, j, 0x15D, 0); U = ((word >> 8) + 1/2) / 2^24
+# (exact in float32, strictly inside (0, 1)) and G = -ln(-ln U).
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32-10 blocks.  counter: four uint32 arrays (broadcast together),
+    key: two uint32 arrays.  Returns four uint32 arrays."""
+    c0, c1, c2, c3 = (np.asarray(v, dtype=np.uint64) & _U32 for v in counter)
+    k0, k1 = (np.asarray(v, dtype=np.uint64) & _U32 for v in key)
+    for r in range(10):
+        if r:
+            k0 = (k0 + np.uint64(_PHILOX_W[0])) & _U32
+            k1 = (k1 + np.uint64(_PHILOX_W[1])) & _U32
+        p0 = np.uint64(_PHILOX_M[0]) * c0
+        p1 = np.uint64(_PHILOX_M[1]) * c2
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & _U32,
+                          (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & _U32)
+    return tuple(v.astype(np.uint32) for v in (c0, c1, c2, c3))
+
+
+def gumbel_noise(key0: int, key1: int, j: int, V: int) -> np.ndarray:
+    """Standard Gumbel noise [V] (float64) of one correction draw."""
+    i = np.arange(V, dtype=np.uint64)
+    blocks = philox4x32_10((i >> np.uint64(2), np.full(V, j), np.full(V, 0x15D), np.zeros(V)),
+                           (np.full(V, key0), np.full(V, key1)))
+    words = np.stack(blocks, axis=-1)[np.arange(V), (i & np.uint64(3)).astype(np.int64)]
+    u = ((words >> np.uint32(8)).astype(np.float64) + 0.5) * 2.0 ** -24
+    return -np.log(-np.log(u))
+
+
+def gumbel_argmax(weights: np.ndarray, g: np.ndarray):
+    """argmax over w > 0 of ln w + g (lowest index on ties), and the gap to the
+    second best perturbed value (inf when only one weight is positive)."""
+    w = np.asarray(weights, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        score = np.where(w > 0, np.log(w), -np.inf) + g
+    best = int(np.argmax(score))
+    rest = np.delete(score, best)
+    gap = score[best] - rest.max() if rest.size and np.isfinite(rest.max()) else np.inf
+    return best, gap
+
+
 def accept_ratio(px: np.ndarray, qx: np.ndarray) -> np.ndarray:
     """min(1, px/qx), with the q(x) = 0 convention (1 if px > 0 else 0)."""
     px = np.asarray(px, dtype=np.float64)
@@ -137,7 +201,8 @@ def accept_ratio(px: np.ndarray, qx: np.ndarray) -> np.ndarray:
 # Sample mode
 # ---------------------------------------------------------------------------
 
-def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False):
+def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False,
+                  sampler="cdf", seq_ids=None):
     """ISD verification of proposals ``x`` against the anchor, batched.
 
     p, q: [B, L, V] logits (anchor rows, proposal rows that generated x);
@@ -149,7 +214,10 @@ def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False):
         the exact rule); the correction and alpha are unchanged;
       q_onehot: the proposals were argmax picks, so their law is one-hot at
         x (q is not read): the ratio is P(x) and the residual is P with x
-        removed.
+        removed;
+      sampler = "gumbel" draws the correction by Gumbel-max with the noise of
+        ``gumbel_noise`` (seq_ids: the sequences' indices c in the batch, for
+        the key; default 0..B-1) instead of by inverse CDF.
     Returns a dict of per-sequence arrays:
       accept_len [B], out_tokens [B, L] (-1 padded), n_emitted [B],
       p_x, q_x, ratio [B, L], alpha [B], decision_margin [B] (smallest
@@ -200,7 +268,20 @@ def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False):
         Z = R.sum(axis=-1)
         resid_fallback[rows] = Z == 0
         W = np.where((Z == 0)[:, None], Pj, R)
-        tok, margin, _ = inverse_cdf(W, ur[rows, jj])
+        if sampler == "gumbel":
+            ids = np.arange(B) if seq_ids is None else np.asarray(seq_ids)
+            bits = np.asarray(ur, dtype=np.float32).view(np.uint32)
+            tok = np.empty(rows.size, dtype=np.int64)
+            margin = np.empty(rows.size)
+            for n, (b, jb) in enumerate(zip(rows, jj)):
+                g = gumbel_noise(int(bits[b, jb]), int(ids[b]), int(jb), V)
+                tok[n], gap = gumbel_argmax(W[n], g)
+                # a gap under GUMBEL_WINDOW counts as a near tie
+                margin[n] = TIE_WINDOW * gap / GUMBEL_WINDOW
+        elif sampler == "cdf":
+            tok, margin, _ = inverse_cdf(W, ur[rows, jj])
+        else:
+            raise ValueError(f"unknown sampler {sampler!r}")
         out[rows, jj] = tok
         resid_margin[rows] = np.where(Z == 0, 0.0, margin)
 
