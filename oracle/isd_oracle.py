@@ -142,7 +142,7 @@ def inverse_cdf(weights: np.ndarray, u: np.ndarray):
 #
 # Reading (listed in the design doc): for sequence c with first rejection j the key
 # is (bits of the float32 u_resid[c, j], c) and entry i takes 32-bit word i % 4
-# of the block with counter (i // 4, j, 0x15D, 0); U = ((word >> 8) + 1/2) / 2^24
+# of the block with counter (i // 4, j, 0x15D, 0); U = (2 * (word >> 9) + 1) / 2^24
 # (exact in float32, strictly inside (0, 1)) and G = -ln(-ln U).
 
 _PHILOX_M = (0xD2511F53, 0xCD9E8D57)
@@ -172,7 +172,7 @@ def gumbel_noise(key0: int, key1: int, j: int, V: int) -> np.ndarray:
     blocks = philox4x32_10((i >> np.uint64(2), np.full(V, j), np.full(V, 0x15D), np.zeros(V)),
                            (np.full(V, key0), np.full(V, key1)))
     words = np.stack(blocks, axis=-1)[np.arange(V), (i & np.uint64(3)).astype(np.int64)]
-    u = ((words >> np.uint32(8)).astype(np.float64) + 0.5) * 2.0 ** -24
+    u = (2.0 * (words >> np.uint32(9)).astype(np.float64) + 1.0) * 2.0 ** -24
     return -np.log(-np.log(u))
 
 
