@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--resid-segments", type=int, default=0)
     ap.add_argument("--propose-segments", type=int, default=0)
+    ap.add_argument("--sampler", choices=["cdf", "gumbel"], default="cdf",
+                    help="correction draw: inverse CDF or Gumbel-max on Philox4x32-10")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -280,7 +282,7 @@ def main():
 
     d0 = dev_sets[0]
     call = isd.StepCall(d0["p"], d0["q"], d0["x"], uni[0, 0], uni[0, 1], d0["qn"], uni[0, 2],
-                        mode=mode, temperature=T)
+                        mode=mode, temperature=T, sampler=args.sampler)
 
     def bind(i):
         t = dev_sets[i % nsets]
@@ -328,7 +330,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("kernel_digest") == kernel_digest() and tr.get("config") == args.config:
+        if (tr.get("kernel_digest") == kernel_digest() and tr.get("config") == args.config
+                and tr.get("sampler", "cdf") == args.sampler):
             traffic = tr.get("bytes_per_launch")
 
     acc = accept.cpu().numpy()
@@ -348,7 +351,8 @@ def main():
         data="synthetic",
         config=dict(workload=f"{cfg['name']} ISD step: C={C}, L={L}, V={V}, bf16 logits, "
                              f"{'greedy' if mode == 'greedy' else f'T={T}'}",
-                    C=C, L=L, V=V, logits_dtype="bf16", mode=mode, input_sets=nsets,
+                    C=C, L=L, V=V, logits_dtype="bf16", mode=mode, sampler=args.sampler,
+                    input_sets=nsets,
                     parallelism="single GPU"),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic),

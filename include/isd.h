@@ -87,6 +87,19 @@ typedef enum { ISD_DTYPE_BF16 = 0, ISD_DTYPE_F32 = 1 } isd_dtype_t;
  * q_logits and all uniforms are ignored (may be NULL). */
 typedef enum { ISD_MODE_SAMPLE = 0, ISD_MODE_GREEDY = 1 } isd_mode_t;
 
+/* How the correction token is drawn from the residual max(0, P - Q) (P if
+ * that is empty) after a rejection (sample mode; section 3.2).
+ * ISD_SAMPLER_CDF: inverse CDF in vocabulary order at the uniform
+ *   u_resid[c, j].
+ * ISD_SAMPLER_GUMBEL: Gumbel-max, the correction of the pages' fused
+ *   verification kernel (section 3.3): argmax_i ln w_i + G_i with standard
+ *   Gumbel noise G_i = -ln(-ln U_i), ties to the lowest index.  U_i comes from
+ *   Philox4x32-10 (Salmon et al., SC 2011) with key (bits of the fp32
+ *   u_resid[c, j], c) and counter (i / 4, j, 0x15D, 0), word i % 4 of the
+ *   block w giving U_i = (2 * (w >> 9) + 1) / 2^24; c is the sequence's index
+ *   in the call.  Same law as the inverse CDF, different samples. */
+typedef enum { ISD_SAMPLER_CDF = 0, ISD_SAMPLER_GUMBEL = 1 } isd_sampler_t;
+
 typedef struct {
     int32_t C;           /* concurrent sequences, >= 1 */
     int32_t L;           /* strided positions per step, 1..64 */
@@ -103,6 +116,7 @@ typedef struct {
                             is one-hot at x (section 3.3 with a sampled anchor): q_logits
                             is not read (may be NULL), the ratio is P(x), and the
                             correction draws from P with x removed.  0: q_logits as given */
+    int32_t sampler;     /* isd_sampler_t of the correction draw (sample mode) */
 } isd_shape_t;
 
 /* Workspace bytes needed by any call on shape `s`; 0 if `s` is invalid. */

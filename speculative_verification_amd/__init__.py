@@ -9,6 +9,8 @@ from .isd import (  # noqa: F401
     DTYPE_F32,
     MODE_GREEDY,
     MODE_SAMPLE,
+    SAMPLER_CDF,
+    SAMPLER_GUMBEL,
     IsdError,
     Shape,
     Decoder,

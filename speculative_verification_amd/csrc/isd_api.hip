@@ -74,6 +74,9 @@ isd_status_t check_shape(const isd_shape_t *s, bool need_temperature) {
     if (!(isfinite(s->relax) && s->relax >= 0.0f))
         return fail(ISD_ERR_ARG, "relax must be finite and >= 0");
     if (s->q_onehot != 0 && s->q_onehot != 1) return fail(ISD_ERR_ARG, "q_onehot must be 0 or 1");
+    if (s->sampler != ISD_SAMPLER_CDF && s->sampler != ISD_SAMPLER_GUMBEL)
+        return fail(ISD_ERR_ARG, "sampler must be 0 (inverse CDF) or 1 (Gumbel-max), got %d",
+                    (int)s->sampler);
     return ISD_OK;
 }
 
@@ -148,6 +151,7 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
 
     a.q_onehot = (!greedy && s->q_onehot) ? 1 : 0;
     a.relax1p = greedy ? 1.0 : 1.0 + (double)s->relax;
+    a.sampler = (!greedy && s->sampler == ISD_SAMPLER_GUMBEL) ? 1 : 0;
     a.rows_pq = plan.verify ? ((greedy || a.q_onehot) ? L : 2 * L) : 0;
     a.n_pq = C * a.rows_pq * a.S;
     a.q_blk = plan.propose ? L * a.Sq : 0;
@@ -198,6 +202,8 @@ WorkspaceLayout workspace_layout(int C, int L, int V) {
     off = align256(off + sizeof(ResTile) * (size_t)C * tiles_row);
     lay.off_info = off;
     off = align256(off + sizeof(SeqInfo) * C);
+    lay.off_garg = off;
+    off = align256(off + sizeof(ArgRec) * 2 * (size_t)C * kMaxResidSegments);
     lay.total = off;
     return lay;
 }
@@ -215,6 +221,7 @@ Workspace workspace_at(void *base, const WorkspaceLayout &lay) {
     w.tiles = reinterpret_cast<TileRec *>(b + lay.off_tiles);
     w.rtiles = reinterpret_cast<ResTile *>(b + lay.off_rtiles);
     w.info = reinterpret_cast<SeqInfo *>(b + lay.off_info);
+    w.garg = reinterpret_cast<ArgRec *>(b + lay.off_garg);
     return w;
 }
 

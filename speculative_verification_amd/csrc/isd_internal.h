@@ -81,11 +81,12 @@ struct Workspace {
     TileRec *tiles;            // [C*L*tiles_row] mask rows
     ResTile *rtiles;           // [C*tiles_row]  residual rows
     SeqInfo *info;             // [C]
+    ArgRec *garg;              // [C*kMaxResidSegments*2] Gumbel-max partials (R, P) per residual segment
 };
 
 struct WorkspaceLayout {
     size_t off_seq_cnt, off_res_cnt, off_flag, off_row_cnt, off_seg, off_tiles,
-        off_rtiles, off_info, total;
+        off_rtiles, off_info, off_garg, total;
     int smax;
 };
 
@@ -105,6 +106,7 @@ struct StepArgs {
     const int32_t *vmask, *pmask;   // per-sequence verify / propose masks (NULL: all)
     double relax1p;            // 1 + tau: the accept test uses min(1, (1 + tau) P/Q)
     int q_onehot;              // proposals are argmax picks: Q = onehot(x), q not read
+    int sampler;               // correction draw: 0 inverse CDF, 1 Gumbel-max
     // outputs (NULL when not requested)
     int32_t *accept_len, *out_tokens, *n_emitted;
     float *p_x, *q_x, *alpha, *alpha_mean;

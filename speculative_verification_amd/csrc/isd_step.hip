@@ -646,6 +646,8 @@ struct Shared {
     double sums[kWavesPerGroup];
     float vals[kWavesPerGroup];
     int idxs[kWavesPerGroup];
+    float vals2[kWavesPerGroup];
+    int idxs2[kWavesPerGroup];
     SeqInfo info;
 };
 
@@ -994,6 +996,121 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
     }
 }
 
+// ---------------------------------------------------------------------------
+// Gumbel-max correction
+// ---------------------------------------------------------------------------
+//
+// The correction of the pages' fused kernel is a Gumbel-max draw
+// ("Introspective Diffusion Language Models | Summary", section 3.3): the
+// token is argmax_i ln w_i + G_i with G_i = -ln(-ln U_i).  Since exp is
+// increasing, that is argmax_i w_i / E_i with E_i = -ln U_i, which costs one
+// logarithm and one reciprocal per entry instead of two logarithms; the
+// ratio's relative error is a few fp32 ulps.  The noise comes from
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011), implemented here from that definition: ten
+// rounds of two 32x32->64-bit products, the key bumped by the Weyl constants
+// between rounds.  Entry i uses word i % 4 of the block at counter
+// (i / 4, j, 0x15D, 0) under key (bits of u_resid[c, j], c).
+
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
+constexpr uint32_t kGumbelStream = 0x15Du;
+
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += kPhiloxW0;
+            k1 += kPhiloxW1;
+        }
+        const uint32_t hi0 = __umulhi(kPhiloxM0, c[0]), lo0 = kPhiloxM0 * c[0];
+        const uint32_t hi1 = __umulhi(kPhiloxM1, c[2]), lo1 = kPhiloxM1 * c[2];
+        const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+}
+
+// 1 / E for the 8 consecutive entries first, first + 1, ... (first % 8 == 0)
+// of correction position j under key (k0, k1).
+__device__ __forceinline__ void inv_exp_noise8(uint32_t first, uint32_t j, uint32_t k0,
+                                               uint32_t k1, float (&inv_e)[kGroupElems]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        uint32_t w[4] = {(first >> 2) + (uint32_t)b, j, kGumbelStream, 0u};
+        philox4x32_10(w, k0, k1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // U = (2 * (w >> 9) + 1) / 2^24: exact in fp32, strictly inside (0, 1)
+            const float u = (float)(((w[e] >> 9) << 1) | 1u) * 0x1p-24f;
+            inv_e[b * 4 + e] = __builtin_amdgcn_rcpf(-logf(u));
+        }
+    }
+}
+
+// Running per-lane argmax of a score over entries visited in increasing index
+// order: strict '>' keeps the first of equal scores; zero scores never win.
+__device__ __forceinline__ void gumbel_take(float s, int i, float &bv, int &bi) {
+    if (s > bv) {
+        bv = s;
+        bi = i;
+    }
+}
+
+// Block-wide merge of the per-wave argmax pairs (v, i) and (v2, i2); thread 0
+// writes them to rec[0] and rec[1].
+__device__ __forceinline__ void gumbel_publish(Shared &sh, int wave, int lane, float v, int i,
+                                               float v2, int i2, ArgRec *rec) {
+    wave_argmax(v, i);
+    wave_argmax(v2, i2);
+    if (lane == 0) {
+        sh.vals[wave] = v;
+        sh.idxs[wave] = i;
+        sh.vals2[wave] = v2;
+        sh.idxs2[wave] = i2;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float bv = 0.0f, bv2 = 0.0f;
+        int bi = INT_MAX, bi2 = INT_MAX;
+        for (int w = 0; w < kWavesPerGroup; ++w) {
+            if (arg_better(sh.vals[w], sh.idxs[w], bv, bi)) {
+                bv = sh.vals[w];
+                bi = sh.idxs[w];
+            }
+            if (arg_better(sh.vals2[w], sh.idxs2[w], bv2, bi2)) {
+                bv2 = sh.vals2[w];
+                bi2 = sh.idxs2[w];
+            }
+        }
+        st_pair(&rec[0], pack2(bv, bi));
+        st_pair(&rec[1], pack2(bv2, bi2));
+    }
+}
+
+// Merges the n segment records (pairs of R and P partials) of one correction
+// and clears them (one wavefront).  Returns the Gumbel-max token over R if
+// any R entry is positive, else over P.
+__device__ __forceinline__ int gumbel_finish(ArgRec *rec, int n, int lane) {
+    float vr = 0.0f, vp = 0.0f;
+    int ir = INT_MAX, ip = INT_MAX;
+    if (lane < n) {
+        const uint64_t r = ld_pair(&rec[2 * lane]), q = ld_pair(&rec[2 * lane + 1]);
+        vr = lo_f(r);
+        ir = hi_i(r);
+        vp = lo_f(q);
+        ip = hi_i(q);
+        st_pair(&rec[2 * lane], 0);
+        st_pair(&rec[2 * lane + 1], 0);
+    }
+    wave_argmax(vr, ir);
+    wave_argmax(vp, ip);
+    const int tok = vr > 0.0f ? ir : ip;
+    return tok == INT_MAX ? 0 : tok;
+}
+
 template <typename T, bool VEC>
 __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shared &sh, int wave,
                                          int lane) {
@@ -1029,7 +1146,58 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
     const T *prow = static_cast<const T *>(a.p) + row_offset(a, c, j < L ? j : 0);
     const T *qrow = static_cast<const T *>(a.q) + row_offset(a, c, j < L ? j : 0);
 
-    if (j < L && a.q_onehot) {
+    if (j < L && a.sampler) {
+        // Gumbel-max partials of this segment: best R / E and best P / E
+        const uint32_t k0 = __float_as_uint(inf.u), k1 = (uint32_t)c;
+        float br = 0.0f, bp = 0.0f;
+        int ir = INT_MAX, ip = INT_MAX;
+        auto take = [&](const float (&P)[kGroupElems], const float (&R)[kGroupElems], int tile,
+                        int g) {
+            const long long first = elem_index(tile, lane, g * kGroupElems);
+            float inv_e[kGroupElems];
+            inv_exp_noise8((uint32_t)first, (uint32_t)j, k0, k1, inv_e);
+#pragma unroll
+            for (int e = 0; e < kGroupElems; ++e) {
+                gumbel_take(R[e] * inv_e[e], (int)first + e, br, ir);
+                gumbel_take(P[e] * inv_e[e], (int)first + e, bp, ip);
+            }
+        };
+        const int tb = seg * a.tpsr;
+        const int te = min(a.tiles_row, tb + a.tpsr);
+        if (a.q_onehot) {
+            stream_row<T, VEC>(prow, tb, te, a.V, wave, lane, [&](const TileRaw<T> &rp, int tile) {
+#pragma unroll
+                for (int g = 0; g < kGroupsPerTile; ++g) {
+                    float P[kGroupElems], R[kGroupElems];
+#pragma unroll
+                    for (int e = 0; e < kGroupElems; ++e) {
+                        const int i = g * kGroupElems + e;
+                        P[e] = fast_exp2(fmaf(elem<T>(rp, i), a.k2, -inf.cp)) * inf.inv_sp;
+                        R[e] = elem_index(tile, lane, i) == (long long)inf.xj ? 0.0f : P[e];
+                    }
+                    take(P, R, tile, g);
+                }
+            });
+        } else {
+            stream_rows2<T, VEC>(prow, qrow, tb, te, a.V, wave, lane,
+                                 [&](const TileRaw<T> &rp, const TileRaw<T> &rq, int tile) {
+#pragma unroll
+                for (int g = 0; g < kGroupsPerTile; ++g) {
+                    float P[kGroupElems], R[kGroupElems];
+#pragma unroll
+                    for (int e = 0; e < kGroupElems; ++e) {
+                        const int i = g * kGroupElems + e;
+                        P[e] = fast_exp2(fmaf(elem<T>(rp, i), a.k2, -inf.cp)) * inf.inv_sp;
+                        const float Q = fast_exp2(fmaf(elem<T>(rq, i), a.k2, -inf.cq)) * inf.inv_sq;
+                        R[e] = fmaxf(P[e] - Q, 0.0f);
+                    }
+                    take(P, R, tile, g);
+                }
+            });
+        }
+        gumbel_publish(sh, wave, lane, br, ir, bp, ip,
+                       a.ws.garg + ((size_t)c * kMaxResidSegments + seg) * 2);
+    } else if (j < L && a.q_onehot) {
         // Q is one-hot at x_j: the residual is P with x_j removed
         const int tb = seg * a.tpsr;
         const int te = min(a.tiles_row, tb + a.tpsr);
@@ -1080,7 +1248,10 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
 
     if (!arrive(counter(a.ws.res_cnt, c), (uint32_t)a.r_blk, &sh.flag)) return;
     if (wave != 0) return;
-    if (j < L) {
+    if (j < L && a.sampler) {
+        const int tok = gumbel_finish(a.ws.garg + (size_t)c * kMaxResidSegments * 2, a.Sr, lane);
+        if (lane == 0 && a.verify_outputs) a.out_tokens[c * L + j] = tok;
+    } else if (j < L) {
         // ---- inverse-CDF draw over max(0, P - Q) (P if that is empty) ----
         const uint64_t *recs = reinterpret_cast<const uint64_t *>(rt);
         const int nt = a.tiles_row;

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libisd.so")
 ISD_OK, ISD_ERR_ARG, ISD_ERR_UNSUPPORTED, ISD_ERR_WORKSPACE, ISD_ERR_DEVICE = range(5)
 DTYPE_BF16, DTYPE_F32 = 0, 1
 MODE_SAMPLE, MODE_GREEDY = 0, 1
+SAMPLER_CDF, SAMPLER_GUMBEL = 0, 1
 
 _STATUS_NAMES = {ISD_ERR_ARG: "ISD_ERR_ARG", ISD_ERR_UNSUPPORTED: "ISD_ERR_UNSUPPORTED",
                  ISD_ERR_WORKSPACE: "ISD_ERR_WORKSPACE", ISD_ERR_DEVICE: "ISD_ERR_DEVICE"}
@@ -35,7 +36,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("C", ctypes.c_int32), ("L", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("ld", ctypes.c_int64), ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("ldc", ctypes.c_int64),
-                ("relax", ctypes.c_float), ("q_onehot", ctypes.c_int32)]
+                ("relax", ctypes.c_float), ("q_onehot", ctypes.c_int32),
+                ("sampler", ctypes.c_int32)]
 
 
 _vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
@@ -114,10 +116,19 @@ def _logits_layout(t: torch.Tensor):
     return C, L, V, ld, ldc, code
 
 
+def _sampler_code(sampler) -> int:
+    if sampler in ("cdf", SAMPLER_CDF):
+        return SAMPLER_CDF
+    if sampler in ("gumbel", SAMPLER_GUMBEL):
+        return SAMPLER_GUMBEL
+    raise ValueError(f"unknown sampler {sampler!r}")
+
+
 def make_shape(logits: torch.Tensor, mode: int = MODE_SAMPLE, temperature: float = 1.0,
-               relax: float = 0.0, q_onehot: bool = False) -> Shape:
+               relax: float = 0.0, q_onehot: bool = False, sampler="cdf") -> Shape:
     C, L, V, ld, ldc, code = _logits_layout(logits)
-    return Shape(C, L, V, ld, code, mode, float(temperature), ldc, float(relax), int(bool(q_onehot)))
+    return Shape(C, L, V, ld, code, mode, float(temperature), ldc, float(relax),
+                 int(bool(q_onehot)), _sampler_code(sampler))
 
 
 def _same_layout(ref: Shape, t, name: str, mode: int, temperature: float):
@@ -167,11 +178,11 @@ def _out(out, key, shape, dtype, device):
 
 
 def verify_step(p, q, x, ua, ur, *, mode="sample", temperature=1.0, relax=0.0, q_onehot=False,
-                out=None, ws=None):
+                sampler="cdf", out=None, ws=None):
     """Verify proposals x [C, L] against anchor rows p (and proposal rows q;
     None with q_onehot)."""
     m = _mode_code(mode)
-    shape = make_shape(p, m, temperature, relax, q_onehot)
+    shape = make_shape(p, m, temperature, relax, q_onehot, sampler)
     if m == MODE_SAMPLE:
         _same_layout(shape, q, "q", m, temperature)
     C, L, dev = shape.C, shape.L, p.device
@@ -222,9 +233,9 @@ class StepCall:
     timing loop pays one ctypes call per step."""
 
     def __init__(self, p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, relax=0.0,
-                 q_onehot=False, out=None, ws=None):
+                 q_onehot=False, sampler="cdf", out=None, ws=None):
         m = _mode_code(mode)
-        self.shape = make_shape(p, m, temperature, relax, q_onehot)
+        self.shape = make_shape(p, m, temperature, relax, q_onehot, sampler)
         _same_layout(self.shape, qn, "qn", m, temperature)
         if m == MODE_SAMPLE:
             _same_layout(self.shape, q, "q", m, temperature)
@@ -257,17 +268,17 @@ class StepCall:
 
 
 def step(p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, relax=0.0, q_onehot=False,
-         out=None, ws=None):
+         sampler="cdf", out=None, ws=None):
     """One fused ISD step (verify + propose in one launch)."""
     return StepCall(p, q, x, ua, ur, qn, up, mode=mode, temperature=temperature, relax=relax,
-                    q_onehot=q_onehot, out=out, ws=ws)()
+                    q_onehot=q_onehot, sampler=sampler, out=out, ws=ws)()
 
 
 def step_masked(p, q, x, ua, ur, qn, up, verify_mask=None, propose_mask=None, *, mode="sample",
-                temperature=1.0, relax=0.0, q_onehot=False, out=None, ws=None):
+                temperature=1.0, relax=0.0, q_onehot=False, sampler="cdf", out=None, ws=None):
     """isd_step with per-sequence verify / propose masks (int32 [C]; None = all)."""
     m = _mode_code(mode)
-    shape = make_shape(p, m, temperature, relax, q_onehot)
+    shape = make_shape(p, m, temperature, relax, q_onehot, sampler)
     _same_layout(shape, qn, "qn", m, temperature)
     if m == MODE_SAMPLE:
         _same_layout(shape, q, "q", m, temperature)

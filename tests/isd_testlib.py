@@ -52,9 +52,10 @@ def to_host(o: dict) -> dict:
 
 
 def oracle_step(d: dict, dtype: str, mode: str, T: float, chunk: int = 8, relax: float = 0.0,
-                q_onehot: bool = False) -> dict:
+                q_onehot: bool = False, sampler: str = "cdf") -> dict:
     """Oracle outputs for every sequence in d (chunked to bound memory);
-    relax and q_onehot select the verification variants (sample mode)."""
+    relax, q_onehot and sampler select the verification variants (sample
+    mode).  The Gumbel-max key takes each sequence's index in the whole call."""
     n = d["x"].shape[0]
     parts = []
     for s0 in range(0, n, chunk):
@@ -75,7 +76,8 @@ def oracle_step(d: dict, dtype: str, mode: str, T: float, chunk: int = 8, relax:
         else:
             q = None if q_onehot else O.decode_logits(d["q"][sl], dtype)
             v = O.verify_sample(p, q, d["x"][sl], d["ua"][sl], d["ur"][sl], T, relax=relax,
-                                q_onehot=q_onehot)
+                                q_onehot=q_onehot, sampler=sampler,
+                                seq_ids=np.arange(sl.start, sl.stop))
             tok, prob, _, pflag = O.propose_sample(qn, d["up"][sl], T)
         parts.append(dict(accept_len=v["accept_len"], out_tokens=v["out_tokens"],
                           n_emitted=v["n_emitted"], p_x=v["p_x"], q_x=v["q_x"],

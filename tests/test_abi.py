@@ -200,6 +200,14 @@ def test_variant_shape_validation(isd):
     bad = _shape(isd)
     bad.q_onehot = 2
     assert _verify(isd, bad) == 1 and "q_onehot" in lib.isd_last_error().decode()
+    for v in (2, -1):
+        bad = _shape(isd)
+        bad.sampler = v
+        assert _verify(isd, bad) == 1 and "sampler" in lib.isd_last_error().decode()
+    import torch
+    assert isd.make_shape(torch.zeros(1, 1, 8), sampler="gumbel").sampler == 1
+    with pytest.raises(ValueError):
+        isd.make_shape(torch.zeros(1, 1, 8), sampler="topk")
     # with one-hot proposals q may be NULL: the only remaining error is the workspace size
     ok = _shape(isd)
     ok.q_onehot = 1
