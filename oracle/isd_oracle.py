@@ -127,6 +127,68 @@ def inverse_cdf(weights: np.ndarray, u: np.ndarray):
 
 
 # ---------------------------------------------------------------------------
+# Truncated sampling laws (top-k, then top-p)
+# ---------------------------------------------------------------------------
+#
+# The pages' quality runs sample at temperature 1 with top-k 50 and top-p 0.95
+# ("Introspective Diffusion Language Models | Summary", section 4.1), and the
+# verification must use the law of the proposal mechanism actually used
+# (section 3.3): with truncation both P and Q are the truncated laws.
+#
+# Reading (listed in the design doc): entries are ranked by logit, larger first,
+# ties to the lower vocabulary index; top-k keeps the first k of that ranking
+# (exactly k, ties included in rank order); top-p then keeps an entry of the
+# ranking iff the probability mass, within the top-k renormalised law, of the
+# entries ranked before it is below p; the survivors are renormalised.  k = 0
+# disables top-k and p >= 1 disables top-p.  The top-p cut is a floating-point
+# decision: a row whose cumulative mass lies within TRUNC_WINDOW of p at some
+# rank is flagged.
+
+TRUNC_WINDOW = 1e-9
+
+
+def truncated_probs(logits: np.ndarray, temperature: float = 1.0, top_k: int = 0,
+                    top_p: float = 1.0):
+    """The truncated law of each row, float64 [..., V], and the top-p margin
+    [...] (smallest |mass before rank t - p| over the top-k ranks; inf when
+    top-p is off)."""
+    a = np.asarray(logits, dtype=np.float64) / float(temperature)
+    if np.isnan(a).any() or np.isposinf(a).any():
+        raise ValueError("logits contain NaN or +inf")
+    if top_k < 0 or not top_p > 0:
+        raise ValueError("top_k must be >= 0 and top_p > 0")
+    V = a.shape[-1]
+    rows = a.reshape(-1, V)
+    out = np.zeros_like(rows)
+    margin = np.full(rows.shape[0], np.inf)
+    k = V if top_k == 0 else min(int(top_k), V)
+    for n, z in enumerate(rows):
+        # stable sort of the negated logits: larger first, ties to the lower index
+        rank = np.argsort(-z, kind="stable")[:k]
+        zk = z[rank]
+        if np.isneginf(zk[0]):
+            raise ValueError("a logits row is entirely -inf")
+        w = np.exp(zk - zk[0])
+        keep = np.ones(k, dtype=bool)
+        if top_p < 1.0:
+            pi = w / w.sum()
+            before = np.concatenate([[0.0], np.cumsum(pi)[:-1]])
+            keep = before < top_p
+            margin[n] = np.abs(before - top_p).min()
+        out[n, rank[keep]] = w[keep] / w[keep].sum()
+    return out.reshape(a.shape), margin.reshape(a.shape[:-1])
+
+
+def sampling_law(logits, temperature=1.0, top_k=0, top_p=1.0):
+    """(law [..., V], top-p margin [...]): softmax(logits / T) when no
+    truncation is asked for, else ``truncated_probs``."""
+    if top_k == 0 and top_p >= 1.0:
+        P = softmax(logits, temperature)
+        return P, np.full(P.shape[:-1], np.inf)
+    return truncated_probs(logits, temperature, top_k, top_p)
+
+
+# ---------------------------------------------------------------------------
 # Gumbel-max draws driven by a counter-based generator
 # ---------------------------------------------------------------------------
 #
@@ -202,7 +264,7 @@ def accept_ratio(px: np.ndarray, qx: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False,
-                  sampler="cdf", seq_ids=None):
+                  sampler="cdf", seq_ids=None, top_k=0, top_p=1.0):
     """ISD verification of proposals ``x`` against the anchor, batched.
 
     p, q: [B, L, V] logits (anchor rows, proposal rows that generated x);
@@ -217,7 +279,10 @@ def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False,
         removed;
       sampler = "gumbel" draws the correction by Gumbel-max with the noise of
         ``gumbel_noise`` (seq_ids: the sequences' indices c in the batch, for
-        the key; default 0..B-1) instead of by inverse CDF.
+        the key; default 0..B-1) instead of by inverse CDF;
+      top_k, top_p truncate both laws (``truncated_probs``): P and Q are the
+        truncated anchor and proposal laws, and a sequence whose rows have a
+        top-p margin under TRUNC_WINDOW is flagged.
     Returns a dict of per-sequence arrays:
       accept_len [B], out_tokens [B, L] (-1 padded), n_emitted [B],
       p_x, q_x, ratio [B, L], alpha [B], decision_margin [B] (smallest
@@ -233,12 +298,14 @@ def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False,
     if relax < 0:
         raise ValueError("relax must be >= 0")
 
-    P = softmax(p, temperature)
+    P, trunc_margin = sampling_law(p, temperature, top_k, top_p)
+    trunc_margin = trunc_margin.min(axis=-1)
     if q_onehot:
         Q = np.zeros_like(P)
         np.put_along_axis(Q, x[..., None], 1.0, axis=-1)
     else:
-        Q = softmax(np.asarray(q, dtype=np.float64), temperature)
+        Q, mq = sampling_law(np.asarray(q, dtype=np.float64), temperature, top_k, top_p)
+        trunc_margin = np.minimum(trunc_margin, mq.min(axis=-1))
     px = np.take_along_axis(P, x[..., None], axis=-1)[..., 0]
     qx = np.take_along_axis(Q, x[..., None], axis=-1)[..., 0]
     r = accept_ratio(px, qx)
@@ -285,7 +352,7 @@ def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False,
         out[rows, jj] = tok
         resid_margin[rows] = np.where(Z == 0, 0.0, margin)
 
-    flagged = decision_margin < TIE_WINDOW
+    flagged = (decision_margin < TIE_WINDOW) | (trunc_margin < TRUNC_WINDOW)
     resid_flagged = (resid_margin < TIE_WINDOW) | resid_fallback
     return dict(accept_len=j, out_tokens=out, n_emitted=n_emitted, p_x=px, q_x=qx,
                 ratio=r, alpha=alpha, decision_margin=decision_margin,
@@ -293,16 +360,17 @@ def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False,
                 flagged=flagged, resid_flagged=resid_flagged)
 
 
-def propose_sample(qn, up, temperature=1.0):
+def propose_sample(qn, up, temperature=1.0, top_k=0, top_p=1.0):
     """Draw the next proposals from the mask-position logits, batched.
 
     qn: [..., V] logits; up: [...] uniforms.  Returns ``(tokens, prob,
-    margin, flagged)`` where prob is softmax(qn/T) at the drawn token.
+    margin, flagged)`` where prob is the sampling law (softmax(qn/T), or its
+    top-k / top-p truncation) at the drawn token.
     """
-    Qn = softmax(qn, temperature)
+    Qn, trunc_margin = sampling_law(qn, temperature, top_k, top_p)
     tok, margin, _ = inverse_cdf(Qn, up)
     prob = np.take_along_axis(Qn, tok[..., None], axis=-1)[..., 0]
-    return tok, prob, margin, margin < TIE_WINDOW
+    return tok, prob, margin, (margin < TIE_WINDOW) | (trunc_margin < TRUNC_WINDOW)
 
 
 def alpha_sample(p, q, x, temperature=1.0):
