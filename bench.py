@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_isd_step_serving.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_verification_amd", "csrc", f)
-                  for f in ("isd_step.hip", "isd_internal.h", "isd_api.hip")]
+                  for f in ("isd_step.hip", "isd_device.h", "isd_internal.h", "isd_api.hip")]
 
 
 def kernel_digest() -> str:

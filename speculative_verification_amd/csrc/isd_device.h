@@ -1,0 +1,379 @@
+// Device building blocks shared by the ISD kernels: wavefront reductions,
+// vectorised tile loads of logits rows, the records and completion counters
+// that workgroups of one launch exchange, and the Philox4x32-10 generator of
+// the Gumbel-max draws.
+#pragma once
+
+#include "isd_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace isd {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// Wavefront primitives
+// ---------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// row_ror:n rotates within each row of 16 lanes; four rotations give every
+// lane its row's result, two cross-row exchanges finish the wavefront.  All
+// lanes end with bitwise-identical results.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0x128>(v));
+    v = fmaxf(v, dpp<0x124>(v));
+    v = fmaxf(v, dpp<0x122>(v));
+    v = fmaxf(v, dpp<0x121>(v));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0x128>(v);
+    v += dpp<0x124>(v);
+    v += dpp<0x122>(v);
+    v += dpp<0x121>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        double n = __shfl_up(v, o);
+        if (lane >= o) v += n;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_first(unsigned long long mask) {
+    return __ffsll((long long)mask) - 1;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 2^n for an integer-valued float n, saturating far below the fp64 range.
+__device__ __forceinline__ double pow2_int(float n) {
+    return ldexp(1.0, (int)fmaxf(n, -2000.0f));
+}
+
+// ---------------------------------------------------------------------------
+// Tile loads
+// ---------------------------------------------------------------------------
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct TileRaw {
+    static constexpr int kWords = kLaneElems * (int)sizeof(T) / 4;
+    uint32_t w[kWords];
+};
+
+template <typename T>
+__device__ __forceinline__ uint32_t neg_inf_bits();
+template <>
+__device__ __forceinline__ uint32_t neg_inf_bits<uint16_t>() { return 0xFF80u; }
+template <>
+__device__ __forceinline__ uint32_t neg_inf_bits<float>() { return 0xFF800000u; }
+
+template <typename T>
+__device__ __forceinline__ uint32_t load_bits(const T *p) {
+    if constexpr (sizeof(T) == 2) return (uint32_t)(*reinterpret_cast<const uint16_t *>(p));
+    else return *reinterpret_cast<const uint32_t *>(p);
+}
+
+// One lane's 8-element group at element offset i of `row` (8 consecutive
+// elements); elements at or past V read as -inf and are never loaded.  With
+// VEC the group is one or two 16-byte non-temporal loads when it lies wholly
+// below V: the logits are streamed once, and non-temporal loads keep them
+// from displacing useful cache lines and measurably raise the read rate.
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_group(const T *__restrict__ row, long long i, int V, bool whole,
+                                           uint32_t *w) {
+    constexpr int kVecPerGroup = kGroupElems * (int)sizeof(T) / 16;   // 1 (bf16) or 2 (fp32)
+    if (VEC && whole) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(row + i);
+#pragma unroll
+        for (int h = 0; h < kVecPerGroup; ++h) {
+            const u32x4 v = __builtin_nontemporal_load(&src[h]);
+            w[h * 4 + 0] = v.x;
+            w[h * 4 + 1] = v.y;
+            w[h * 4 + 2] = v.z;
+            w[h * 4 + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kGroupElems; ++e) {
+            const uint32_t b = (i + e < (long long)V) ? load_bits<T>(row + i + e) : neg_inf_bits<T>();
+            if constexpr (sizeof(T) == 2) {
+                if (e & 1) w[e >> 1] |= b << 16;
+                else w[e >> 1] = b;
+            } else {
+                w[e] = b;
+            }
+        }
+    }
+}
+
+// Lane `lane`'s 32 elements of tile `tile` of `row`; elements at or past V
+// read as -inf and are never loaded.  In the last, partial tile of a row the
+// groups wholly below V still take the vector path, so that tile costs about
+// what a full one does.
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_tile(const T *__restrict__ row, int tile, int V, int lane,
+                                          TileRaw<T> &r) {
+    constexpr int kWordsPerGroup = kGroupElems * (int)sizeof(T) / 4;
+    const long long base = (long long)tile * kTileElems + lane * kGroupElems;
+    const bool full = (long long)(tile + 1) * kTileElems <= (long long)V;
+#pragma unroll
+    for (int g = 0; g < kGroupsPerTile; ++g) {
+        const long long i = base + g * (kWave * kGroupElems);
+        load_group<T, VEC>(row, i, V, full || i + kGroupElems <= (long long)V,
+                           &r.w[g * kWordsPerGroup]);
+    }
+}
+
+// Element idx (0..31, group-major) of a lane's tile as fp32.
+template <typename T>
+__device__ __forceinline__ float elem(const TileRaw<T> &r, int idx) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w = r.w[idx >> 1];
+        return (idx & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    } else {
+        return __uint_as_float(r.w[idx]);
+    }
+}
+
+// Vocab index of element idx of lane `lane` in tile `tile`.
+__device__ __forceinline__ long long elem_index(int tile, int lane, int idx) {
+    return (long long)tile * kTileElems + (idx / kGroupElems) * (kWave * kGroupElems) +
+           lane * kGroupElems + (idx % kGroupElems);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_value(const T *row, long long i) {
+    const uint32_t b = load_bits<T>(row + i);
+    if constexpr (sizeof(T) == 2) return __uint_as_float(b << 16);
+    else return __uint_as_float(b);
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack(const TileRaw<T> &r, float (&v)[kLaneElems]) {
+#pragma unroll
+    for (int i = 0; i < kLaneElems; ++i) v[i] = elem<T>(r, i);
+}
+
+__device__ __forceinline__ float max32(const float (&v)[kLaneElems]) {
+    float m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m[i] = fmaxf(v[i], v[i + 16]);
+#pragma unroll
+    for (int s = 8; s >= 1; s >>= 1)
+#pragma unroll
+        for (int i = 0; i < s; ++i) m[i] = fmaxf(m[i], m[i + s]);
+    return m[0];
+}
+
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&e)[N]) {
+#pragma unroll
+    for (int s = N / 2; s >= 1; s >>= 1)
+#pragma unroll
+        for (int i = 0; i < s; ++i) e[i] += e[i + s];
+    return e[0];
+}
+
+// Streams tiles tile_begin + wave, + kWavesPerGroup, ... < tile_end of `row`,
+// keeping the loads of the next AHEAD tiles in flight while `f` consumes the
+// current one.
+template <typename T, bool VEC, typename F>
+__device__ __forceinline__ void stream_row(const T *__restrict__ row, int tile_begin, int tile_end,
+                                           int V, int wave, int lane, F &&f) {
+    int t = tile_begin + wave;
+    if (t >= tile_end) return;
+    TileRaw<T> cur;
+    load_tile<T, VEC>(row, t, V, lane, cur);
+    for (;;) {
+        const int tn = t + kWavesPerGroup;
+        const bool more = tn < tile_end;
+        TileRaw<T> nxt;
+        if (more) load_tile<T, VEC>(row, tn, V, lane, nxt);
+        f(cur, t);
+        if (!more) break;
+        cur = nxt;
+        t = tn;
+    }
+}
+
+// Streams the same tiles of two rows together (one tile of each in flight).
+template <typename T, bool VEC, typename F>
+__device__ __forceinline__ void stream_rows2(const T *__restrict__ ra, const T *__restrict__ rb,
+                                             int tile_begin, int tile_end, int V, int wave,
+                                             int lane, F &&f) {
+    for (int t = tile_begin + wave; t < tile_end; t += kWavesPerGroup) {
+        TileRaw<T> ca, cb;
+        load_tile<T, VEC>(ra, t, V, lane, ca);
+        load_tile<T, VEC>(rb, t, V, lane, cb);
+        f(ca, cb, t);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Data exchanged between workgroups of one launch
+// ---------------------------------------------------------------------------
+//
+// Records that one workgroup writes and another reads in the same launch
+// (segment partials, tile masses, the per-sequence decision) are written and
+// read with agent-scope atomic stores and loads, which are coherent across
+// the XCDs and never served from a stale per-XCD L2 line.  Each wave waits
+// for its own record stores to complete (s_waitcnt) before the workgroup
+// barrier; thread 0 then counts the workgroup with one relaxed atomic on a
+// counter that has a 128-byte line to itself.  No agent-scope fence is
+// issued: on this part such a fence writes back or invalidates the L2 and,
+// issued by thousands of workgroups, serialises the launch.
+
+__device__ __forceinline__ void st32(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st64(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld32(const uint32_t *p) {
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld64(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
+    return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+}
+__device__ __forceinline__ uint64_t pack2(float lo, int hi) {
+    return (uint64_t)__float_as_uint(lo) | ((uint64_t)(uint32_t)hi << 32);
+}
+__device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
+__device__ __forceinline__ int hi_i(uint64_t v) { return (int)(uint32_t)(v >> 32); }
+
+__device__ __forceinline__ void st_pair(void *r, uint64_t v) { st64(static_cast<uint64_t *>(r), v); }
+__device__ __forceinline__ uint64_t ld_pair(const void *r) {
+    return ld64(static_cast<const uint64_t *>(r));
+}
+
+// Completes this workgroup's share of a unit counted by `counter` (total
+// arrivals `total`).  All threads call it after their record stores; it
+// returns, to every thread, whether this was the last arrival.  The last one
+// resets the counter for the next launch.
+__device__ __forceinline__ bool arrive(uint32_t *counter, uint32_t total, int *s_flag) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev + 1 == total;
+        if (last) st32(counter, 0u);
+        *s_flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    const bool last = *s_flag != 0;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return last;
+}
+
+__device__ __forceinline__ bool arg_better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ void wave_argmax(float &bv, int &bi) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (arg_better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t *counter(uint32_t *base, int i) {
+    return base + (size_t)i * kCounterStride;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10
+// ---------------------------------------------------------------------------
+//
+// Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3"
+// (SC 2011), implemented from that definition: ten rounds of two 32x32->64-bit
+// products, the key bumped by the Weyl constants between rounds.  The Gumbel
+// noise of vocabulary entry i at correction position j under key (k0, k1) is
+// word i % 4 of the block at counter (i / 4, j, 0x15D, 0), turned into
+// U = (2 * (w >> 9) + 1) / 2^24 (exact in fp32, strictly inside (0, 1)).
+
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
+constexpr uint32_t kGumbelStream = 0x15Du;
+
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += kPhiloxW0;
+            k1 += kPhiloxW1;
+        }
+        const uint32_t hi0 = __umulhi(kPhiloxM0, c[0]), lo0 = kPhiloxM0 * c[0];
+        const uint32_t hi1 = __umulhi(kPhiloxM1, c[2]), lo1 = kPhiloxM1 * c[2];
+        const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+}
+
+// 1 / E for the 8 consecutive entries first, first + 1, ... (first % 8 == 0)
+// of correction position j under key (k0, k1).
+__device__ __forceinline__ void inv_exp_noise8(uint32_t first, uint32_t j, uint32_t k0,
+                                               uint32_t k1, float (&inv_e)[kGroupElems]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        uint32_t w[4] = {(first >> 2) + (uint32_t)b, j, kGumbelStream, 0u};
+        philox4x32_10(w, k0, k1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // U = (2 * (w >> 9) + 1) / 2^24: exact in fp32, strictly inside (0, 1)
+            const float u = (float)(((w[e] >> 9) << 1) | 1u) * 0x1p-24f;
+            inv_e[b * 4 + e] = __builtin_amdgcn_rcpf(-logf(u));
+        }
+    }
+}
+
+// 1 / E for the single entry i (same noise as inv_exp_noise8).
+__device__ __forceinline__ float inv_exp_noise1(uint32_t i, uint32_t j, uint32_t k0, uint32_t k1) {
+    uint32_t w[4] = {i >> 2, j, kGumbelStream, 0u};
+    philox4x32_10(w, k0, k1);
+    const uint32_t sel = i & 3u;
+    const uint32_t word = sel == 0 ? w[0] : sel == 1 ? w[1] : sel == 2 ? w[2] : w[3];
+    const float u = (float)(((word >> 9) << 1) | 1u) * 0x1p-24f;
+    return __builtin_amdgcn_rcpf(-logf(u));
+}
+
+}  // namespace
+}  // namespace isd
