@@ -64,6 +64,11 @@ def parse():
     ap.add_argument("--propose-segments", type=int, default=0)
     ap.add_argument("--sampler", choices=["cdf", "gumbel"], default="cdf",
                     help="correction draw: inverse CDF or Gumbel-max on Philox4x32-10")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="truncate P, Q and the proposal law to the top k entries (0: off)")
+    ap.add_argument("--top-p", type=float, default=1.0, help="nucleus mass with --top-k (1: off)")
+    ap.add_argument("--trunc-segments", type=int, default=0,
+                    help="workgroups per row on the truncated path (0: automatic)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -260,6 +265,7 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     isd.set_tuning(args.segments, args.resid_segments, 0, args.propose_segments)
+    isd.set_trunc_tuning(args.trunc_segments)
 
     nsets = max(1, args.sets)
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -282,7 +288,8 @@ def main():
 
     d0 = dev_sets[0]
     call = isd.StepCall(d0["p"], d0["q"], d0["x"], uni[0, 0], uni[0, 1], d0["qn"], uni[0, 2],
-                        mode=mode, temperature=T, sampler=args.sampler)
+                        mode=mode, temperature=T, sampler=args.sampler, top_k=args.top_k,
+                        top_p=args.top_p)
 
     def bind(i):
         t = dev_sets[i % nsets]
@@ -331,7 +338,7 @@ def main():
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("kernel_digest") == kernel_digest() and tr.get("config") == args.config
-                and tr.get("sampler", "cdf") == args.sampler):
+                and tr.get("sampler", "cdf") == args.sampler and args.top_k == 0):
             traffic = tr.get("bytes_per_launch")
 
     acc = accept.cpu().numpy()
@@ -352,6 +359,7 @@ def main():
         config=dict(workload=f"{cfg['name']} ISD step: C={C}, L={L}, V={V}, bf16 logits, "
                              f"{'greedy' if mode == 'greedy' else f'T={T}'}",
                     C=C, L=L, V=V, logits_dtype="bf16", mode=mode, sampler=args.sampler,
+                    top_k=args.top_k, top_p=args.top_p,
                     input_sets=nsets,
                     parallelism="single GPU"),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",

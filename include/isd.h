@@ -51,8 +51,11 @@
  *     ISD_ERR_ARG          bad shape (C < 1, L not in [1, 64], V < 1, ld < V,
  *                          0 < ldc < L*ld),
  *                          a required NULL pointer, a base not aligned to its
- *                          element size, or T <= 0 / non-finite in sample mode
- *     ISD_ERR_UNSUPPORTED  unknown dtype or mode
+ *                          element size, T <= 0 / non-finite in sample mode,
+ *                          relax < 0, q_onehot or sampler out of range,
+ *                          top_k < 0, top_p < 0 or NaN
+ *     ISD_ERR_UNSUPPORTED  unknown dtype or mode, top_k > 64, top_p < 1
+ *                          without top_k
  *     ISD_ERR_WORKSPACE    ws_bytes smaller than isd_workspace_bytes()
  *     ISD_ERR_DEVICE       a HIP call failed (text in isd_last_error())
  *   Out-of-range proposal ids and NaN/+inf logits are undefined input; the
@@ -100,6 +103,19 @@ typedef enum { ISD_MODE_SAMPLE = 0, ISD_MODE_GREEDY = 1 } isd_mode_t;
  *   in the call.  Same law as the inverse CDF, different samples. */
 typedef enum { ISD_SAMPLER_CDF = 0, ISD_SAMPLER_GUMBEL = 1 } isd_sampler_t;
 
+/* Truncated laws (sample mode, top_k >= 1).  The pages' quality runs sample
+ * with top-k 50 and top-p 0.95 (section 4.1), and verification must use the
+ * law of the proposal mechanism actually used (section 3.3).  So with
+ * truncation P, Q and the law of the next proposals are all the truncated
+ * laws of their rows: rank the entries of a row by logit, larger first, ties
+ * to the lower index (-0 ranks as +0); keep the first top_k ranks; then, if
+ * top_p is on, keep a rank while the probability mass of the ranks before it
+ * (in the top-k renormalised law at temperature T) is below top_p; the
+ * survivors are renormalised.  Proposals and the correction draw over the
+ * survivors in increasing vocabulary index, exactly as without truncation.
+ * Greedy mode ignores truncation: it never changes an argmax.  top_p without
+ * top_k is ISD_ERR_UNSUPPORTED. */
+
 typedef struct {
     int32_t C;           /* concurrent sequences, >= 1 */
     int32_t L;           /* strided positions per step, 1..64 */
@@ -117,6 +133,12 @@ typedef struct {
                             is not read (may be NULL), the ratio is P(x), and the
                             correction draws from P with x removed.  0: q_logits as given */
     int32_t sampler;     /* isd_sampler_t of the correction draw (sample mode) */
+    int32_t top_k;       /* sample mode: 0 = no truncation; 1..64 = keep the top_k
+                            highest-ranked entries of every row (ranked by logit, ties to
+                            the lower index) */
+    float top_p;         /* sample mode, with top_k >= 1: nucleus mass in (0, 1); 0 (the
+                            zero-initialised value) or >= 1 turns it off.  See the
+                            truncated laws below. */
 } isd_shape_t;
 
 /* Workspace bytes needed by any call on shape `s`; 0 if `s` is invalid. */
@@ -272,6 +294,10 @@ isd_status_t isd_check_device_error(void *workspace, size_t ws_bytes, void *stre
  *                     before it gives up and flags the device error word */
 isd_status_t isd_set_tuning(int32_t segments, int32_t propose_segments, int32_t resid_segments,
                             int64_t spin_limit);
+
+/* Tuning knob of the truncated (top-k) path, process-wide: workgroups sharing
+ * one row (1..8); 0 restores the automatic choice. */
+isd_status_t isd_set_trunc_tuning(int32_t segments);
 
 /* Thread-local description of the last non-OK status of this thread. */
 const char *isd_last_error(void);

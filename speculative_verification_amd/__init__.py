@@ -26,6 +26,7 @@ from .isd import (  # noqa: F401
     make_shape,
     propose,
     propose_masked,
+    set_trunc_tuning,
     set_tuning,
     step,
     step_masked,

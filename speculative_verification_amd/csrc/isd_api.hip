@@ -28,10 +28,14 @@ isd_status_t fail(isd_status_t st, const char *fmt, ...) {
 std::atomic<int> g_segments{0};
 std::atomic<int> g_propose_segments{0};
 std::atomic<int> g_resid_segments{0};
+std::atomic<int> g_trunc_segments{0};
 // default decomposition (tiles of 2048 elements per workgroup segment)
 constexpr int kVerifyTilesPerSeg = 38;
 constexpr int kProposeTilesPerSeg = 19;
 constexpr int kResidTilesPerSeg = 8;
+// truncated path: split rows only as far as needed for about this many items
+// (each item's warm-up costs more than a longer stream)
+constexpr int kTruncTargetItems = 1024;
 constexpr int kItemOrder = 0;
 std::atomic<long long> g_spin_limit{0};
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
@@ -77,10 +81,20 @@ isd_status_t check_shape(const isd_shape_t *s, bool need_temperature) {
     if (s->sampler != ISD_SAMPLER_CDF && s->sampler != ISD_SAMPLER_GUMBEL)
         return fail(ISD_ERR_ARG, "sampler must be 0 (inverse CDF) or 1 (Gumbel-max), got %d",
                     (int)s->sampler);
+    if (s->top_k < 0) return fail(ISD_ERR_ARG, "top_k must be >= 0 (got %d)", (int)s->top_k);
+    if (s->top_k > kMaxTopK)
+        return fail(ISD_ERR_UNSUPPORTED, "top_k must be at most %d (got %d)", kMaxTopK, (int)s->top_k);
+    if (!(isfinite(s->top_p) && s->top_p >= 0.0f))
+        return fail(ISD_ERR_ARG, "top_p must be finite and >= 0 (0 or >= 1: off)");
+    if (s->top_p > 0.0f && s->top_p < 1.0f && s->top_k == 0)
+        return fail(ISD_ERR_UNSUPPORTED, "top_p needs top_k in [1, %d]", kMaxTopK);
     return ISD_OK;
 }
 
 size_t elem_size(const isd_shape_t *s) { return s->dtype == ISD_DTYPE_BF16 ? 2 : 4; }
+
+// Sample-mode calls with top-k (and possibly top-p) take the truncated path.
+bool truncated(const isd_shape_t *s) { return s->mode == ISD_MODE_SAMPLE && s->top_k > 0; }
 
 isd_status_t check_ptr(const void *p, const char *name, size_t align) {
     if (!p) return fail(ISD_ERR_ARG, "%s is NULL", name);
@@ -111,7 +125,8 @@ struct Plan {
 
 isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *workspace,
                  size_t ws_bytes, void *stream) {
-    const WorkspaceLayout lay = workspace_layout(s->C, s->L, s->V);
+    const bool trunc = truncated(s);
+    const WorkspaceLayout lay = workspace_layout(s->C, s->L, s->V, trunc);
     if (!workspace) return fail(ISD_ERR_ARG, "workspace is NULL");
     if (((uintptr_t)workspace) % 256) return fail(ISD_ERR_ARG, "workspace is not 256-byte aligned");
     if (ws_bytes < lay.total)
@@ -126,6 +141,7 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
     a.ldc = (long long)seq_stride(s);
     a.k2 = greedy ? 1.0f : (float)(1.4426950408889634 / (double)s->temperature);
     a.ws = workspace_at(workspace, lay);
+    a.tws = trunc_workspace_at(workspace, lay);
     a.tiles_row = ceil_div(V, kTileElems);
 
     // Segments per row.  Verify rows are dispatched first and can be large;
@@ -148,6 +164,34 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
     a.tpsr = ceil_div(a.tiles_row, Sr);
     a.Sr = ceil_div(a.tiles_row, a.tpsr);
     a.order = kItemOrder;
+
+    if (trunc) {
+        // truncated path: every row is cut into St segments; no residual items
+        a.q_onehot = s->q_onehot ? 1 : 0;
+        a.relax1p = 1.0 + (double)s->relax;
+        a.sampler = s->sampler == ISD_SAMPLER_GUMBEL ? 1 : 0;
+        a.top_k = min((int)s->top_k, V);
+        a.top_p = (s->top_p > 0.0f && s->top_p < 1.0f) ? (double)s->top_p : 1.0;
+        a.temp = (double)s->temperature;
+        a.rows_pq = plan.verify ? (s->q_onehot ? L : 2 * L) : 0;
+        const int rows = C * (a.rows_pq + (plan.propose ? L : 0));
+        int St = g_trunc_segments.load();
+        if (St <= 0) St = ceil_div(kTruncTargetItems, max(rows, 1));
+        St = max(1, min(St, min(kMaxTruncSegments, a.tiles_row)));
+        a.tpst = ceil_div(a.tiles_row, St);
+        a.St = ceil_div(a.tiles_row, a.tpst);
+        const long long n_items =
+            (long long)C * a.rows_pq * a.St + (plan.propose ? (long long)C * L * a.St : 0);
+        if (n_items <= 0 || n_items >= (1LL << 31))
+            return fail(ISD_ERR_ARG, "work decomposition out of range (%lld items)", n_items);
+        a.n_items = (int)n_items;
+        a.verify_outputs = plan.verify_outputs ? 1 : 0;
+        const bool vec = vec_ok(s, a.p, a.q, a.qn);
+        const hipError_t e = launch_trunc(a, s->dtype, vec, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return fail(ISD_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+        return ISD_OK;
+    }
 
     a.q_onehot = (!greedy && s->q_onehot) ? 1 : 0;
     a.relax1p = greedy ? 1.0 : 1.0 + (double)s->relax;
@@ -179,7 +223,7 @@ StepArgs blank_args() {
 
 }  // namespace
 
-WorkspaceLayout workspace_layout(int C, int L, int V) {
+WorkspaceLayout workspace_layout(int C, int L, int V, bool trunc) {
     WorkspaceLayout lay;
     const size_t CL = (size_t)C * L;
     const int tiles_row = ceil_div(V, kTileElems);
@@ -204,6 +248,24 @@ WorkspaceLayout workspace_layout(int C, int L, int V) {
     off = align256(off + sizeof(SeqInfo) * C);
     lay.off_garg = off;
     off = align256(off + sizeof(ArgRec) * 2 * (size_t)C * kMaxResidSegments);
+    lay.trunc = trunc;
+    lay.off_trow_cnt = lay.off_tseq_cnt = lay.off_tkeys = lay.off_tlists = lay.off_tpxq =
+        lay.off_talpha = 0;
+    if (trunc) {
+        const int St = min(kMaxTruncSegments, tiles_row);
+        lay.off_trow_cnt = off;
+        off = align256(off + cs * 3 * CL);
+        lay.off_tseq_cnt = off;
+        off = align256(off + cs * C);
+        lay.off_tkeys = off;
+        off = align256(off + sizeof(uint64_t) * 3 * CL * St * kWave);
+        lay.off_tlists = off;
+        off = align256(off + sizeof(uint64_t) * 2 * CL * kWave * 2);
+        lay.off_tpxq = off;
+        off = align256(off + sizeof(uint64_t) * 2 * CL);
+        lay.off_talpha = off;
+        off = align256(off + sizeof(uint32_t) * C);
+    }
     lay.total = off;
     return lay;
 }
@@ -225,6 +287,20 @@ Workspace workspace_at(void *base, const WorkspaceLayout &lay) {
     return w;
 }
 
+TruncWorkspace trunc_workspace_at(void *base, const WorkspaceLayout &lay) {
+    char *b = static_cast<char *>(base);
+    TruncWorkspace t;
+    memset(&t, 0, sizeof(t));
+    if (!lay.trunc) return t;
+    t.row_cnt = reinterpret_cast<uint32_t *>(b + lay.off_trow_cnt);
+    t.seq_cnt = reinterpret_cast<uint32_t *>(b + lay.off_tseq_cnt);
+    t.keys = reinterpret_cast<uint64_t *>(b + lay.off_tkeys);
+    t.lists = reinterpret_cast<uint64_t *>(b + lay.off_tlists);
+    t.pxq = reinterpret_cast<uint64_t *>(b + lay.off_tpxq);
+    t.alpha = reinterpret_cast<uint32_t *>(b + lay.off_talpha);
+    return t;
+}
+
 }  // namespace isd
 
 using namespace isd;
@@ -233,7 +309,7 @@ extern "C" {
 
 size_t isd_workspace_bytes(const isd_shape_t *s) {
     if (check_shape(s, false) != ISD_OK) return 0;
-    return workspace_layout(s->C, s->L, s->V).total;
+    return workspace_layout(s->C, s->L, s->V, truncated(s)).total;
 }
 
 isd_status_t isd_verify_step(const isd_shape_t *s, const void *p_logits, const void *q_logits,
@@ -491,6 +567,13 @@ isd_status_t isd_set_tuning(int32_t segments, int32_t propose_segments, int32_t 
     g_propose_segments.store(propose_segments);
     g_resid_segments.store(resid_segments);
     g_spin_limit.store(spin_limit);
+    return ISD_OK;
+}
+
+isd_status_t isd_set_trunc_tuning(int32_t segments) {
+    if (segments < 0 || segments > kMaxTruncSegments)
+        return fail(ISD_ERR_ARG, "segments must be in [0, %d]", kMaxTruncSegments);
+    g_trunc_segments.store(segments);
     return ISD_OK;
 }
 

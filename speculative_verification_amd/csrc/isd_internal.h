@@ -22,6 +22,8 @@ constexpr int kTileElems = kWave * kLaneElems;                 // 2048
 constexpr int kMaxL = 64;
 constexpr int kMaxSegments = 32;
 constexpr int kMaxResidSegments = 64;
+constexpr int kMaxTopK = 64;           // largest top-k of the truncated path
+constexpr int kMaxTruncSegments = 8;   // row segments of the truncated path
 // Completion counters and flags each own a 128-byte line: atomics that share
 // a line serialise at the memory side.
 constexpr int kCounterStride = 32;   // uint32 words
@@ -84,14 +86,28 @@ struct Workspace {
     ArgRec *garg;              // [C*kMaxResidSegments*2] Gumbel-max partials (R, P) per residual segment
 };
 
+// Records of the truncated (top-k / top-p) path; all return to zero.
+struct TruncWorkspace {
+    uint32_t *row_cnt;         // [C*3L] segments finished per row (p, q, then mask rows; strided)
+    uint32_t *seq_cnt;         // [C]    verify rows finished per sequence (strided)
+    uint64_t *keys;            // [C*3L*St*64] top keys of each row segment
+    uint64_t *lists;           // [C*2L*64*2] survivors of verify rows: (index, fp64 weight)
+    uint64_t *pxq;             // [C*2L] fp64 P'(x_k), then Q'(x_k)
+    uint32_t *alpha;           // [C] fp32 alpha (batch mean)
+};
+
 struct WorkspaceLayout {
     size_t off_seq_cnt, off_res_cnt, off_flag, off_row_cnt, off_seg, off_tiles,
         off_rtiles, off_info, off_garg, total;
+    size_t off_trow_cnt, off_tseq_cnt, off_tkeys, off_tlists, off_tpxq, off_talpha;
     int smax;
+    bool trunc;
 };
 
-WorkspaceLayout workspace_layout(int C, int L, int V);
+// `trunc` adds the records of the truncated path.
+WorkspaceLayout workspace_layout(int C, int L, int V, bool trunc);
 Workspace workspace_at(void *base, const WorkspaceLayout &lay);
+TruncWorkspace trunc_workspace_at(void *base, const WorkspaceLayout &lay);
 
 // Everything one launch of the step kernel needs (passed by value).
 struct StepArgs {
@@ -107,6 +123,9 @@ struct StepArgs {
     double relax1p;            // 1 + tau: the accept test uses min(1, (1 + tau) P/Q)
     int q_onehot;              // proposals are argmax picks: Q = onehot(x), q not read
     int sampler;               // correction draw: 0 inverse CDF, 1 Gumbel-max
+    int top_k;                 // truncated path: keep the first top_k ranks (1..64)
+    double top_p;              // truncated path: nucleus mass, or 1 (off)
+    double temp;               // T
     // outputs (NULL when not requested)
     int32_t *accept_len, *out_tokens, *n_emitted;
     float *p_x, *q_x, *alpha, *alpha_mean;
@@ -127,6 +146,9 @@ struct StepArgs {
     int verify_outputs;        // write tokens / counts (0: alpha only)
     int order;                 // 0: per sequence [mask rows, residual]; 1: all mask rows first
     uint32_t spin_limit;
+    // truncated path
+    int St, tpst;              // segments per row, tiles per segment
+    TruncWorkspace tws;
 };
 
 enum Dtype { kBf16 = 0, kF32 = 1 };
@@ -134,6 +156,8 @@ enum Mode { kSample = 0, kGreedy = 1 };
 
 // Launches the step kernel for `a` (dtype/mode select the instantiation).
 hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStream_t stream);
+// Launches the truncated (top-k / top-p) step kernel for `a` (sample mode).
+hipError_t launch_trunc(const StepArgs &a, int dtype, bool vec, hipStream_t stream);
 
 // Bookkeeping kernels of the multi-step decoding loop.
 hipError_t launch_decode_masks(int C, int L, const int32_t *state, const int32_t *accept_len,

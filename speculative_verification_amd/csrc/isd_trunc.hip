@@ -1,0 +1,632 @@
+// ISD step with top-k / top-p truncated sampling laws, for gfx950.
+//
+// The pages' quality runs sample with top-k 50 and top-p 0.95
+// ("Introspective Diffusion Language Models | Summary", section 4.1), and the
+// acceptance test must use the law of the proposal mechanism actually used
+// (section 3.3).  With truncation the anchor law P, the proposal law Q and the
+// law of the next proposals are each supported on at most k <= 64 entries of
+// their row, so the whole step reduces to one top-k selection per row; every
+// later stage works on those k entries.
+//
+// Ranking: entries are ordered by logit, larger first, ties to the lower
+// vocabulary index (-0 ranks as +0).  Each entry gets a unique 64-bit key
+// (order-preserving bits of the value, then the complemented index), so the
+// ranking is the order of the keys and the top k are the k largest keys.
+// top-k keeps the first k ranks; top-p then keeps a rank while the mass of the
+// ranks before it, in the top-k renormalised law, is below p; the survivors
+// are renormalised.  All probabilities and decisions are in fp64.
+//
+// Work items, in dispatch order:
+//   [verify-row items]  for each sequence c, each verify row (p_0..p_{L-1},
+//       then q_0..q_{L-1} unless the proposals are one-hot) and each row
+//       segment;
+//   [mask-row items]    for each sequence c, each mask row qn_k and segment.
+// An item streams its segment with four wavefronts.  Each wavefront keeps its
+// best 64 keys in a lane-distributed sorted list (lane t holds rank t) and a
+// threshold, the key of its rank k-1; an entry enters only if it beats the
+// threshold of its own wavefront or of any wavefront of the workgroup (shared
+// in LDS).  Candidates are merged 64 at a time with a bitonic sort and a
+// bitonic merge across lanes.  The workgroup's four lists are merged and the
+// segment's top k keys recorded.  The item that completes a row merges its
+// segment records, applies top-k and top-p and then either draws the next
+// proposal (mask row; inverse CDF over the survivors in vocabulary order) or
+// stores P'(x_k) or Q'(x_k) and the row's survivors sorted by index (verify
+// row).  The item that completes the last verify row of sequence c decides:
+// ratios, accept test, first rejection j, alpha, and the correction from
+// max(0, P' - Q') over the survivors of p_j (inverse CDF, or Gumbel-max).
+// No item ever waits for another.
+
+#include "isd_device.h"
+#include "isd_internal.h"
+
+#include <math.h>
+
+namespace isd {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Keys and lane-distributed sorted lists
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t ord_bits(float v) {
+    const uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);   // -0 ranks as +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Unique key of entry idx with value v; larger key = earlier rank.  0 is below
+// every real key and marks an empty slot.
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
+    return ((uint64_t)ord_bits(v) << 32) | (uint64_t)(uint32_t)~idx;
+}
+
+__device__ __forceinline__ float key_value(uint64_t k) {
+    const uint32_t o = (uint32_t)(k >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~(uint32_t)k; }
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// Bitonic sort of one key per lane across the wavefront, largest first.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t y = __shfl_xor(x, j);
+            const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+            x = keep_max ? umax64(x, y) : umin64(x, y);
+        }
+    }
+    return x;
+}
+
+// The 64 largest keys of two lists sorted largest first, sorted largest first:
+// the lane-wise max of one list and the other reversed is bitonic and holds
+// them; a bitonic merge sorts it.
+__device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t b, int lane) {
+    uint64_t x = umax64(a, __shfl(b, kWave - 1 - lane));
+#pragma unroll
+    for (int j = kWave / 2; j > 0; j >>= 1) {
+        const uint64_t y = __shfl_xor(x, j);
+        x = ((lane & j) == 0) ? umax64(x, y) : umin64(x, y);
+    }
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Selection of a segment's top k (one workgroup)
+// ---------------------------------------------------------------------------
+//
+// Every wavefront keeps its best keys in a lane-distributed sorted list and
+// filters entries against a threshold theta, the key of some list's rank k-1:
+// at least k entries beat it, so nothing at or below it can reach the top k.
+// The four wavefronts seed their lists with the 64 lane bests of their first
+// tile and take theta from the merged seeds (the k-th best of 256 entries),
+// which already discards nearly everything; later tiles are skipped unless a
+// lane's maximum reaches theta's value, and the few entries that beat theta
+// are inserted one at a time.  Wavefronts share their thresholds through LDS.
+
+template <typename T>
+struct TruncShared {
+    int flag;
+    unsigned long long theta;              // largest wavefront threshold of the workgroup
+    uint64_t lists[kWavesPerGroup][kWave];
+    // a tile with candidates is staged here so that single entries can be read
+    // back by (lane, element): word w of lane l at [w * 64 + l]
+    uint32_t stage[kWavesPerGroup][TileRaw<T>::kWords * kWave];
+};
+
+// The workgroup's shared threshold, read fresh (other wavefronts raise it).
+template <typename T>
+__device__ __forceinline__ uint64_t shared_theta(TruncShared<T> &sh) {
+    return (uint64_t)__hip_atomic_load(&sh.theta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Whole-wavefront shift by one lane (lane l gets lane l - 1; lane 0 keeps its
+// own value, which the caller never uses): DPP wave_shr:1.
+__device__ __forceinline__ uint64_t wave_shr1(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, 0x138, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), 0x138,
+                                               0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Key held by lane `l` (wave-uniform l).
+__device__ __forceinline__ uint64_t lane_key(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inserts a wave-uniform key into the sorted list (largest first); keys are
+// unique, so the lanes holding larger keys are exactly lanes 0..pos-1.
+__device__ __forceinline__ uint64_t list_insert(uint64_t list, uint64_t key, int lane) {
+    const int pos = __popcll(__ballot(list > key));
+    const uint64_t up = wave_shr1(list);
+    return lane < pos ? list : (lane == pos ? key : up);
+}
+
+// The lane's best entry of a tile: largest value, lowest index among equals
+// (a lane holds its entries in increasing index); 0 if it holds none below V.
+__device__ __forceinline__ uint64_t lane_best(const float (&v)[kLaneElems], float vmax, int tile,
+                                              int lane, int V) {
+    int fi = 0;
+#pragma unroll
+    for (int i = kLaneElems - 1; i >= 0; --i) fi = (v[i] == vmax) ? i : fi;
+    const long long idx = elem_index(tile, lane, fi);
+    return idx < V ? make_key(vmax, (uint32_t)idx) : 0;
+}
+
+struct SegSelect {
+    uint64_t list = 0;     // lane t: rank t of this wavefront's best keys so far
+    uint64_t theta = 0;    // wave-uniform threshold
+};
+
+// Element i of lane l of a staged tile, as fp32 (same layout as elem()).
+template <typename T>
+__device__ __forceinline__ float staged_value(const uint32_t *stage, int l, int i) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w = stage[(i >> 1) * kWave + l];
+        return (i & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    } else {
+        return __uint_as_float(stage[i * kWave + l]);
+    }
+}
+
+// Inserts every entry of the tile (raw words `raw`, values v) that beats the
+// threshold, except a lane's entry whose key equals `skip` (that lane's seed,
+// already listed).  The candidates are the entries whose value reaches the
+// threshold's value; they are visited one at a time in a compact loop.
+template <typename T>
+__device__ __forceinline__ void take_tile(const TileRaw<T> &raw, const float (&v)[kLaneElems],
+                                          float vmax, int tile, int V, int k, int wave, int lane,
+                                          uint64_t skip, SegSelect &s, TruncShared<T> &sh) {
+    s.theta = umax64(s.theta, shared_theta(sh));
+    const float tv = s.theta ? key_value(s.theta) : -__builtin_inff();
+    if (!__ballot(vmax >= tv)) return;
+    uint32_t cm = 0;   // the lane's candidate elements
+#pragma unroll
+    for (int i = 0; i < kLaneElems; ++i) cm |= (v[i] >= tv ? 1u : 0u) << i;
+    // a lane with one candidate holds it as its maximum; lanes with more are
+    // read back from a staged copy of the tile
+    const bool several = __popc(cm) > 1;
+    uint32_t *stage = sh.stage[wave];
+    if (__ballot(several)) {
+#pragma unroll
+        for (int w = 0; w < TileRaw<T>::kWords; ++w) stage[w * kWave + lane] = raw.w[w];
+    }
+    const unsigned long long multi = __ballot(several);
+    const uint64_t theta = s.theta;   // the list's own threshold is refreshed after the tile
+    bool raised = false;
+    for (;;) {
+        const unsigned long long lanes = __ballot(cm != 0);
+        if (!lanes) break;
+        const int l = __ffsll((long long)lanes) - 1;
+        const uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)cm, l);
+        const int i = __ffs((int)bits) - 1;
+        if (lane == l) cm &= cm - 1;
+        const long long idx = elem_index(tile, l, i);
+        if (idx >= V) continue;
+        const float vi = ((multi >> l) & 1ull)
+                             ? staged_value<T>(stage, l, i)
+                             : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vmax), l));
+        const uint64_t key = make_key(vi, (uint32_t)idx);
+        if (key <= theta || key == lane_key(skip, l)) continue;
+        s.list = list_insert(s.list, key, lane);
+        raised = true;
+    }
+    if (raised) {
+        s.theta = umax64(s.theta, uniform64(lane_key(s.list, k - 1)));
+        if (lane == 0) atomicMax(&sh.theta, (unsigned long long)s.theta);
+    }
+}
+
+// Top k keys of tiles [tb, te) of `row`, merged over the workgroup into
+// sh.lists[0] (largest first; 0 past the end).  All threads call it.
+template <typename T, bool VEC>
+__device__ __forceinline__ void select_segment(const T *__restrict__ row, int tb, int te, int V,
+                                               int k, int wave, int lane, TruncShared<T> &sh) {
+    if (threadIdx.x == 0) sh.theta = 0;
+    int t = tb + wave;
+    const bool have = t < te;
+    TileRaw<T> cur, nxt;
+    if (have) load_tile<T, VEC>(row, t, V, lane, cur);
+    bool more = have && t + kWavesPerGroup < te;
+    if (more) load_tile<T, VEC>(row, t + kWavesPerGroup, V, lane, nxt);
+
+    // seeds: the lane bests of each wavefront's first tile
+    float v[kLaneElems];
+    float vmax = -__builtin_inff();
+    uint64_t best = 0;
+    if (have) {
+        unpack<T>(cur, v);
+        vmax = max32(v);
+        best = lane_best(v, vmax, t, lane, V);
+    }
+    SegSelect s;
+    s.list = wave_sort_desc(best, lane);
+    sh.lists[wave][lane] = s.list;
+    __syncthreads();
+    uint64_t merged = sh.lists[0][lane];
+#pragma unroll
+    for (int w = 1; w < kWavesPerGroup; ++w) merged = wave_merge_desc(merged, sh.lists[w][lane], lane);
+    s.theta = uniform64(lane_key(merged, k - 1));
+    __syncthreads();
+    if (have) take_tile<T>(cur, v, vmax, t, V, k, wave, lane, best, s, sh);
+
+    while (more) {
+        t += kWavesPerGroup;
+        cur = nxt;
+        more = t + kWavesPerGroup < te;
+        if (more) load_tile<T, VEC>(row, t + kWavesPerGroup, V, lane, nxt);
+        unpack<T>(cur, v);
+        vmax = max32(v);
+        take_tile<T>(cur, v, vmax, t, V, k, wave, lane, 0, s, sh);
+    }
+
+    sh.lists[wave][lane] = s.list;
+    __syncthreads();
+    if (wave == 0) {
+        uint64_t x = sh.lists[0][lane];
+#pragma unroll
+        for (int w = 1; w < kWavesPerGroup; ++w) x = wave_merge_desc(x, sh.lists[w][lane], lane);
+        sh.lists[0][lane] = x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Truncated law of one row from its top keys (one wavefront)
+// ---------------------------------------------------------------------------
+
+struct RowLaw {
+    uint32_t idx;      // lane s < n: the s-th survivor in increasing vocabulary index
+    double w;          // its probability under the truncated law (0 for s >= n)
+    int n;             // survivors
+    bool empty;        // no finite logit among the top keys
+};
+
+// `top` holds the row's keys sorted largest first (lane t = rank t, 0 past the
+// row's end); ranks >= k are ignored.
+__device__ __forceinline__ RowLaw truncated_law(uint64_t top, int k, double temp, double top_p,
+                                                int lane) {
+    const bool real = lane < k && top != 0;
+    const float v = key_value(top);
+    const float v0 = __shfl(v, 0);
+    RowLaw law;
+    law.empty = __shfl(top, 0) == 0 || !(v0 > -__builtin_inff());
+    double w = 0.0;
+    if (real && !law.empty && v > -__builtin_inff())
+        w = exp((double)v / temp - (double)v0 / temp);
+    bool keep = real;
+    if (top_p < 1.0) {
+        const double W = wave_sum_d(w);
+        const double pi = W > 0.0 ? w / W : 0.0;
+        const double incl = wave_incl_scan_d(pi, lane);
+        double before = __shfl_up(incl, 1);
+        if (lane == 0) before = 0.0;
+        keep = real && before < top_p;
+    }
+    const double Wk = wave_sum_d(keep ? w : 0.0);
+    const double P = (keep && Wk > 0.0) ? w / Wk : 0.0;
+    // survivors in increasing vocabulary index: sort (index, rank) ascending
+    const uint64_t key2 = keep ? (((uint64_t)key_index(top) << 32) | (uint64_t)lane) : ~0ull;
+    const uint64_t asc = ~wave_sort_desc(~key2, lane);
+    const int src = (int)(uint32_t)asc;
+    const bool live = asc != ~0ull;
+    law.n = __popcll(__ballot(keep));
+    law.idx = live ? (uint32_t)(asc >> 32) : 0u;
+    const double Ps = __shfl(P, live ? src : 0);
+    law.w = live ? Ps : 0.0;
+    return law;
+}
+
+// Inverse-CDF draw over weights held one per lane in increasing vocabulary
+// index: the first lane whose running sum exceeds u times the total, else the
+// last lane with positive weight, else lane 0.
+__device__ __forceinline__ int lane_inverse_cdf(double w, double u, int lane) {
+    const double Z = wave_sum_d(w);
+    const double inc = wave_incl_scan_d(w, lane);
+    const unsigned long long hit = __ballot(w > 0.0 && inc > u * Z);
+    if (hit) return wave_first(hit);
+    const unsigned long long pos = __ballot(w > 0.0);
+    return pos ? 63 - __clzll((long long)pos) : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace records
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint64_t *seg_keys(const StepArgs &a, int row, int seg) {
+    return a.tws.keys + ((size_t)row * a.St + seg) * kWave;
+}
+// survivors of verify row `slot` (0..2L-1) of sequence c: (index, weight) pairs
+__device__ __forceinline__ uint64_t *row_list(const StepArgs &a, int c, int slot) {
+    return a.tws.lists + ((size_t)c * 2 * a.L + slot) * kWave * 2;
+}
+
+__device__ __forceinline__ double ld_f64(const uint64_t *p) {
+    return __longlong_as_double((long long)ld64(p));
+}
+__device__ __forceinline__ void st_f64(uint64_t *p, double v) {
+    st64(p, (uint64_t)__double_as_longlong(v));
+}
+
+// Counts one arrival of a single wavefront on `counter` (total arrivals
+// `total`) after its own record stores; returns, to every lane, whether it was
+// the last.  The last one resets the counter for the next launch.
+__device__ __forceinline__ bool arrive_wave(uint32_t *counter, uint32_t total, int lane) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    int last = 0;
+    if (lane == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = prev + 1 == total;
+        if (last) st32(counter, 0u);
+    }
+    last = __shfl(last, 0);
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return last != 0;
+}
+
+// ---------------------------------------------------------------------------
+// Decision of one sequence (wavefront 0 of the item completing its rows)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void trunc_decide(const StepArgs &a, int c, int lane) {
+    const int L = a.L;
+    const bool valid = lane < L;
+    const int kk = valid ? lane : 0;
+    const int xk = valid ? a.x[c * L + kk] : 0;
+    const bool bad = valid && (xk < 0 || xk >= a.V);
+    if (bad) atomicOr(&a.ws.ctl->error, kErrBadToken);
+    uint64_t *pxq = a.tws.pxq + (size_t)c * 2 * L;
+    double px = 0.0, qx = 0.0;
+    if (valid) {
+        px = ld_f64(&pxq[kk]);
+        qx = a.q_onehot ? (bad ? 0.0 : 1.0) : ld_f64(&pxq[L + kk]);
+        st64(&pxq[kk], 0);
+        if (!a.q_onehot) st64(&pxq[L + kk], 0);
+    }
+    // min(1, P'(x)/Q'(x)); Q'(x) = 0 gives 1 if P'(x) > 0, else 0.  The accept
+    // test may use the relaxed ratio; alpha stays the plain rate.
+    const double r = qx > 0.0 ? fmin(1.0, px / qx) : (px > 0.0 ? 1.0 : 0.0);
+    const double ra = a.relax1p == 1.0
+                          ? r
+                          : (qx > 0.0 ? fmin(1.0, (a.relax1p * px) / qx) : (px > 0.0 ? 1.0 : 0.0));
+    const bool accepted = !valid || (a.ua == nullptr || (double)a.ua[c * L + kk] < ra);
+    const unsigned long long rej = __ballot(!accepted);
+    const int j = rej ? wave_first(rej) : L;
+    const float alpha = (float)(wave_sum_d(valid ? r : 0.0) / (double)L);
+    if (valid) {
+        if (a.p_x) a.p_x[c * L + kk] = (float)px;
+        if (a.q_x) a.q_x[c * L + kk] = (float)qx;
+        if (a.verify_outputs && kk != j) a.out_tokens[c * L + kk] = kk < j ? xk : -1;
+    }
+    if (lane == 0 && a.alpha) a.alpha[c] = alpha;
+    if (lane == 0 && a.verify_outputs) {
+        a.accept_len[c] = j;
+        a.n_emitted[c] = j + (j < L ? 1 : 0);
+    }
+
+    if (a.verify_outputs && j < L) {
+        // correction from max(0, P' - Q') over the survivors of p_j (P' if that is empty)
+        const uint64_t *pl = row_list(a, c, j);
+        const uint32_t idx = (uint32_t)ld64(&pl[2 * lane]);
+        const double P = ld_f64(&pl[2 * lane + 1]);
+        double Q = 0.0;
+        const int xj = __shfl(xk, j);
+        if (a.q_onehot) {
+            Q = (int)idx == xj ? 1.0 : 0.0;
+        } else {
+            const uint64_t *ql = row_list(a, c, L + j);
+            const uint32_t qidx = (uint32_t)ld64(&ql[2 * lane]);
+            const double qw = ld_f64(&ql[2 * lane + 1]);
+            for (int t = 0; t < kWave; ++t) {
+                const uint32_t ti = __shfl(qidx, t);
+                const double tw = __shfl(qw, t);
+                if (ti == idx) Q += tw;    // unused slots carry weight 0
+            }
+        }
+        const double R = fmax(P - Q, 0.0);
+        const bool use_p = !(wave_sum_d(R) > 0.0);
+        const double wgt = use_p ? P : R;
+        const float ur = a.ur[c * L + j];
+        int tok;
+        if (a.sampler) {
+            // Gumbel-max: argmax of w / E over the survivors (ties to the lower index)
+            const float e = inv_exp_noise1(idx, (uint32_t)j, __float_as_uint(ur), (uint32_t)c);
+            float bv = 0.0f;
+            int bi = INT_MAX;
+            const float s = (float)wgt * e;
+            if (wgt > 0.0 && s > 0.0) {
+                bv = s;
+                bi = (int)idx;
+            }
+            wave_argmax(bv, bi);
+            tok = bi == INT_MAX ? 0 : bi;
+        } else {
+            const int l = lane_inverse_cdf(wgt, (double)ur, lane);
+            tok = (int)__shfl(idx, l);
+        }
+        if (lane == 0) a.out_tokens[c * L + j] = tok;
+    }
+    // the survivor lists of c are consumed: return them to zero
+    for (int slot = 0; slot < 2 * L; ++slot) {
+        uint64_t *l = row_list(a, c, slot);
+        st64(&l[2 * lane], 0);
+        st64(&l[2 * lane + 1], 0);
+    }
+
+    // batch mean of alpha, by the last sequence to be decided
+    if (a.alpha_mean) {
+        int last = 0;
+        if (lane == 0) {
+            st32(&a.tws.alpha[c], __float_as_uint(alpha));
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_s_waitcnt(0);
+            last = __hip_atomic_fetch_add(&a.ws.ctl->seq_done, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) + 1 == (uint32_t)a.C;
+        }
+        last = __shfl(last, 0);
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            double sum = 0.0;
+            for (int c0 = 0; c0 < a.C; c0 += kWave) {
+                const int cc = c0 + lane;
+                sum += wave_sum_d(cc < a.C ? (double)__uint_as_float(ld32(&a.tws.alpha[cc])) : 0.0);
+            }
+            for (int cc = lane; cc < a.C; cc += kWave) st32(&a.tws.alpha[cc], 0u);
+            if (lane == 0) {
+                a.alpha_mean[0] = (float)(sum / (double)a.C);
+                st32(&a.ws.ctl->seq_done, 0u);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ long long trunc_row_offset(const StepArgs &a, int c, int k) {
+    return (long long)c * a.ldc + (long long)k * a.ld;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void trunc_kernel(StepArgs a) {
+    __shared__ TruncShared<T> sh;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int t = (int)blockIdx.x;
+    const int L = a.L;
+    const int n_v = a.C * a.rows_pq * a.St;
+
+    // which row and segment this item streams
+    int c, slot, seg;
+    bool verify;
+    if (t < n_v) {
+        const int per = a.rows_pq * a.St;
+        c = t / per;
+        const int rem = t - c * per;
+        slot = rem / a.St;       // 0..L-1: p rows; L..2L-1: q rows
+        seg = rem - slot * a.St;
+        verify = true;
+    } else {
+        const int t2 = t - n_v;
+        const int per = L * a.St;
+        c = t2 / per;
+        const int rem = t2 - c * per;
+        slot = 2 * L + rem / a.St;
+        seg = rem % a.St;
+        verify = false;
+    }
+    const int k_row = verify ? (slot < L ? slot : slot - L) : slot - 2 * L;
+    const int rowid = c * 3 * L + slot;
+
+    if (verify && a.vmask && a.vmask[c] == 0) {
+        if (slot == 0 && seg == 0) {
+            for (int kk = threadIdx.x; kk < L; kk += kThreads) {
+                if (a.verify_outputs) a.out_tokens[c * L + kk] = -1;
+                if (a.p_x) a.p_x[c * L + kk] = 0.0f;
+                if (a.q_x) a.q_x[c * L + kk] = 0.0f;
+            }
+            if (threadIdx.x == 0) {
+                if (a.verify_outputs) {
+                    a.accept_len[c] = -1;
+                    a.n_emitted[c] = 0;
+                }
+                if (a.alpha) a.alpha[c] = 0.0f;
+            }
+        }
+        return;
+    }
+    if (!verify && a.pmask && a.pmask[c] == 0) {
+        if (seg == 0 && threadIdx.x == 0) {
+            a.next_tokens[c * L + k_row] = -1;
+            if (a.qnext_x) a.qnext_x[c * L + k_row] = 0.0f;
+        }
+        return;
+    }
+
+    const void *base = verify ? (slot < L ? a.p : a.q) : a.qn;
+    const T *row = static_cast<const T *>(base) + trunc_row_offset(a, c, k_row);
+    const int k = a.top_k;
+
+    // ---- this segment's top k ----
+    const int tb = seg * a.tpst;
+    const int te = min(a.tiles_row, tb + a.tpst);
+    select_segment<T, VEC>(row, tb, te, a.V, k, wave, lane, sh);
+    if (wave == 0 && lane < k) st64(&seg_keys(a, rowid, seg)[lane], sh.lists[0][lane]);
+    if (!arrive(counter(a.tws.row_cnt, rowid), (uint32_t)a.St, &sh.flag)) return;
+    if (wave != 0) return;
+
+    // ---- the row's top k, truncated law ----
+    uint64_t top = 0;
+    {
+        uint64_t rec[kMaxTruncSegments];
+#pragma unroll
+        for (int s = 0; s < kMaxTruncSegments; ++s)
+            rec[s] = (s < a.St && lane < k) ? ld64(&seg_keys(a, rowid, s)[lane]) : 0;
+#pragma unroll
+        for (int s = 0; s < kMaxTruncSegments; ++s)
+            if (s < a.St && lane < k) st64(&seg_keys(a, rowid, s)[lane], 0);
+        top = rec[0];
+#pragma unroll
+        for (int s = 1; s < kMaxTruncSegments; ++s)
+            if (s < a.St) top = wave_merge_desc(top, rec[s], lane);
+    }
+    const RowLaw law = truncated_law(top, k, a.temp, a.top_p, lane);
+    if (law.empty && lane == 0) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
+
+    if (!verify) {
+        const int r = c * L + k_row;
+        const int l = lane_inverse_cdf(law.w, (double)a.up[r], lane);
+        const int tok = (int)__shfl(law.idx, l);
+        const double pw = __shfl(law.w, l);
+        if (lane == 0) {
+            a.next_tokens[r] = tok;
+            if (a.qnext_x) a.qnext_x[r] = (float)pw;
+        }
+        return;
+    }
+
+    // verify row: P'(x_k) or Q'(x_k), and the survivors for a correction
+    const int xk = a.x[c * L + k_row];
+    const unsigned long long hit = __ballot(lane < law.n && (int)law.idx == xk);
+    const double wx = hit ? __shfl(law.w, wave_first(hit)) : 0.0;
+    if (lane == 0) st_f64(&a.tws.pxq[(size_t)c * 2 * L + slot], wx);
+    if (a.verify_outputs) {
+        uint64_t *l = row_list(a, c, slot);
+        st64(&l[2 * lane], lane < law.n ? (uint64_t)law.idx : 0);
+        st_f64(&l[2 * lane + 1], lane < law.n ? law.w : 0.0);
+    }
+    if (!arrive_wave(counter(a.tws.seq_cnt, c), (uint32_t)a.rows_pq, lane)) return;
+    trunc_decide(a, c, lane);
+}
+
+}  // namespace
+
+hipError_t launch_trunc(const StepArgs &a, int dtype, bool vec, hipStream_t stream) {
+    const dim3 grid((unsigned)a.n_items), block(kThreads);
+    if (dtype == kBf16) {
+        if (vec) hipLaunchKernelGGL((trunc_kernel<uint16_t, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((trunc_kernel<uint16_t, false>), grid, block, 0, stream, a);
+    } else {
+        if (vec) hipLaunchKernelGGL((trunc_kernel<float, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((trunc_kernel<float, false>), grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace isd

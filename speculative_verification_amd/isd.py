@@ -37,7 +37,8 @@ class Shape(ctypes.Structure):
                 ("ld", ctypes.c_int64), ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("ldc", ctypes.c_int64),
                 ("relax", ctypes.c_float), ("q_onehot", ctypes.c_int32),
-                ("sampler", ctypes.c_int32)]
+                ("sampler", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("top_p", ctypes.c_float)]
 
 
 _vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
@@ -56,6 +57,7 @@ _SIGS = {
     "isd_lm_head_pack": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "isd_check_device_error": (ctypes.c_int, [_vp, _sz, _vp]),
     "isd_set_tuning": (ctypes.c_int, [_i32, _i32, _i32, _i64]),
+    "isd_set_trunc_tuning": (ctypes.c_int, [_i32]),
     "isd_last_error": (ctypes.c_char_p, []),
 }
 
@@ -125,10 +127,14 @@ def _sampler_code(sampler) -> int:
 
 
 def make_shape(logits: torch.Tensor, mode: int = MODE_SAMPLE, temperature: float = 1.0,
-               relax: float = 0.0, q_onehot: bool = False, sampler="cdf") -> Shape:
+               relax: float = 0.0, q_onehot: bool = False, sampler="cdf", top_k: int = 0,
+               top_p: float = 1.0) -> Shape:
+    """Shape of a call on `logits` [C, L, V]; top_k = 0 and top_p >= 1 mean no
+    truncation."""
     C, L, V, ld, ldc, code = _logits_layout(logits)
+    tp = 0.0 if top_p >= 1.0 else float(top_p)
     return Shape(C, L, V, ld, code, mode, float(temperature), ldc, float(relax),
-                 int(bool(q_onehot)), _sampler_code(sampler))
+                 int(bool(q_onehot)), _sampler_code(sampler), int(top_k), tp)
 
 
 def _same_layout(ref: Shape, t, name: str, mode: int, temperature: float):
@@ -178,11 +184,11 @@ def _out(out, key, shape, dtype, device):
 
 
 def verify_step(p, q, x, ua, ur, *, mode="sample", temperature=1.0, relax=0.0, q_onehot=False,
-                sampler="cdf", out=None, ws=None):
+                sampler="cdf", top_k=0, top_p=1.0, out=None, ws=None):
     """Verify proposals x [C, L] against anchor rows p (and proposal rows q;
     None with q_onehot)."""
     m = _mode_code(mode)
-    shape = make_shape(p, m, temperature, relax, q_onehot, sampler)
+    shape = make_shape(p, m, temperature, relax, q_onehot, sampler, top_k, top_p)
     if m == MODE_SAMPLE:
         _same_layout(shape, q, "q", m, temperature)
     C, L, dev = shape.C, shape.L, p.device
@@ -200,10 +206,10 @@ def verify_step(p, q, x, ua, ur, *, mode="sample", temperature=1.0, relax=0.0, q
     return o
 
 
-def propose(qn, up, *, mode="sample", temperature=1.0, out=None, ws=None):
+def propose(qn, up, *, mode="sample", temperature=1.0, top_k=0, top_p=1.0, out=None, ws=None):
     """Draw the next proposals [C, L] from the mask-position rows qn."""
     m = _mode_code(mode)
-    shape = make_shape(qn, m, temperature)
+    shape = make_shape(qn, m, temperature, top_k=top_k, top_p=top_p)
     C, L, dev = shape.C, shape.L, qn.device
     o = dict(next_tokens=_out(out, "next_tokens", (C, L), torch.int32, dev),
              qnext_x=_out(out, "qnext_x", (C, L), torch.float32, dev))
@@ -213,10 +219,11 @@ def propose(qn, up, *, mode="sample", temperature=1.0, out=None, ws=None):
     return o
 
 
-def alpha(p, q, x, *, mode="sample", temperature=1.0, q_onehot=False, out=None, ws=None):
+def alpha(p, q, x, *, mode="sample", temperature=1.0, q_onehot=False, top_k=0, top_p=1.0,
+          out=None, ws=None):
     """Introspective acceptance rate per sequence and its batch mean."""
     m = _mode_code(mode)
-    shape = make_shape(p, m, temperature, 0.0, q_onehot)
+    shape = make_shape(p, m, temperature, 0.0, q_onehot, top_k=top_k, top_p=top_p)
     if m == MODE_SAMPLE:
         _same_layout(shape, q, "q", m, temperature)
     dev = p.device
@@ -233,9 +240,9 @@ class StepCall:
     timing loop pays one ctypes call per step."""
 
     def __init__(self, p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, relax=0.0,
-                 q_onehot=False, sampler="cdf", out=None, ws=None):
+                 q_onehot=False, sampler="cdf", top_k=0, top_p=1.0, out=None, ws=None):
         m = _mode_code(mode)
-        self.shape = make_shape(p, m, temperature, relax, q_onehot, sampler)
+        self.shape = make_shape(p, m, temperature, relax, q_onehot, sampler, top_k, top_p)
         _same_layout(self.shape, qn, "qn", m, temperature)
         if m == MODE_SAMPLE:
             _same_layout(self.shape, q, "q", m, temperature)
@@ -268,17 +275,19 @@ class StepCall:
 
 
 def step(p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, relax=0.0, q_onehot=False,
-         sampler="cdf", out=None, ws=None):
+         sampler="cdf", top_k=0, top_p=1.0, out=None, ws=None):
     """One fused ISD step (verify + propose in one launch)."""
     return StepCall(p, q, x, ua, ur, qn, up, mode=mode, temperature=temperature, relax=relax,
-                    q_onehot=q_onehot, sampler=sampler, out=out, ws=ws)()
+                    q_onehot=q_onehot, sampler=sampler, top_k=top_k, top_p=top_p, out=out,
+                    ws=ws)()
 
 
 def step_masked(p, q, x, ua, ur, qn, up, verify_mask=None, propose_mask=None, *, mode="sample",
-                temperature=1.0, relax=0.0, q_onehot=False, sampler="cdf", out=None, ws=None):
+                temperature=1.0, relax=0.0, q_onehot=False, sampler="cdf", top_k=0, top_p=1.0,
+                out=None, ws=None):
     """isd_step with per-sequence verify / propose masks (int32 [C]; None = all)."""
     m = _mode_code(mode)
-    shape = make_shape(p, m, temperature, relax, q_onehot, sampler)
+    shape = make_shape(p, m, temperature, relax, q_onehot, sampler, top_k, top_p)
     _same_layout(shape, qn, "qn", m, temperature)
     if m == MODE_SAMPLE:
         _same_layout(shape, q, "q", m, temperature)
@@ -300,10 +309,11 @@ def step_masked(p, q, x, ua, ur, qn, up, verify_mask=None, propose_mask=None, *,
     return o
 
 
-def propose_masked(rows, u, mask=None, *, mode="sample", temperature=1.0, out=None, ws=None):
+def propose_masked(rows, u, mask=None, *, mode="sample", temperature=1.0, top_k=0, top_p=1.0,
+                   out=None, ws=None):
     """isd_propose with a per-sequence mask (int32 [C]; None = all)."""
     m = _mode_code(mode)
-    shape = make_shape(rows, m, temperature)
+    shape = make_shape(rows, m, temperature, top_k=top_k, top_p=top_p)
     C, L, dev = shape.C, shape.L, rows.device
     o = dict(next_tokens=_out(out, "next_tokens", (C, L), torch.int32, dev),
              qnext_x=_out(out, "qnext_x", (C, L), torch.float32, dev))
@@ -420,3 +430,8 @@ def set_tuning(segments: int = 0, resid_segments: int = 0, spin_limit: int = 0,
                propose_segments: int = 0):
     """Process-wide decomposition knobs (0 = automatic)."""
     _check(lib().isd_set_tuning(segments, propose_segments, resid_segments, spin_limit))
+
+
+def set_trunc_tuning(segments: int = 0):
+    """Workgroups per row of the truncated (top-k) path (0 = automatic)."""
+    _check(lib().isd_set_trunc_tuning(segments))

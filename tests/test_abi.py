@@ -204,7 +204,20 @@ def test_variant_shape_validation(isd):
         bad = _shape(isd)
         bad.sampler = v
         assert _verify(isd, bad) == 1 and "sampler" in lib.isd_last_error().decode()
+    # truncation: top_k in [0, 64]; top_p needs top_k; 0 or >= 1 turns top_p off
+    for k, p_, status, word in ((65, 0.0, 2, "top_k"), (-1, 0.0, 1, "top_k"), (0, 0.9, 2, "top_p"),
+                                (8, -0.5, 1, "top_p"), (8, float("nan"), 1, "top_p")):
+        bad = _shape(isd)
+        bad.top_k, bad.top_p = k, p_
+        assert _verify(isd, bad) == status and word in lib.isd_last_error().decode(), (k, p_)
+    plain = _shape(isd)
+    trunc = _shape(isd)
+    trunc.top_k, trunc.top_p = 50, 0.95
+    assert lib.isd_workspace_bytes(ctypes.byref(trunc)) > lib.isd_workspace_bytes(ctypes.byref(plain))
+    assert lib.isd_set_trunc_tuning(9) == 1 and lib.isd_set_trunc_tuning(0) == 0
     import torch
+    s = isd.make_shape(torch.zeros(1, 1, 8), top_k=50, top_p=1.0)
+    assert (s.top_k, s.top_p) == (50, 0.0)
     assert isd.make_shape(torch.zeros(1, 1, 8), sampler="gumbel").sampler == 1
     with pytest.raises(ValueError):
         isd.make_shape(torch.zeros(1, 1, 8), sampler="topk")

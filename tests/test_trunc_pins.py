@@ -133,8 +133,8 @@ def test_truncated_verification_emits_truncated_anchor_law(top_k, top_p):
     V = 6
     zp, Pt = _trunc_rows(rng, 1, V, top_k=top_k, top_p=top_p)
     zq, Qt = _trunc_rows(rng, 1, V, top_k=top_k, top_p=top_p)
-    # the helper converts probability rows to logits; pass the truncated laws'
-    # logits straight to the oracle, with truncation on (idempotent on them)
+    # the helper takes probability rows (it passes their logarithms to the
+    # oracle); give it the untruncated softmax rows and let the oracle truncate
     law = _emitted_law(np.exp(zp - zp.max()) / np.exp(zp - zp.max()).sum(),
                        np.exp(zq - zq.max()) / np.exp(zq - zq.max()).sum(), Qt, 0,
                        top_k=top_k, top_p=top_p)
