@@ -425,3 +425,23 @@ def propose_greedy(qn):
 def lm_head(h, w):
     """logits = h @ w in float64 on exactly decoded inputs."""
     return np.asarray(h, dtype=np.float64) @ np.asarray(w, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Segment-gated LoRA projection
+# ---------------------------------------------------------------------------
+
+def lora_gemm(x, w, a, b, mask):
+    """h_j = W x_j + [j is a mask position] * B A x_j ("Introspective Diffusion
+    Language Models | Summary", appendix G; section 3.2: the adapter acts only
+    at mask positions, clean and introspection positions keep the base
+    weights), in float64 on exactly decoded inputs.
+
+    x [M, K]; w [N, K]; a [r, K]; b [N, r] (output features first); mask [M]
+    (nonzero = mask position).  Returns h [M, N].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    base = x @ np.asarray(w, dtype=np.float64).T
+    t = x @ np.asarray(a, dtype=np.float64).T
+    gate = (np.asarray(mask) != 0).astype(np.float64)[:, None]
+    return base + gate * (t @ np.asarray(b, dtype=np.float64).T)
