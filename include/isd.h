@@ -295,6 +295,32 @@ isd_status_t isd_check_device_error(void *workspace, size_t ws_bytes, void *stre
 isd_status_t isd_set_tuning(int32_t segments, int32_t propose_segments, int32_t resid_segments,
                             int64_t spin_limit);
 
+/* Segment-gated LoRA projection of the residual ISD variant (appendix G;
+ * section 3.2): h_j = W x_j + [mask_j != 0] B A x_j.  The adapter acts only at
+ * mask positions, so clean and introspection rows keep the base weights and
+ * the causal anchor stays the base model's.  Everything is bf16 bit patterns,
+ * row-major, output features first (the torch Linear layout):
+ *   x     [M, K]       inputs, 16-byte aligned
+ *   a     [r, K]       adapter down-projection A, 16-byte aligned
+ *   wcat  [N, K + r]   (W | B) from isd_lora_pack, 16-byte aligned
+ *   mask  [M] int32    nonzero at mask positions; NULL: every row
+ *   t     [M, r]       written: the gated adapter activations gate * A x
+ *                      (bf16, zero on clean rows); caller-owned scratch,
+ *                      16-byte aligned
+ *   out   [M, N]       written: h, fp32 accumulation rounded to bf16
+ * K and r must be multiples of 64.  Two launches on `stream` (the shrink,
+ * then one GEMM over the concatenated K); no host synchronisation, no
+ * allocation, so the call can be captured in a graph.  Errors: ISD_ERR_ARG
+ * for bad sizes or pointers, ISD_ERR_DEVICE if a launch fails. */
+isd_status_t isd_lora_gemm(const void *x, const void *a, const void *wcat, const int32_t *mask,
+                           int32_t M, int32_t K, int32_t N, int32_t r, void *t, void *out,
+                           void *stream);
+
+/* wcat [N, K + r] = (W [N, K] | B [N, r]), row by row (two 2-D device copies on
+ * `stream`, done once per adapter).  All bf16, 2-byte aligned. */
+isd_status_t isd_lora_pack(const void *w, const void *b, int32_t N, int32_t K, int32_t r,
+                           void *wcat, void *stream);
+
 /* Tuning knob of the truncated (top-k) path, process-wide: workgroups sharing
  * one row (1..8); 0 restores the automatic choice. */
 isd_status_t isd_set_trunc_tuning(int32_t segments);

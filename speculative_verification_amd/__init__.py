@@ -23,6 +23,8 @@ from .isd import (  # noqa: F401
     lm_head,
     lm_head_pack,
     lm_head_packed,
+    lora_gemm,
+    lora_pack,
     make_shape,
     propose,
     propose_masked,

@@ -570,6 +570,43 @@ isd_status_t isd_set_tuning(int32_t segments, int32_t propose_segments, int32_t 
     return ISD_OK;
 }
 
+isd_status_t isd_lora_pack(const void *w, const void *b, int32_t N, int32_t K, int32_t r,
+                           void *wcat, void *stream) {
+    ISD_TRY(check_ptr(w, "w", 2));
+    ISD_TRY(check_ptr(b, "b", 2));
+    ISD_TRY(check_ptr(wcat, "wcat", 2));
+    if (N < 1 || K < 1 || r < 1) return fail(ISD_ERR_ARG, "N, K, r must be >= 1");
+    const size_t pitch = (size_t)(K + r) * 2;
+    hipError_t e = hipMemcpy2DAsync(wcat, pitch, w, (size_t)K * 2, (size_t)K * 2, (size_t)N,
+                                    hipMemcpyDeviceToDevice, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = hipMemcpy2DAsync(static_cast<char *>(wcat) + (size_t)K * 2, pitch, b, (size_t)r * 2,
+                             (size_t)r * 2, (size_t)N, hipMemcpyDeviceToDevice,
+                             (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "lora pack copy failed: %s", hipGetErrorString(e));
+    return ISD_OK;
+}
+
+isd_status_t isd_lora_gemm(const void *x, const void *a, const void *wcat, const int32_t *mask,
+                           int32_t M, int32_t K, int32_t N, int32_t r, void *t, void *out,
+                           void *stream) {
+    ISD_TRY(check_ptr(x, "x", 16));
+    ISD_TRY(check_ptr(a, "a", 16));
+    ISD_TRY(check_ptr(wcat, "wcat", 16));
+    ISD_TRY(check_ptr(t, "t", 16));
+    ISD_TRY(check_ptr(out, "out", 2));
+    if (mask) ISD_TRY(check_ptr(mask, "mask", 4));
+    if (M < 1 || N < 1 || K < 1 || r < 1) return fail(ISD_ERR_ARG, "M, K, N, r must be >= 1");
+    if (K % 64) return fail(ISD_ERR_ARG, "K must be a multiple of 64 (got %d)", (int)K);
+    if (r % 64) return fail(ISD_ERR_ARG, "r must be a multiple of 64 (got %d)", (int)r);
+    const hipError_t e = launch_lora_gemm(
+        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(a),
+        static_cast<const uint16_t *>(wcat), mask, M, K, N, r, static_cast<uint16_t *>(t),
+        static_cast<uint16_t *>(out), (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "lora launch failed: %s", hipGetErrorString(e));
+    return ISD_OK;
+}
+
 isd_status_t isd_set_trunc_tuning(int32_t segments) {
     if (segments < 0 || segments > kMaxTruncSegments)
         return fail(ISD_ERR_ARG, "segments must be in [0, %d]", kMaxTruncSegments);

@@ -172,6 +172,12 @@ hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, i
                                  uint16_t *out, hipStream_t stream);
 hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStream_t stream);
 
+// Segment-gated LoRA projection: t = gate * (x a^T), then out = (x | t) wcat^T
+// with wcat = (w | b) [N, K + r].
+hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t *wcat,
+                            const int32_t *mask, int M, int K, int N, int r, uint16_t *t,
+                            uint16_t *out, hipStream_t stream);
+
 // LM-head GEMM (bf16 in, fp32 accumulate, bf16 out).
 hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, int N,
                           uint16_t *out, hipStream_t stream);

@@ -167,9 +167,13 @@ constexpr int kPVecRow = kPBK / 8;                          // 16-byte vectors p
 constexpr int kPAPerThread = kPBM * kPVecRow / kThreadsG;   // 8
 constexpr int kPBPerThread = kPBN * kPVecRow / kThreadsG;   // 4
 
+// The A operand may come in two K segments: columns [0, K1) from h [M, K1]
+// and [K1, K1 + K2) from h2 [M, K2] (K2 = 0: none); wt is [N, K1 + K2].  Both
+// K1 and K2 are multiples of 64, so a K step never straddles the two.
 __global__ __launch_bounds__(256, 2) void lm_head_packed_kernel(
-    const uint16_t *__restrict__ h, const uint16_t *__restrict__ wt, int M, int K, int N,
-    uint16_t *__restrict__ out, int m_tiles, int total, int per_xcd) {
+    const uint16_t *__restrict__ h, int K1, const uint16_t *__restrict__ h2, int K2,
+    const uint16_t *__restrict__ wt, int M, int N, uint16_t *__restrict__ out, int m_tiles,
+    int total, int per_xcd) {
     __shared__ __attribute__((aligned(16))) uint16_t As[kPBM * kPLd];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[kPBN * kPLd];
 
@@ -184,13 +188,18 @@ __global__ __launch_bounds__(256, 2) void lm_head_packed_kernel(
     const int wm = wave / 2, wn = wave % 2;
 
     // thread tid moves the 16-byte vectors tid, tid + 256, ... of each tile
+    const int K = K1 + K2;
     uint4 ra[kPAPerThread], rb[kPBPerThread];
     auto load_step = [&](int k0) {
+        const bool first = k0 < K1;
+        const uint16_t *src = first ? h : h2;
+        const int lda = first ? K1 : K2;
+        const int ka = first ? k0 : k0 - K1;
 #pragma unroll
         for (int r = 0; r < kPAPerThread; ++r) {
             const int v = tid + kThreadsG * r;
-            const int row = m0 + v / kPVecRow, kk = k0 + (v % kPVecRow) * 8;
-            ra[r] = row < M ? *reinterpret_cast<const uint4 *>(h + (size_t)row * K + kk)
+            const int row = m0 + v / kPVecRow, kk = ka + (v % kPVecRow) * 8;
+            ra[r] = row < M ? *reinterpret_cast<const uint4 *>(src + (size_t)row * lda + kk)
                             : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
@@ -263,6 +272,73 @@ __global__ __launch_bounds__(256, 2) void lm_head_packed_kernel(
         }
 }
 
+// ---------------------------------------------------------------------------
+// Segment-gated LoRA shrink: t[M, r] = gate_j * (x_j A^T), bf16
+// ---------------------------------------------------------------------------
+//
+// The adapter acts only at mask positions ("Introspective Diffusion Language
+// Models | Summary", appendix G), so t is zero on the other rows; the expand
+// B t then rides on the base projection as a second K segment (x | t) times
+// (W | B)^T.  The shrink is small (r columns), so a workgroup owns 32 rows x
+// 64 adapter channels and its four wavefronts split K four ways, reading both
+// operands straight from global memory as the 8-element k-runs the MFMA
+// takes; the four partial tiles are summed through LDS.
+
+constexpr int kSRows = 32, kSCols = 64;
+
+__global__ __launch_bounds__(256) void lora_shrink_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ a,
+                                                          const int32_t *__restrict__ mask, int M,
+                                                          int K, int r, uint16_t *__restrict__ t) {
+    __shared__ float part[kWavesPerGroup - 1][2][16][kWave];
+    const int m0 = blockIdx.x * kSRows, n0 = blockIdx.y * kSCols;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int kq = K / kWavesPerGroup;                  // multiple of 16
+    const int kb = wave * kq;
+    const int row = m0 + lane % 32;
+    const bool live = row < M;
+    const uint16_t *xr = x + (size_t)(live ? row : 0) * K + 8 * (lane / 32);
+    const uint16_t *ar0 = a + (size_t)(n0 + lane % 32) * K + 8 * (lane / 32);
+    const uint16_t *ar1 = ar0 + (size_t)32 * K;
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
+#pragma unroll 4
+    for (int k = kb; k < kb + kq; k += 16) {
+        bf16x8 xa = *reinterpret_cast<const bf16x8 *>(xr + k);
+        const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(ar0 + k);
+        const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(ar1 + k);
+        if (!live) xa = bf16x8{};
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, b0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, b1, acc1, 0, 0, 0);
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            part[wave - 1][0][i][lane] = acc0[i];
+            part[wave - 1][1][i][lane] = acc1[i];
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup - 1; ++w)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc0[i] += part[w][0][i][lane];
+            acc1[i] += part[w][1][i][lane];
+        }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int rr = m0 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+        if (rr >= M) continue;
+        const bool gate = mask == nullptr || mask[rr] != 0;
+        const int col = n0 + lane % 32;
+        t[(size_t)rr * r + col] = gate ? bf16_rne(acc0[i]) : (uint16_t)0;
+        t[(size_t)rr * r + col + 32] = gate ? bf16_rne(acc1[i]) : (uint16_t)0;
+    }
+}
+
 // wt[N, K] = w[K, N]^T through 64 x 64 LDS tiles (bit copies).
 __global__ __launch_bounds__(256) void pack_wt_kernel(const uint16_t *__restrict__ w,
                                                       uint16_t *__restrict__ wt, int K, int N) {
@@ -303,7 +379,24 @@ hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, i
     if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
     const int per_xcd = (int)((total + kXcds - 1) / kXcds);
     hipLaunchKernelGGL(lm_head_packed_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0,
-                       stream, h, wt, M, K, N, out, m_tiles, (int)total, per_xcd);
+                       stream, h, K, nullptr, 0, wt, M, N, out, m_tiles, (int)total, per_xcd);
+    return hipGetLastError();
+}
+
+hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t *wcat,
+                            const int32_t *mask, int M, int K, int N, int r, uint16_t *t,
+                            uint16_t *out, hipStream_t stream) {
+    const dim3 sgrid((unsigned)((M + kSRows - 1) / kSRows), (unsigned)(r / kSCols));
+    hipLaunchKernelGGL(lora_shrink_kernel, sgrid, dim3(256), 0, stream, x, a, mask, M, K, r, t);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int m_tiles = (M + kPBM - 1) / kPBM;
+    const int n_tiles = (N + kPBN - 1) / kPBN;
+    const long long total = (long long)m_tiles * n_tiles;
+    if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
+    const int per_xcd = (int)((total + kXcds - 1) / kXcds);
+    hipLaunchKernelGGL(lm_head_packed_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0,
+                       stream, x, K, t, r, wcat, M, N, out, m_tiles, (int)total, per_xcd);
     return hipGetLastError();
 }
 

@@ -58,6 +58,8 @@ _SIGS = {
     "isd_check_device_error": (ctypes.c_int, [_vp, _sz, _vp]),
     "isd_set_tuning": (ctypes.c_int, [_i32, _i32, _i32, _i64]),
     "isd_set_trunc_tuning": (ctypes.c_int, [_i32]),
+    "isd_lora_pack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "isd_lora_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "isd_last_error": (ctypes.c_char_p, []),
 }
 
@@ -435,3 +437,36 @@ def set_tuning(segments: int = 0, resid_segments: int = 0, spin_limit: int = 0,
 def set_trunc_tuning(segments: int = 0):
     """Workgroups per row of the truncated (top-k) path (0 = automatic)."""
     _check(lib().isd_set_trunc_tuning(segments))
+
+
+def lora_pack(w: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """(W [N, K] | B [N, r]) as one bf16 tensor [N, K + r] for lora_gemm."""
+    if w.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise ValueError("w and b must be bf16")
+    N, K = w.shape
+    r = b.shape[1]
+    if b.shape[0] != N or not (w.is_contiguous() and b.is_contiguous()):
+        raise ValueError("w [N, K] and b [N, r] must be contiguous with the same N")
+    wcat = torch.empty((N, K + r), dtype=torch.bfloat16, device=w.device)
+    _check(lib().isd_lora_pack(_ptr(w), _ptr(b), N, K, r, _ptr(wcat), _stream()))
+    return wcat
+
+
+def lora_gemm(x: torch.Tensor, a: torch.Tensor, wcat: torch.Tensor, mask=None, *, out=None,
+              t=None):
+    """h = x W^T + [mask] (x A^T) B^T with wcat = lora_pack(W, B); returns (h, t)."""
+    for name, v in (("x", x), ("a", a), ("wcat", wcat)):
+        if v.dtype != torch.bfloat16 or not v.is_contiguous():
+            raise ValueError(f"{name} must be contiguous bf16")
+    M, K = x.shape
+    r = a.shape[0]
+    N = wcat.shape[0]
+    if a.shape[1] != K or wcat.shape[1] != K + r:
+        raise ValueError("shapes must be x [M, K], a [r, K], wcat [N, K + r]")
+    if mask is not None and (mask.dtype != torch.int32 or mask.numel() != M):
+        raise ValueError("mask must be int32 [M]")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    t = torch.empty((M, r), dtype=torch.bfloat16, device=x.device) if t is None else t
+    _check(lib().isd_lora_gemm(_ptr(x), _ptr(a), _ptr(wcat), _ptr(mask), M, K, N, r, _ptr(t),
+                               _ptr(out), _stream()))
+    return out, t
