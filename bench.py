@@ -54,7 +54,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6],
+                    help="2 serving step, 3 greedy step, 4 LM head + step, 5 high concurrency, "
+                         "6 segment-gated LoRA projection")
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -240,6 +242,64 @@ def lm_head_workload(args):
         accept_len_mean_last=round(acc, 3))), flush=True)
 
 
+def lora_workload(args):
+    """Segment-gated LoRA projection of the residual ISD variant: per step,
+    h = x W^T + [mask] (x A^T) B^T for the MLP gate/up projection of an 8B
+    model at the serving batch (M = 64 sequences x 16 extend rows, K = 4096,
+    N = 24576, rank 128, adapter on the 8 mask rows of each sequence).  The
+    base projection alone is timed beside it."""
+    import torch
+
+    import speculative_verification_amd as isd
+    from isd_inputs import LORA_CONFIGS, gen_lora
+
+    cfg = LORA_CONFIGS["mlp_up"]
+    dev = torch.device("cuda", 0)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    d = gen_lora(cfg, 0)
+    x, a, w, b = bf16(d["x"]), bf16(d["a"]), bf16(d["w"]), bf16(d["b"])
+    mask = torch.from_numpy(d["mask"]).to(dev)
+    wcat = isd.lora_pack(w, b)    # once per adapter (untimed)
+    M, K = x.shape
+    N, r = w.shape[0], a.shape[0]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t0) * 1e3 / args.steps
+
+    base_ms, _ = timed(lambda: isd.lm_head_packed(x, w, out=out))
+    lora_ms, wall_ms = timed(lambda: isd.lora_gemm(x, a, wcat, mask, out=out, t=t))
+    gated = int((d["mask"] != 0).sum())
+    flops = 2.0 * M * K * N + 2.0 * gated * r * (K + N)
+    tflops = flops / (lora_ms * 1e-3) / 1e12
+    print(json.dumps(dict(
+        metric="segment-gated LoRA projection TFLOP/s (h = W x + [mask] B A x)",
+        value=round(tflops, 1), unit="TFLOP/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(wall_ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload=f"gated LoRA projection: x [{M}, {K}], W [{N}, {K}], rank {r}, "
+                             f"adapter on {gated} mask rows", M=M, K=K, N=N, r=r),
+        roofline=dict(bound="mfma", achieved=round(tflops, 1), peak=2500.0, unit="TFLOP/s",
+                      frac=round(tflops / 2500.0, 4), traffic=None),
+        kernel_us_avg=round(lora_ms * 1e3, 2), base_projection_us=round(base_ms * 1e3, 2),
+        adapter_overhead=round(lora_ms / base_ms - 1.0, 4))), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -247,6 +307,9 @@ def main():
         return
     if args.config == 4:
         lm_head_workload(args)
+        return
+    if args.config == 6:
+        lora_workload(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
