@@ -279,63 +279,64 @@ __global__ __launch_bounds__(256, 2) void lm_head_packed_kernel(
 // The adapter acts only at mask positions ("Introspective Diffusion Language
 // Models | Summary", appendix G), so t is zero on the other rows; the expand
 // B t then rides on the base projection as a second K segment (x | t) times
-// (W | B)^T.  The shrink is small (r columns), so a workgroup owns 32 rows x
-// 64 adapter channels and its four wavefronts split K four ways, reading both
-// operands straight from global memory as the 8-element k-runs the MFMA
-// takes; the four partial tiles are summed through LDS.
+// (W | B)^T.  The shrink has only r columns, so what bounds it is the length
+// of each wavefront's K loop, not the MFMA rate: a workgroup of sixteen
+// wavefronts owns 32 rows x 32 adapter channels, the wavefronts take every
+// sixteenth 16-wide K step each (reading both operands straight from global
+// memory as the 8-element k-runs the MFMA takes), and wavefront 0 sums the
+// sixteen partial tiles through LDS in a fixed order.
 
-constexpr int kSRows = 32, kSCols = 64;
+constexpr int kSRows = 32, kSCols = 32, kSWaves = 16;
 
-__global__ __launch_bounds__(256) void lora_shrink_kernel(const uint16_t *__restrict__ x,
-                                                          const uint16_t *__restrict__ a,
-                                                          const int32_t *__restrict__ mask, int M,
-                                                          int K, int r, uint16_t *__restrict__ t) {
-    __shared__ float part[kWavesPerGroup - 1][2][16][kWave];
+__global__ __launch_bounds__(kSWaves * 64) void lora_shrink_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ a,
+    const int32_t *__restrict__ mask, int M, int K, int r, uint16_t *__restrict__ t) {
+    __shared__ float part[kSWaves - 1][16][64];
     const int m0 = blockIdx.x * kSRows, n0 = blockIdx.y * kSCols;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int kq = K / kWavesPerGroup;                  // multiple of 16
-    const int kb = wave * kq;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int row = m0 + lane % 32;
-    const bool live = row < M;
-    const uint16_t *xr = x + (size_t)(live ? row : 0) * K + 8 * (lane / 32);
-    const uint16_t *ar0 = a + (size_t)(n0 + lane % 32) * K + 8 * (lane / 32);
-    const uint16_t *ar1 = ar0 + (size_t)32 * K;
-    f32x16 acc0, acc1;
+    const uint16_t *xr = x + (size_t)(row < M ? row : 0) * K + 8 * (lane / 32);
+    const uint16_t *ar = a + (size_t)(n0 + lane % 32) * K + 8 * (lane / 32);
+    f32x16 acc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
-#pragma unroll 4
-    for (int k = kb; k < kb + kq; k += 16) {
-        bf16x8 xa = *reinterpret_cast<const bf16x8 *>(xr + k);
-        const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(ar0 + k);
-        const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(ar1 + k);
-        if (!live) xa = bf16x8{};
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, b0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, b1, acc1, 0, 0, 0);
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    // rows past M read row 0 and are never stored; the K steps of this
+    // wavefront are loaded eight at a time so that their loads overlap
+    constexpr int kBatch = 8;
+    const int stride = 16 * kSWaves;
+    for (int k0 = 16 * wave; k0 < K; k0 += kBatch * stride) {
+        bf16x8 xa[kBatch], av[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int k = k0 + b * stride;
+            if (k < K) {
+                xa[b] = *reinterpret_cast<const bf16x8 *>(xr + k);
+                av[b] = *reinterpret_cast<const bf16x8 *>(ar + k);
+            } else {
+                xa[b] = bf16x8{};
+                av[b] = bf16x8{};
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[b], av[b], acc, 0, 0, 0);
     }
     if (wave > 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            part[wave - 1][0][i][lane] = acc0[i];
-            part[wave - 1][1][i][lane] = acc1[i];
-        }
+        for (int i = 0; i < 16; ++i) part[wave - 1][i][lane] = acc[i];
     }
     __syncthreads();
     if (wave != 0) return;
+#pragma unroll 1
+    for (int w = 0; w < kSWaves - 1; ++w)
 #pragma unroll
-    for (int w = 0; w < kWavesPerGroup - 1; ++w)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            acc0[i] += part[w][0][i][lane];
-            acc1[i] += part[w][1][i][lane];
-        }
+        for (int i = 0; i < 16; ++i) acc[i] += part[w][i][lane];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int rr = m0 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
         if (rr >= M) continue;
         const bool gate = mask == nullptr || mask[rr] != 0;
-        const int col = n0 + lane % 32;
-        t[(size_t)rr * r + col] = gate ? bf16_rne(acc0[i]) : (uint16_t)0;
-        t[(size_t)rr * r + col + 32] = gate ? bf16_rne(acc1[i]) : (uint16_t)0;
+        t[(size_t)rr * r + n0 + lane % 32] = gate ? bf16_rne(acc[i]) : (uint16_t)0;
     }
 }
 
@@ -387,7 +388,8 @@ hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t
                             const int32_t *mask, int M, int K, int N, int r, uint16_t *t,
                             uint16_t *out, hipStream_t stream) {
     const dim3 sgrid((unsigned)((M + kSRows - 1) / kSRows), (unsigned)(r / kSCols));
-    hipLaunchKernelGGL(lora_shrink_kernel, sgrid, dim3(256), 0, stream, x, a, mask, M, K, r, t);
+    hipLaunchKernelGGL(lora_shrink_kernel, sgrid, dim3(kSWaves * 64), 0, stream, x, a, mask, M, K,
+                       r, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int m_tiles = (M + kPBM - 1) / kPBM;
