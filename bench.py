@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--top-k", type=int, default=0,
                     help="truncate P, Q and the proposal law to the top k entries (0: off)")
     ap.add_argument("--top-p", type=float, default=1.0, help="nucleus mass with --top-k (1: off)")
+    ap.add_argument("--fused", action="store_true",
+                    help="config 4: the LM head writes softmax statistics and the step reads them")
     ap.add_argument("--trunc-segments", type=int, default=0,
                     help="workgroups per row on the truncated path (0: automatic)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -172,6 +174,8 @@ def lm_head_workload(args):
     total = args.warmup + args.steps + 1
     uni = torch.from_numpy(gen_uniforms(4, total)).to(dev)
     logits = [torch.empty((M, V), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    nt = (V + isd.isd.STATS_TILE - 1) // isd.isd.STATS_TILE
+    stats = [torch.empty((M, nt, 2), dtype=torch.float32, device=dev) for _ in range(2)]
     xs = [torch.zeros((C, L), dtype=torch.int32, device=dev) for _ in range(2)]
     torch.cuda.synchronize()
     print(f"# W [{H}, {V}] and hidden states ready, {time.perf_counter() - t_gen:.1f} s",
@@ -181,21 +185,38 @@ def lm_head_workload(args):
         ext = logits[i % 2].view(C, 2 * L, V)
         return ext[:, :L], ext[:, L:]
 
+    def sviews(i):
+        st = stats[i % 2].view(C, 2 * L, nt, 2)
+        return st[:, :L], st[:, L:]
+
+    def head(h, i):
+        if args.fused:
+            isd.lm_head_stats(h, Wt, T, out=logits[i % 2], stats=stats[i % 2])
+        else:
+            isd.lm_head_packed(h, Wt, out=logits[i % 2])
+
+    def verify_propose(i):
+        p, qn = views(i)
+        _, q = views(i - 1)
+        u = uni[i + 1]
+        if args.fused:
+            ps, qns = sviews(i)
+            _, qs = sviews(i - 1)
+            return isd.step_fused(p, q, xs[(i - 1) % 2], u[0], u[1], qn, u[2], ps, qs, qns,
+                                  temperature=T, ws=ws, out=dict(next_tokens=xs[i % 2]))
+        return isd.step(p, q, xs[(i - 1) % 2], u[0], u[1], qn, u[2], temperature=T, ws=ws,
+                        out=dict(next_tokens=xs[i % 2]))
+
     # step -1: proposal-only bootstrap gives the first q and x
-    isd.lm_head_packed(hs[0], Wt, out=logits[1])
+    head(hs[0], 1)
     _, qn0 = views(1)
     isd.propose(qn0, uni[0, 2], temperature=T, out=dict(next_tokens=xs[1]))
     ws = isd.workspace(isd.make_shape(views(0)[0]))
     outs = [None, None]
 
     def step(i):
-        h = hs[i % 2]
-        isd.lm_head_packed(h, Wt, out=logits[i % 2])
-        p, qn = views(i)
-        _, q = views(i - 1)
-        o = isd.step(p, q, xs[(i - 1) % 2], uni[i + 1, 0], uni[i + 1, 1], qn, uni[i + 1, 2],
-                     temperature=T, ws=ws, out=dict(next_tokens=xs[i % 2]))
-        outs[i % 2] = o
+        head(hs[i % 2], i)
+        outs[i % 2] = verify_propose(i)
 
     for i in range(args.warmup):
         step(i)
@@ -206,15 +227,10 @@ def lm_head_workload(args):
     t0 = time.perf_counter()
     for n in range(args.steps):
         i = args.warmup + n
-        h = hs[i % 2]
         ev[3 * n].record(stream)
-        isd.lm_head_packed(h, Wt, out=logits[i % 2])
+        head(hs[i % 2], i)
         ev[3 * n + 1].record(stream)
-        p, qn = views(i)
-        _, q = views(i - 1)
-        outs[i % 2] = isd.step(p, q, xs[(i - 1) % 2], uni[i + 1, 0], uni[i + 1, 1], qn,
-                               uni[i + 1, 2], temperature=T, ws=ws,
-                               out=dict(next_tokens=xs[i % 2]))
+        outs[i % 2] = verify_propose(i)
         ev[3 * n + 2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -223,7 +239,7 @@ def lm_head_workload(args):
     step_ms = np.mean([ev[3 * n + 1].elapsed_time(ev[3 * n + 2]) for n in range(args.steps)])
     flops = 2.0 * M * H * V
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    step_bytes = 3 * C * L * V * 2
+    step_bytes = 3 * C * L * V * 2   # what the step would read without the statistics
     ms_per_step = wall * 1e3 / args.steps
     acc = outs[(args.warmup + args.steps - 1) % 2]["accept_len"].float().mean().item()
     print(json.dumps(dict(
@@ -233,12 +249,16 @@ def lm_head_workload(args):
         higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload=f"LM head + ISD step: h [{M}, {H}] x W [{H}, {V}] bf16, then "
                              f"C={C}, L={L} verify/propose", C=C, L=L, V=V, H=H,
-                    head_layout="W packed once (untimed) to k-contiguous [V, H]"),
+                    head_layout="W packed once (untimed) to k-contiguous [V, H]",
+                    step_input="LM-head tile statistics" if args.fused else "logits"),
         gemm=dict(ms=round(float(gemm_ms), 4), tflops=round(gemm_tflops, 1),
                   mfma_util=round(gemm_tflops / 2500.0, 4), peak_tflops=2500.0),
-        step=dict(us=round(float(step_ms) * 1e3, 2),
-                  hbm_gbs=round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
-                  frac=round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
+        step=(dict(us=round(float(step_ms) * 1e3, 2),
+                   note="reads the residual rows and one 128-column tile per proposal")
+              if args.fused else
+              dict(us=round(float(step_ms) * 1e3, 2),
+                   hbm_gbs=round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+                   frac=round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))),
         accept_len_mean_last=round(acc, 3))), flush=True)
 
 

@@ -295,6 +295,39 @@ isd_status_t isd_check_device_error(void *workspace, size_t ws_bytes, void *stre
 isd_status_t isd_set_tuning(int32_t segments, int32_t propose_segments, int32_t resid_segments,
                             int64_t spin_limit);
 
+/* The LM head with softmax statistics (fused epilogue).  Like
+ * isd_lm_head_packed (logits [M, N] = h [M, K] wt[N, K]^T, bf16, K a multiple
+ * of 64), and in the same launch, for every output row and 128-column tile t:
+ *   stats[(row * ceil(N / 128) + t) * 2 + 0] = e = ceil(max_i x_i * k2)
+ *   stats[(row * ceil(N / 128) + t) * 2 + 1] = sum_i 2^(x_i * k2 - e)
+ * over the bf16 logits x it writes, k2 = log2(e) / temperature; e is an
+ * integer (fp32), -inf for a tile past N.  stats: fp32, 8-byte aligned,
+ * M * ceil(N / 128) * 2 values.  An extend forward's rows (per sequence L
+ * anchor rows then L mask rows) give both the p and the qn statistics of a
+ * step; the q statistics are the previous step's qn statistics. */
+isd_status_t isd_lm_head_stats(const void *h, const void *wt, int32_t M, int32_t K, int32_t N,
+                               float temperature, void *logits, float *stats, void *stream);
+
+/* isd_step fed by those statistics (sample mode, no top-k): the softmax
+ * denominators and the proposal draws come from the tile partials, and the
+ * logits are read only at the proposals x, along the residual rows p_j, q_j
+ * of rejecting sequences and in the one 128-column tile where each proposal
+ * draw lands.  Same outputs, conventions and workspace as isd_step; the
+ * statistics must be those of the same logits at the same temperature.
+ *   p_stats, q_stats, qn_stats  tile partials of rows (c, k) of p, q, qn at
+ *     stats + 2 * (c * stats_ldc + k * stats_ld); stats_ld >= ceil(V / 128),
+ *     stats_ldc = 0 means L * stats_ld.  q_stats may be NULL with q_onehot.
+ * Three launches on `stream`.  Errors as isd_step, and ISD_ERR_UNSUPPORTED in
+ * greedy mode or with top_k. */
+isd_status_t isd_step_fused(const isd_shape_t *s, const void *p_logits, const void *q_logits,
+                            const int32_t *proposals, const float *u_accept, const float *u_resid,
+                            const void *qnext_logits, const float *u_propose,
+                            const float *p_stats, const float *q_stats, const float *qn_stats,
+                            int64_t stats_ld, int64_t stats_ldc, int32_t *accept_len,
+                            int32_t *out_tokens, int32_t *n_emitted, float *p_x, float *q_x,
+                            float *alpha, int32_t *next_tokens, float *qnext_x, void *workspace,
+                            size_t ws_bytes, void *stream);
+
 /* Segment-gated LoRA projection of the residual ISD variant (appendix G;
  * section 3.2): h_j = W x_j + [mask_j != 0] B A x_j.  The adapter acts only at
  * mask positions, so clean and introspection rows keep the base weights and

@@ -17,4 +17,4 @@ from .gen import (  # noqa: F401
     gen_uniforms,
     host_bytes_per_step,
 )
-from .lora import LORA_CONFIGS, extend_mask, gen_lora  # noqa: F401
+from .lora import LORA_CONFIGS, extend_mask, gen_exact_head, gen_lora  # noqa: F401

@@ -66,3 +66,24 @@ def gen_lora(cfg: dict, seed: int = 0, weights: bool = True) -> dict:
         out["a"] = _bf16(_rng(0, _A), (r, K), 1.0 / np.sqrt(K))
         out["b"] = _bf16(_rng(0, _B), (N, r), 0.02)
     return out
+
+
+def gen_exact_head(M: int, K: int, N: int, seed: int = 0, which: str = "both") -> dict:
+    """Hidden states and head weights whose products are exact in fp32: h in
+    {-1, 0, 1} and W = k / 128 with integer k in [-16, 16], so every partial
+    sum of a row is a multiple of 2^-7 below 2^9 (K <= 4096).  The bf16 logits
+    are then the round-to-nearest-even of the exact product on any
+    implementation.  wt is [N, K] (k-contiguous); bf16 bits."""
+    out = {}
+    if which in ("both", "h"):
+        rng = _rng(seed, 10)
+        out["h"] = f32_to_bf16_bits(rng.integers(-1, 2, size=(M, K)).astype(np.float32))
+    if which in ("both", "w"):
+        rng = _rng(0, 11)
+        wt = np.empty((N, K), dtype=np.uint16)
+        rows = max(1, (1 << 22) // K)
+        for r0 in range(0, N, rows):
+            r1 = min(N, r0 + rows)
+            wt[r0:r1] = f32_to_bf16_bits(rng.integers(-16, 17, size=(r1 - r0, K)).astype(np.float32) / 128.0)
+        out["wt"] = wt
+    return out

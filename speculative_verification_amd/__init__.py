@@ -23,6 +23,7 @@ from .isd import (  # noqa: F401
     lm_head,
     lm_head_pack,
     lm_head_packed,
+    lm_head_stats,
     lora_gemm,
     lora_pack,
     make_shape,
@@ -31,6 +32,7 @@ from .isd import (  # noqa: F401
     set_trunc_tuning,
     set_tuning,
     step,
+    step_fused,
     step_masked,
     verify_step,
     workspace,

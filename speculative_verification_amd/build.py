@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libisd.so")
-SOURCES = ["isd_step.hip", "isd_trunc.hip", "isd_lm_head.hip", "isd_decode.hip", "isd_api.hip"]
+SOURCES = ["isd_step.hip", "isd_trunc.hip", "isd_fused.hip", "isd_lm_head.hip", "isd_decode.hip",
+           "isd_api.hip"]
 ARCH = "gfx950"
 
 

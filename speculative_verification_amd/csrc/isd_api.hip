@@ -121,6 +121,7 @@ bool vec_ok(const isd_shape_t *s, const void *a, const void *b, const void *c) {
 
 struct Plan {
     bool verify = false, propose = false, residual = false, verify_outputs = false;
+    bool fused = false;   // statistics from the LM head: decide, residual items, propose
 };
 
 isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *workspace,
@@ -196,9 +197,9 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
     a.q_onehot = (!greedy && s->q_onehot) ? 1 : 0;
     a.relax1p = greedy ? 1.0 : 1.0 + (double)s->relax;
     a.sampler = (!greedy && s->sampler == ISD_SAMPLER_GUMBEL) ? 1 : 0;
-    a.rows_pq = plan.verify ? ((greedy || a.q_onehot) ? L : 2 * L) : 0;
+    a.rows_pq = plan.fused ? 0 : plan.verify ? ((greedy || a.q_onehot) ? L : 2 * L) : 0;
     a.n_pq = C * a.rows_pq * a.S;
-    a.q_blk = plan.propose ? L * a.Sq : 0;
+    a.q_blk = (plan.propose && !plan.fused) ? L * a.Sq : 0;
     a.r_blk = (plan.residual && !greedy) ? a.Sr : 0;
     const long long n_items = (long long)a.n_pq + (long long)C * (a.q_blk + a.r_blk);
     if (n_items <= 0 || n_items >= (1LL << 31))
@@ -210,7 +211,10 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
                             : kDefaultSpinLimit;
 
     const bool vec = vec_ok(s, a.p, a.q, a.qn);
-    const hipError_t e = launch_step(a, s->dtype, s->mode, vec, (hipStream_t)stream);
+    hipError_t e = hipSuccess;
+    if (plan.fused) e = launch_fused_decide(a, s->dtype, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_step(a, s->dtype, s->mode, vec, (hipStream_t)stream);
+    if (e == hipSuccess && plan.fused) e = launch_fused_propose(a, s->dtype, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ISD_OK;
 }
@@ -453,6 +457,88 @@ isd_status_t isd_step_masked(const isd_shape_t *s, const void *p_logits, const v
     Plan plan;
     plan.verify = plan.propose = plan.residual = plan.verify_outputs = true;
     return run(s, plan, a, workspace, ws_bytes, stream);
+}
+
+isd_status_t isd_step_fused(const isd_shape_t *s, const void *p_logits, const void *q_logits,
+                            const int32_t *proposals, const float *u_accept, const float *u_resid,
+                            const void *qnext_logits, const float *u_propose,
+                            const float *p_stats, const float *q_stats, const float *qn_stats,
+                            int64_t stats_ld, int64_t stats_ldc, int32_t *accept_len,
+                            int32_t *out_tokens, int32_t *n_emitted, float *p_x, float *q_x,
+                            float *alpha, int32_t *next_tokens, float *qnext_x, void *workspace,
+                            size_t ws_bytes, void *stream) {
+    ISD_TRY(check_shape(s, true));
+    if (s->mode != ISD_MODE_SAMPLE)
+        return fail(ISD_ERR_UNSUPPORTED, "the statistics path is for sample mode");
+    if (s->top_k != 0) return fail(ISD_ERR_UNSUPPORTED, "the statistics path takes no top-k");
+    const size_t es = elem_size(s);
+    ISD_TRY(check_ptr(p_logits, "p_logits", es));
+    ISD_TRY(check_ptr(qnext_logits, "qnext_logits", es));
+    if (!s->q_onehot) {
+        ISD_TRY(check_ptr(q_logits, "q_logits", es));
+        ISD_TRY(check_ptr(q_stats, "q_stats", 8));
+    }
+    ISD_TRY(check_ptr(p_stats, "p_stats", 8));
+    ISD_TRY(check_ptr(qn_stats, "qn_stats", 8));
+    ISD_TRY(check_ptr(u_accept, "u_accept", 4));
+    ISD_TRY(check_ptr(u_resid, "u_resid", 4));
+    ISD_TRY(check_ptr(u_propose, "u_propose", 4));
+    ISD_TRY(check_ptr(proposals, "proposals", 4));
+    ISD_TRY(check_ptr(accept_len, "accept_len", 4));
+    ISD_TRY(check_ptr(out_tokens, "out_tokens", 4));
+    ISD_TRY(check_ptr(n_emitted, "n_emitted", 4));
+    ISD_TRY(check_ptr(next_tokens, "next_tokens", 4));
+    const int n_st = ceil_div(s->V, kStatsTile);
+    if (stats_ld < n_st)
+        return fail(ISD_ERR_ARG, "stats_ld (%lld) must be >= ceil(V / %d) = %d", (long long)stats_ld,
+                    kStatsTile, n_st);
+    if (stats_ldc == 0) stats_ldc = (int64_t)s->L * stats_ld;
+    if (stats_ldc < (int64_t)s->L * stats_ld)
+        return fail(ISD_ERR_ARG, "stats_ldc must be 0 or >= L * stats_ld");
+    StepArgs a = blank_args();
+    a.p = p_logits;
+    a.q = s->q_onehot ? nullptr : q_logits;
+    a.qn = qnext_logits;
+    a.x = proposals;
+    a.ua = u_accept;
+    a.ur = u_resid;
+    a.up = u_propose;
+    a.p_stats = p_stats;
+    a.q_stats = s->q_onehot ? nullptr : q_stats;
+    a.qn_stats = qn_stats;
+    a.s_ld = stats_ld;
+    a.s_ldc = stats_ldc;
+    a.n_stiles = n_st;
+    a.accept_len = accept_len;
+    a.out_tokens = out_tokens;
+    a.n_emitted = n_emitted;
+    a.p_x = p_x;
+    a.q_x = q_x;
+    a.alpha = alpha;
+    a.next_tokens = next_tokens;
+    a.qnext_x = qnext_x;
+    Plan plan;
+    plan.verify = plan.propose = plan.residual = plan.verify_outputs = plan.fused = true;
+    return run(s, plan, a, workspace, ws_bytes, stream);
+}
+
+isd_status_t isd_lm_head_stats(const void *h, const void *wt, int32_t M, int32_t K, int32_t N,
+                               float temperature, void *logits, float *stats, void *stream) {
+    ISD_TRY(check_ptr(h, "h", 16));
+    ISD_TRY(check_ptr(wt, "wt", 16));
+    ISD_TRY(check_ptr(logits, "logits", 2));
+    ISD_TRY(check_ptr(stats, "stats", 8));
+    if (M < 1 || N < 1 || K < 1) return fail(ISD_ERR_ARG, "M, K, N must be >= 1");
+    if (K % 64) return fail(ISD_ERR_ARG, "K must be a multiple of 64 (got %d)", (int)K);
+    if (!(isfinite(temperature) && temperature > 0.0f))
+        return fail(ISD_ERR_ARG, "temperature must be finite and > 0");
+    const float k2 = (float)(1.4426950408889634 / (double)temperature);
+    const hipError_t e = launch_lm_head_stats(static_cast<const uint16_t *>(h),
+                                              static_cast<const uint16_t *>(wt), M, K, N, k2,
+                                              static_cast<uint16_t *>(logits), stats,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "lm_head launch failed: %s", hipGetErrorString(e));
+    return ISD_OK;
 }
 
 isd_status_t isd_lm_head(const void *h, const void *w, int32_t M, int32_t K, int32_t N,

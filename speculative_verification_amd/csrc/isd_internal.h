@@ -149,6 +149,10 @@ struct StepArgs {
     // truncated path
     int St, tpst;              // segments per row, tiles per segment
     TruncWorkspace tws;
+    // statistics path: per-(row, 128-column tile) softmax partials (ref, sum)
+    const float *p_stats, *q_stats, *qn_stats;
+    long long s_ld, s_ldc;     // entries between rows (c, k), (c, k + 1) and sequences
+    int n_stiles;              // ceil(V / 128)
 };
 
 enum Dtype { kBf16 = 0, kF32 = 1 };
@@ -156,6 +160,11 @@ enum Mode { kSample = 0, kGreedy = 1 };
 
 // Launches the step kernel for `a` (dtype/mode select the instantiation).
 hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStream_t stream);
+// The statistics path: the decision from the LM head's partials (before the
+// residual items of launch_step), and the proposals (after it).
+hipError_t launch_fused_decide(const StepArgs &a, int dtype, hipStream_t stream);
+hipError_t launch_fused_propose(const StepArgs &a, int dtype, hipStream_t stream);
+
 // Launches the truncated (top-k / top-p) step kernel for `a` (sample mode).
 hipError_t launch_trunc(const StepArgs &a, int dtype, bool vec, hipStream_t stream);
 
@@ -171,6 +180,12 @@ hipError_t launch_decode_commit(int C, int L, int32_t *state, const int32_t *acc
 hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
                                  uint16_t *out, hipStream_t stream);
 hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStream_t stream);
+
+// The packed LM-head GEMM that also writes per-(row, 128-column tile) softmax
+// partials (ref, sum) of its bf16 logits; k2 = log2(e) / T.
+constexpr int kStatsTile = 128;
+hipError_t launch_lm_head_stats(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
+                                float k2, uint16_t *out, float *stats, hipStream_t stream);
 
 // Segment-gated LoRA projection: t = gate * (x a^T), then out = (x | t) wcat^T
 // with wcat = (w | b) [N, K + r].

@@ -170,12 +170,25 @@ constexpr int kPBPerThread = kPBN * kPVecRow / kThreadsG;   // 4
 // The A operand may come in two K segments: columns [0, K1) from h [M, K1]
 // and [K1, K1 + K2) from h2 [M, K2] (K2 = 0: none); wt is [N, K1 + K2].  Both
 // K1 and K2 are multiples of 64, so a K step never straddles the two.
+//
+// With STATS the epilogue also emits, for every output row and every 128-column
+// tile, the softmax partial of the bf16 logits it writes: an integer reference
+// e = ceil(max * k2) and s = sum 2^(x * k2 - e) (k2 = log2(e) / T), stored as
+// two floats at stats[(row * ceil(N / 128) + tile) * 2].  The ISD step can then
+// take its row statistics from these instead of reading the logits back.
+template <bool STATS>
 __global__ __launch_bounds__(256, 2) void lm_head_packed_kernel(
     const uint16_t *__restrict__ h, int K1, const uint16_t *__restrict__ h2, int K2,
     const uint16_t *__restrict__ wt, int M, int N, uint16_t *__restrict__ out, int m_tiles,
-    int total, int per_xcd) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[kPBM * kPLd];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[kPBN * kPLd];
+    int total, int per_xcd, float k2, float *__restrict__ stats) {
+    // operand tiles; with STATS the same memory later stages the whole output
+    // tile ([256][128 + 8] bf16, 68 KB: two workgroups still share a CU)
+    constexpr int kStageLd = kPBN + 8;
+    constexpr int kOperands = (kPBM + kPBN) * kPLd;
+    constexpr int kSmem = STATS && kPBM * kStageLd > kOperands ? kPBM * kStageLd : kOperands;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
+    uint16_t *As = smem;
+    uint16_t *Bs = smem + kPBM * kPLd;
 
     const int b = blockIdx.x;
     const int idx = (b % kXcds) * per_xcd + b / kXcds;
@@ -259,17 +272,92 @@ __global__ __launch_bounds__(256, 2) void lm_head_packed_kernel(
         __syncthreads();
     }
 
+    if constexpr (!STATS) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-            const int col = n0 + wn * 64 + ni * 32 + lane % 32;
+            for (int ni = 0; ni < 2; ++ni) {
+                const int col = n0 + wn * 64 + ni * 32 + lane % 32;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = m0 + wm * 128 + mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
-                if (row < M && col < N) out[(size_t)row * N + col] = bf16_rne(acc[mi][ni][i]);
+                for (int i = 0; i < 16; ++i) {
+                    const int row = m0 + wm * 128 + mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+                    if (row < M && col < N) out[(size_t)row * N + col] = bf16_rne(acc[mi][ni][i]);
+                }
+            }
+    } else {
+        // The output tile is staged in LDS as bf16 (the K loop ended on a
+        // barrier, so the operand tiles are free) and leaves as 16-byte row
+        // chunks; thread t then reduces the 128 staged columns of row t in two
+        // passes (max, then the sum of 2^(x k2 - e)).
+        uint16_t *tileL = smem;   // [256][kStageLd]
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int rl = wm * 128 + mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+                    const int cl = wn * 64 + ni * 32 + lane % 32;
+                    tileL[rl * kStageLd + cl] = bf16_rne(acc[mi][ni][i]);
+                }
+        __syncthreads();
+        // the logits leave the staged tile as 16-byte row chunks (a row's 16
+        // chunks are consecutive threads), or element by element at a ragged
+        // or unaligned edge
+        const bool vec_out = (N % 8) == 0;
+#pragma unroll 4
+        for (int q = tid; q < kPBM * (kPBN / 8); q += kThreadsG) {
+            const int rl = q / (kPBN / 8), c8 = (q % (kPBN / 8)) * 8;
+            const int grow = m0 + rl, gcol = n0 + c8;
+            if (grow >= M) continue;
+            const uint16_t *sp = &tileL[rl * kStageLd + c8];
+            uint16_t *dp = out + (size_t)grow * N + gcol;
+            if (vec_out && gcol + 8 <= N) {
+                *reinterpret_cast<uint4 *>(dp) = *reinterpret_cast<const uint4 *>(sp);
+            } else {
+                for (int e = 0; e < 8 && gcol + e < N; ++e) dp[e] = sp[e];
             }
         }
+    }
+    if constexpr (STATS) {
+        const uint16_t *tileL = smem;
+        const int row = m0 + tid;
+        const uint16_t *src = &tileL[tid * kStageLd];
+        const float neg = -__builtin_inff();
+        float m = neg;
+#pragma unroll
+        for (int q8 = 0; q8 < kPBN / 8; ++q8) {
+            const uint4 w4 = *reinterpret_cast<const uint4 *>(src + q8 * 8);
+            const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = n0 + q8 * 8 + 2 * e;
+                if (c < N) m = fmaxf(m, __uint_as_float(w[e] << 16));
+                if (c + 1 < N) m = fmaxf(m, __uint_as_float(w[e] & 0xFFFF0000u));
+            }
+        }
+        const float ref = m == neg ? neg : ceilf(m * k2);
+        float sum = 0.0f;
+        if (ref != neg) {
+#pragma unroll
+            for (int q8 = 0; q8 < kPBN / 8; ++q8) {
+                const uint4 w4 = *reinterpret_cast<const uint4 *>(src + q8 * 8);
+                const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = n0 + q8 * 8 + 2 * e;
+                    if (c < N) sum += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(w[e] << 16), k2, -ref));
+                    if (c + 1 < N)
+                        sum += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(w[e] & 0xFFFF0000u), k2, -ref));
+                }
+            }
+        }
+        if (row < M) {
+            const size_t at = ((size_t)row * ((N + kPBN - 1) / kPBN) + n0 / kPBN) * 2;
+            stats[at] = ref;
+            stats[at + 1] = sum;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -379,8 +467,9 @@ hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, i
     const long long total = (long long)m_tiles * n_tiles;
     if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
     const int per_xcd = (int)((total + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(lm_head_packed_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0,
-                       stream, h, K, nullptr, 0, wt, M, N, out, m_tiles, (int)total, per_xcd);
+    hipLaunchKernelGGL(lm_head_packed_kernel<false>, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0,
+                       stream, h, K, nullptr, 0, wt, M, N, out, m_tiles, (int)total, per_xcd, 0.0f,
+                       nullptr);
     return hipGetLastError();
 }
 
@@ -397,14 +486,28 @@ hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t
     const long long total = (long long)m_tiles * n_tiles;
     if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
     const int per_xcd = (int)((total + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(lm_head_packed_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0,
-                       stream, x, K, t, r, wcat, M, N, out, m_tiles, (int)total, per_xcd);
+    hipLaunchKernelGGL(lm_head_packed_kernel<false>, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0,
+                       stream, x, K, t, r, wcat, M, N, out, m_tiles, (int)total, per_xcd, 0.0f,
+                       nullptr);
     return hipGetLastError();
 }
 
 hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStream_t stream) {
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((K + 63) / 64));
     hipLaunchKernelGGL(pack_wt_kernel, grid, dim3(256), 0, stream, w, wt, K, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_lm_head_stats(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
+                               float k2, uint16_t *out, float *stats, hipStream_t stream) {
+    const int m_tiles = (M + kPBM - 1) / kPBM;
+    const int n_tiles = (N + kPBN - 1) / kPBN;
+    const long long total = (long long)m_tiles * n_tiles;
+    if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
+    const int per_xcd = (int)((total + kXcds - 1) / kXcds);
+    hipLaunchKernelGGL(lm_head_packed_kernel<true>, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0,
+                       stream, h, K, nullptr, 0, wt, M, N, out, m_tiles, (int)total, per_xcd, k2,
+                       stats);
     return hipGetLastError();
 }
 

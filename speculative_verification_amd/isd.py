@@ -59,6 +59,9 @@ _SIGS = {
     "isd_set_tuning": (ctypes.c_int, [_i32, _i32, _i32, _i64]),
     "isd_set_trunc_tuning": (ctypes.c_int, [_i32]),
     "isd_lora_pack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "isd_lm_head_stats": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp, _vp]),
+    "isd_step_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 10 + [_i64, _i64] +
+                       [_vp] * 8 + [_vp, _sz, _vp]),
     "isd_lora_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "isd_last_error": (ctypes.c_char_p, []),
 }
@@ -470,3 +473,65 @@ def lora_gemm(x: torch.Tensor, a: torch.Tensor, wcat: torch.Tensor, mask=None, *
     _check(lib().isd_lora_gemm(_ptr(x), _ptr(a), _ptr(wcat), _ptr(mask), M, K, N, r, _ptr(t),
                                _ptr(out), _stream()))
     return out, t
+
+
+STATS_TILE = 128
+
+
+def lm_head_stats(h, wt, temperature=1.0, out=None, stats=None):
+    """logits [M, N] = h @ wt^T like lm_head_packed, plus the softmax partials
+    of every (row, 128-column tile): stats [M, ceil(N / 128), 2] fp32 (e, s)."""
+    if h.dtype != torch.bfloat16 or wt.dtype != torch.bfloat16:
+        raise ValueError("lm_head_stats takes bf16 tensors")
+    if not (h.is_contiguous() and wt.is_contiguous()):
+        raise ValueError("lm_head_stats takes contiguous tensors")
+    M, K = h.shape
+    N, K2 = wt.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    nt = (N + STATS_TILE - 1) // STATS_TILE
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=h.device) if out is None else out
+    stats = torch.empty((M, nt, 2), dtype=torch.float32, device=h.device) if stats is None else stats
+    _check(lib().isd_lm_head_stats(_ptr(h), _ptr(wt), M, K, N, float(temperature), _ptr(out),
+                                   _ptr(stats), _stream()))
+    return out, stats
+
+
+def _stats_layout(st, C, L, nt, name):
+    """(stats_ld, stats_ldc) in entries of a [C, L, nt, 2] fp32 view."""
+    if st.dtype != torch.float32 or st.dim() != 4 or tuple(st.shape) != (C, L, nt, 2):
+        raise ValueError(f"{name} must be fp32 [C, L, ceil(V / 128), 2]")
+    if st.stride(3) != 1 or st.stride(2) != 2 or st.stride(1) % 2 or st.stride(0) % 2:
+        raise ValueError(f"{name} must have contiguous (e, s) entries")
+    return st.stride(1) // 2, st.stride(0) // 2
+
+
+def step_fused(p, q, x, ua, ur, qn, up, p_stats, q_stats, qn_stats, *, temperature=1.0,
+               relax=0.0, q_onehot=False, sampler="cdf", out=None, ws=None):
+    """isd_step from the LM head's tile statistics (views [C, L, ceil(V / 128), 2])."""
+    shape = make_shape(p, MODE_SAMPLE, temperature, relax, q_onehot, sampler)
+    _same_layout(shape, qn, "qn", MODE_SAMPLE, temperature)
+    if not q_onehot:
+        _same_layout(shape, q, "q", MODE_SAMPLE, temperature)
+    C, L, dev = shape.C, shape.L, p.device
+    nt = (shape.V + STATS_TILE - 1) // STATS_TILE
+    lay = _stats_layout(p_stats, C, L, nt, "p_stats")
+    if _stats_layout(qn_stats, C, L, nt, "qn_stats") != lay or (
+            not q_onehot and _stats_layout(q_stats, C, L, nt, "q_stats") != lay):
+        raise ValueError("the statistics views must share one layout")
+    o = dict(accept_len=_out(out, "accept_len", (C,), torch.int32, dev),
+             out_tokens=_out(out, "out_tokens", (C, L), torch.int32, dev),
+             n_emitted=_out(out, "n_emitted", (C,), torch.int32, dev),
+             p_x=_out(out, "p_x", (C, L), torch.float32, dev),
+             q_x=_out(out, "q_x", (C, L), torch.float32, dev),
+             alpha=_out(out, "alpha", (C,), torch.float32, dev),
+             next_tokens=_out(out, "next_tokens", (C, L), torch.int32, dev),
+             qnext_x=_out(out, "qnext_x", (C, L), torch.float32, dev))
+    ws = workspace(shape, dev) if ws is None else ws
+    _check(lib().isd_step_fused(
+        ctypes.byref(shape), _ptr(p), _ptr(q), _ptr(x), _ptr(ua), _ptr(ur), _ptr(qn), _ptr(up),
+        _ptr(p_stats), _ptr(q_stats), _ptr(qn_stats), lay[0], lay[1], _ptr(o["accept_len"]),
+        _ptr(o["out_tokens"]), _ptr(o["n_emitted"]), _ptr(o["p_x"]), _ptr(o["q_x"]),
+        _ptr(o["alpha"]), _ptr(o["next_tokens"]), _ptr(o["qnext_x"]), _ptr(ws), ws.numel(),
+        _stream()))
+    return o

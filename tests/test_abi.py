@@ -225,3 +225,22 @@ def test_variant_shape_validation(isd):
     ok = _shape(isd)
     ok.q_onehot = 1
     assert _verify(isd, ok, ws_bytes=16, q=None) == 3
+
+
+def test_fused_and_stats_validation(isd):
+    """The statistics path checks its arguments on the host (no compute)."""
+    lib = isd.lib()
+    sh = _shape(isd)
+    args = [FAKE] * 10 + [ctypes.c_int64(1187), ctypes.c_int64(0)] + [FAKE] * 8 + [FAKE, 1 << 30, None]
+    bad = list(args)
+    bad[10] = ctypes.c_int64(1186)          # fewer than ceil(151936 / 128) entries per row
+    assert lib.isd_step_fused(ctypes.byref(sh), *bad) == 1
+    assert "stats_ld" in lib.isd_last_error().decode()
+    greedy = _shape(isd, mode=1)
+    assert lib.isd_step_fused(ctypes.byref(greedy), *args) == 2
+    trunc = _shape(isd)
+    trunc.top_k = 8
+    assert lib.isd_step_fused(ctypes.byref(trunc), *args) == 2
+    assert lib.isd_lm_head_stats(FAKE, FAKE, 8, 100, 64, ctypes.c_float(1.0), FAKE, FAKE, None) == 1
+    assert lib.isd_lm_head_stats(FAKE, FAKE, 8, 128, 64, ctypes.c_float(0.0), FAKE, FAKE, None) == 1
+    assert "temperature" in lib.isd_last_error().decode()
