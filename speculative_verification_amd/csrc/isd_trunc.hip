@@ -233,6 +233,8 @@ __device__ __forceinline__ void take_tile(const TileRaw<T> &raw, const float (&v
 
 // Top k keys of tiles [tb, te) of `row`, merged over the workgroup into
 // sh.lists[0] (largest first; 0 past the end).  All threads call it.
+constexpr int kMergeEvery = 2;   // rounds between merges of the four lists
+
 template <typename T, bool VEC>
 __device__ __forceinline__ void select_segment(const T *__restrict__ row, int tb, int te, int V,
                                                int k, int wave, int lane, TruncShared<T> &sh) {
@@ -241,8 +243,7 @@ __device__ __forceinline__ void select_segment(const T *__restrict__ row, int tb
     const bool have = t < te;
     TileRaw<T> cur, nxt;
     if (have) load_tile<T, VEC>(row, t, V, lane, cur);
-    bool more = have && t + kWavesPerGroup < te;
-    if (more) load_tile<T, VEC>(row, t + kWavesPerGroup, V, lane, nxt);
+    if (have && t + kWavesPerGroup < te) load_tile<T, VEC>(row, t + kWavesPerGroup, V, lane, nxt);
 
     // seeds: the lane bests of each wavefront's first tile
     float v[kLaneElems];
@@ -264,14 +265,28 @@ __device__ __forceinline__ void select_segment(const T *__restrict__ row, int tb
     __syncthreads();
     if (have) take_tile<T>(cur, v, vmax, t, V, k, wave, lane, best, s, sh);
 
-    while (more) {
-        t += kWavesPerGroup;
-        cur = nxt;
-        more = t + kWavesPerGroup < te;
-        if (more) load_tile<T, VEC>(row, t + kWavesPerGroup, V, lane, nxt);
-        unpack<T>(cur, v);
-        vmax = max32(v);
-        take_tile<T>(cur, v, vmax, t, V, k, wave, lane, 0, s, sh);
+    // the rest, one tile per wavefront per round; every few rounds the four
+    // lists (disjoint: each holds entries of its own tiles only) are merged so
+    // that every wavefront filters with the workgroup's true k-th best
+    const int rounds = (te - tb + kWavesPerGroup - 1) / kWavesPerGroup;
+    for (int rd = 1; rd < rounds; ++rd) {
+        t = tb + wave + kWavesPerGroup * rd;
+        if (t < te) {
+            cur = nxt;
+            if (t + kWavesPerGroup < te) load_tile<T, VEC>(row, t + kWavesPerGroup, V, lane, nxt);
+            unpack<T>(cur, v);
+            vmax = max32(v);
+            take_tile<T>(cur, v, vmax, t, V, k, wave, lane, 0, s, sh);
+        }
+        if (rd % kMergeEvery == 0 && rd + 1 < rounds) {
+            sh.lists[wave][lane] = s.list;
+            __syncthreads();
+            uint64_t m = sh.lists[0][lane];
+#pragma unroll
+            for (int w = 1; w < kWavesPerGroup; ++w) m = wave_merge_desc(m, sh.lists[w][lane], lane);
+            s.theta = umax64(s.theta, uniform64(lane_key(m, k - 1)));
+            __syncthreads();
+        }
     }
 
     sh.lists[wave][lane] = s.list;
