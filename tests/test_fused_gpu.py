@@ -73,7 +73,7 @@ def _check_stats(logit_bits, stats, T):
     np.testing.assert_allclose(Z_tiles, Z, rtol=1e-5)
 
 
-def _run(isd, C, L, K, V, T, seed, check_rows=None):
+def _run(isd, C, L, K, V, T, seed, check_rows=None, **variant):
     import torch
     M = C * 2 * L
     wt = gen_exact_head(M, K, V, which="w")["wt"]
@@ -102,20 +102,27 @@ def _run(isd, C, L, K, V, T, seed, check_rows=None):
     ua, ur, up, u0 = (rng.random((C, L), dtype=np.float32) for _ in range(4))
     # proposals drawn from the previous mask rows (the q law), by the oracle
     x = np.zeros((C, L), dtype=np.int32)
-    x[seqs] = O.propose_sample(O.decode_logits(op[:, L:], "bf16"), u0[seqs], T)[0]
+    if variant.get("q_onehot"):
+        x[seqs] = O.argmax_first(O.decode_logits(op[:, L:], "bf16"))
+    else:
+        x[seqs] = O.propose_sample(O.decode_logits(op[:, L:], "bf16"), u0[seqs], T)[0]
     if check_rows is not None:
         x[np.setdiff1d(np.arange(C), seqs)] = 7
     dv = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
     args = (p, q, dv(x), dv(ua), dv(ur), qn, dv(up))
-    fused = to_host(isd.step_fused(*args, st_c[:, :L], st_p[:, L:], st_c[:, L:], temperature=T))
-    plain = to_host(isd.step(*args, temperature=T))
+    qs = None if variant.get("q_onehot") else st_p[:, L:]
+    fused = to_host(isd.step_fused(*args, st_c[:, :L], qs, st_c[:, L:], temperature=T, **variant))
+    plain = to_host(isd.step(*args, temperature=T, **variant))
     torch.cuda.synchronize()
 
     d = dict(p=oc[:, :L], q=op[:, L:], qn=oc[:, L:], x=x[seqs], ua=ua[seqs], ur=ur[seqs],
              up=up[seqs])
     ref = {}
-    v = O.verify_sample(O.decode_logits(d["p"], "bf16"), O.decode_logits(d["q"], "bf16"), d["x"],
-                        d["ua"], d["ur"], T)
+    v = O.verify_sample(O.decode_logits(d["p"], "bf16"),
+                        None if variant.get("q_onehot") else O.decode_logits(d["q"], "bf16"), d["x"],
+                        d["ua"], d["ur"], T, relax=variant.get("relax", 0.0),
+                        q_onehot=variant.get("q_onehot", False),
+                        sampler=variant.get("sampler", "cdf"), seq_ids=seqs)
     tok, prob, _, pflag = O.propose_sample(O.decode_logits(d["qn"], "bf16"), d["up"], T)
     ref = dict(accept_len=v["accept_len"], out_tokens=v["out_tokens"], n_emitted=v["n_emitted"],
                p_x=v["p_x"], q_x=v["q_x"], alpha=v["alpha"], flagged=v["flagged"],
@@ -150,3 +157,12 @@ def test_fused_step_serving_shape(isd):
     np.testing.assert_allclose(fused["alpha"], plain["alpha"], rtol=1e-5)
     log(f"fused serving shape: oracle {st}, next tokens equal to the plain path {same_next:.4f}, "
         f"{int(ok.sum())} unflagged sequences of {ok.size} checked against the oracle")
+
+
+@pytest.mark.parametrize("variant", [dict(sampler="gumbel"), dict(q_onehot=True, relax=0.5),
+                                     dict(q_onehot=True, sampler="gumbel")])
+def test_fused_step_variants(isd, variant):
+    """One-hot proposals (no q statistics), relaxed acceptance and the
+    Gumbel-max correction on the statistics path."""
+    fused, plain, ref, st, _ = _run(isd, 4, 8, 256, 20000, 1.0, seed=9, **variant)
+    log(f"fused {variant}: {st}")
