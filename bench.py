@@ -413,7 +413,8 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     positions = C * L
-    bytes_alg = 3 * C * L * V * 2
+    # rows the step reads once: anchor p, proposal q (sample mode only), mask qn
+    bytes_alg = (2 if mode == "greedy" else 3) * C * L * V * 2
     achieved = bytes_alg / (kernel_avg_ms * 1e-3) / 1e9
 
     traffic = None
