@@ -21,13 +21,12 @@
 //       then q_0..q_{L-1} unless the proposals are one-hot) and each row
 //       segment;
 //   [mask-row items]    for each sequence c, each mask row qn_k and segment.
-// An item streams its segment with four wavefronts.  Each wavefront keeps its
-// best 64 keys in a lane-distributed sorted list (lane t holds rank t) and a
-// threshold, the key of its rank k-1; an entry enters only if it beats the
-// threshold of its own wavefront or of any wavefront of the workgroup (shared
-// in LDS).  Candidates are merged 64 at a time with a bitonic sort and a
-// bitonic merge across lanes.  The workgroup's four lists are merged and the
-// segment's top k keys recorded.  The item that completes a row merges its
+// An item streams its segment with four wavefronts and records, in LDS, the
+// best entry of each lane's 32 entries of a tile (a group); it then picks the
+// k best group keys, re-reads those k groups and keeps their best k entries:
+// the segment's top k, recorded for the row.  Keys are kept in lane-
+// distributed sorted lists (lane t holds rank t), merged with a bitonic sort
+// and a bitonic merge across lanes.  The item that completes a row merges its
 // segment records, applies top-k and top-p and then either draws the next
 // proposal (mask row; inverse CDF over the survivors in vocabulary order) or
 // stores P'(x_k) or Q'(x_k) and the row's survivors sorted by index (verify
@@ -101,30 +100,36 @@ __device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t b, int 
 // Selection of a segment's top k (one workgroup)
 // ---------------------------------------------------------------------------
 //
-// Every wavefront keeps its best keys in a lane-distributed sorted list and
-// filters entries against a threshold theta, the key of some list's rank k-1:
-// at least k entries beat it, so nothing at or below it can reach the top k.
-// The four wavefronts seed their lists with the 64 lane bests of their first
-// tile and take theta from the merged seeds (the k-th best of 256 entries),
-// which already discards nearly everything; later tiles are skipped unless a
-// lane's maximum reaches theta's value, and the few entries that beat theta
-// are inserted one at a time.  Wavefronts share their thresholds through LDS.
+// A lane's 32 entries of a tile form a group.  Every top-k entry lies in a
+// group whose best key is among the k best group keys: if it did not, k
+// group maxima would beat it.  So the selection takes three passes:
+//
+//   1. stream the segment and record each group's best entry in LDS: the
+//      order bits of its value and its position in the lane (32 + 8 bits),
+//      nothing else, so the stream never waits on selection work;
+//   2. from LDS: a threshold from the column maxima (below) leaves few
+//      records, which are compacted, sorted and merged; ranks 0..k-1 of the
+//      result are the candidate groups;
+//   3. re-read the candidate groups (k * 32 entries, at most one tile's
+//      worth) and keep the best k of their entries.
+// Passes 1 and 2 run over chunks of kMaxSegTiles tiles, so LDS bounds no
+// segment length.
+
+constexpr int kMaxSegTiles = 80;   // tiles per chunk of group records in LDS
+
+// Candidate records per chunk: at most k columns (below) hold one, and a column
+// holds kMaxSegTiles / kWavesPerGroup records.
+constexpr int kMaxCand = kMaxSegTiles / kWavesPerGroup * kMaxTopK;
 
 template <typename T>
 struct TruncShared {
     int flag;
-    unsigned long long theta;              // largest wavefront threshold of the workgroup
+    int ncand;
     uint64_t lists[kWavesPerGroup][kWave];
-    // a tile with candidates is staged here so that single entries can be read
-    // back by (lane, element): word w of lane l at [w * 64 + l]
-    uint32_t stage[kWavesPerGroup][TileRaw<T>::kWords * kWave];
+    uint32_t gord[kMaxSegTiles * kWave];   // order bits of each group's best value (0: empty)
+    uint8_t gpos[kMaxSegTiles * kWave];    // its position among the lane's 32 entries
+    uint16_t cand[kMaxCand];               // records of a chunk that reach the threshold
 };
-
-// The workgroup's shared threshold, read fresh (other wavefronts raise it).
-template <typename T>
-__device__ __forceinline__ uint64_t shared_theta(TruncShared<T> &sh) {
-    return (uint64_t)__hip_atomic_load(&sh.theta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
@@ -156,145 +161,140 @@ __device__ __forceinline__ uint64_t list_insert(uint64_t list, uint64_t key, int
     return lane < pos ? list : (lane == pos ? key : up);
 }
 
-// The lane's best entry of a tile: largest value, lowest index among equals
-// (a lane holds its entries in increasing index); 0 if it holds none below V.
-__device__ __forceinline__ uint64_t lane_best(const float (&v)[kLaneElems], float vmax, int tile,
-                                              int lane, int V) {
-    int fi = 0;
-#pragma unroll
-    for (int i = kLaneElems - 1; i >= 0; --i) fi = (v[i] == vmax) ? i : fi;
-    const long long idx = elem_index(tile, lane, fi);
-    return idx < V ? make_key(vmax, (uint32_t)idx) : 0;
-}
-
-struct SegSelect {
-    uint64_t list = 0;     // lane t: rank t of this wavefront's best keys so far
-    uint64_t theta = 0;    // wave-uniform threshold
-};
-
-// Element i of lane l of a staged tile, as fp32 (same layout as elem()).
-template <typename T>
-__device__ __forceinline__ float staged_value(const uint32_t *stage, int l, int i) {
-    if constexpr (sizeof(T) == 2) {
-        const uint32_t w = stage[(i >> 1) * kWave + l];
-        return (i & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+// Offers one key per lane (0: none) to the sorted list whose threshold is
+// theta (the key of rank k-1, or 0): a batch with many candidates is sorted
+// and merged, a few are inserted one by one.  Returns the new threshold.
+__device__ __forceinline__ uint64_t list_offer(uint64_t &list, uint64_t key, uint64_t theta,
+                                               int k, int lane) {
+    const unsigned long long cand = __ballot(key > theta);
+    if (!cand) return theta;
+    if (__popcll(cand) > 8) {
+        list = wave_merge_desc(list, wave_sort_desc(key > theta ? key : 0, lane), lane);
     } else {
-        return __uint_as_float(stage[i * kWave + l]);
+        for (unsigned long long m = cand; m; m &= m - 1) {
+            const uint64_t kk = lane_key(key, __ffsll((long long)m) - 1);
+            if (kk > theta) {
+                list = list_insert(list, kk, lane);
+                theta = umax64(theta, uniform64(lane_key(list, k - 1)));
+            }
+        }
     }
+    return umax64(theta, uniform64(lane_key(list, k - 1)));
 }
 
-// Inserts every entry of the tile (raw words `raw`, values v) that beats the
-// threshold, except a lane's entry whose key equals `skip` (that lane's seed,
-// already listed).  The candidates are the entries whose value reaches the
-// threshold's value; they are visited one at a time in a compact loop.
+// Key of the group record at position `at` of the chunk starting at tile cb
+// (0 for an empty group).
 template <typename T>
-__device__ __forceinline__ void take_tile(const TileRaw<T> &raw, const float (&v)[kLaneElems],
-                                          float vmax, int tile, int V, int k, int wave, int lane,
-                                          uint64_t skip, SegSelect &s, TruncShared<T> &sh) {
-    s.theta = umax64(s.theta, shared_theta(sh));
-    const float tv = s.theta ? key_value(s.theta) : -__builtin_inff();
-    if (!__ballot(vmax >= tv)) return;
-    uint32_t cm = 0;   // the lane's candidate elements
-#pragma unroll
-    for (int i = 0; i < kLaneElems; ++i) cm |= (v[i] >= tv ? 1u : 0u) << i;
-    // a lane with one candidate holds it as its maximum; lanes with more are
-    // read back from a staged copy of the tile
-    const bool several = __popc(cm) > 1;
-    uint32_t *stage = sh.stage[wave];
-    if (__ballot(several)) {
-#pragma unroll
-        for (int w = 0; w < TileRaw<T>::kWords; ++w) stage[w * kWave + lane] = raw.w[w];
-    }
-    const unsigned long long multi = __ballot(several);
-    const uint64_t theta = s.theta;   // the list's own threshold is refreshed after the tile
-    bool raised = false;
-    for (;;) {
-        const unsigned long long lanes = __ballot(cm != 0);
-        if (!lanes) break;
-        const int l = __ffsll((long long)lanes) - 1;
-        const uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)cm, l);
-        const int i = __ffs((int)bits) - 1;
-        if (lane == l) cm &= cm - 1;
-        const long long idx = elem_index(tile, l, i);
-        if (idx >= V) continue;
-        const float vi = ((multi >> l) & 1ull)
-                             ? staged_value<T>(stage, l, i)
-                             : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vmax), l));
-        const uint64_t key = make_key(vi, (uint32_t)idx);
-        if (key <= theta || key == lane_key(skip, l)) continue;
-        s.list = list_insert(s.list, key, lane);
-        raised = true;
-    }
-    if (raised) {
-        s.theta = umax64(s.theta, uniform64(lane_key(s.list, k - 1)));
-        if (lane == 0) atomicMax(&sh.theta, (unsigned long long)s.theta);
-    }
+__device__ __forceinline__ uint64_t record_key(const TruncShared<T> &sh, int cb, int at) {
+    const uint32_t o = sh.gord[at];
+    if (o == 0u) return 0;
+    const uint32_t idx = (uint32_t)elem_index(cb + at / kWave, at % kWave, sh.gpos[at]);
+    return ((uint64_t)o << 32) | (uint64_t)(uint32_t)~idx;
 }
 
 // Top k keys of tiles [tb, te) of `row`, merged over the workgroup into
 // sh.lists[0] (largest first; 0 past the end).  All threads call it.
-constexpr int kMergeEvery = 2;   // rounds between merges of the four lists
-
 template <typename T, bool VEC>
 __device__ __forceinline__ void select_segment(const T *__restrict__ row, int tb, int te, int V,
                                                int k, int wave, int lane, TruncShared<T> &sh) {
-    if (threadIdx.x == 0) sh.theta = 0;
-    int t = tb + wave;
-    const bool have = t < te;
-    TileRaw<T> cur, nxt;
-    if (have) load_tile<T, VEC>(row, t, V, lane, cur);
-    if (have && t + kWavesPerGroup < te) load_tile<T, VEC>(row, t + kWavesPerGroup, V, lane, nxt);
-
-    // seeds: the lane bests of each wavefront's first tile
-    float v[kLaneElems];
-    float vmax = -__builtin_inff();
-    uint64_t best = 0;
-    if (have) {
-        unpack<T>(cur, v);
-        vmax = max32(v);
-        best = lane_best(v, vmax, t, lane, V);
-    }
-    SegSelect s;
-    s.list = wave_sort_desc(best, lane);
-    sh.lists[wave][lane] = s.list;
-    __syncthreads();
-    uint64_t merged = sh.lists[0][lane];
+    uint64_t groups = 0;   // the best group keys of the chunks so far (same in every wavefront)
+    for (int cb = tb; cb < te; cb += kMaxSegTiles) {
+        const int ce = min(te, cb + kMaxSegTiles);
+        // ---- 1. stream: each group's best entry into LDS ----
+        stream_row<T, VEC>(row, cb, ce, V, wave, lane, [&](const TileRaw<T> &r, int tile) {
+            float v[kLaneElems];
+            unpack<T>(r, v);
+            const float vmax = max32(v);
+            int fi = 0;   // first position holding the maximum: the lowest index among equals
 #pragma unroll
-    for (int w = 1; w < kWavesPerGroup; ++w) merged = wave_merge_desc(merged, sh.lists[w][lane], lane);
-    s.theta = uniform64(lane_key(merged, k - 1));
-    __syncthreads();
-    if (have) take_tile<T>(cur, v, vmax, t, V, k, wave, lane, best, s, sh);
+            for (int i = kLaneElems - 1; i >= 0; --i) fi = (v[i] == vmax) ? i : fi;
+            const int at = (tile - cb) * kWave + lane;
+            sh.gord[at] = elem_index(tile, lane, fi) < V ? ord_bits(vmax) : 0u;
+            sh.gpos[at] = (uint8_t)fi;
+        });
+        if (threadIdx.x == 0) sh.ncand = 0;
+        __syncthreads();
 
-    // the rest, one tile per wavefront per round; every few rounds the four
-    // lists (disjoint: each holds entries of its own tiles only) are merged so
-    // that every wavefront filters with the workgroup's true k-th best
-    const int rounds = (te - tb + kWavesPerGroup - 1) / kWavesPerGroup;
-    for (int rd = 1; rd < rounds; ++rd) {
-        t = tb + wave + kWavesPerGroup * rd;
-        if (t < te) {
-            cur = nxt;
-            if (t + kWavesPerGroup < te) load_tile<T, VEC>(row, t + kWavesPerGroup, V, lane, nxt);
-            unpack<T>(cur, v);
-            vmax = max32(v);
-            take_tile<T>(cur, v, vmax, t, V, k, wave, lane, 0, s, sh);
-        }
-        if (rd % kMergeEvery == 0 && rd + 1 < rounds) {
-            sh.lists[wave][lane] = s.list;
-            __syncthreads();
-            uint64_t m = sh.lists[0][lane];
+        // ---- 2. the k best group keys ----
+        // A thread's records (lane `lane` of its wavefront's tiles) form a
+        // column.  theta0, the k-th best of the column maxima and of the
+        // earlier chunks' best keys, is reached by at least k keys, so every
+        // top-k key reaches it; and at most k columns hold a key that does.
+        uint64_t colmax = 0;
+        for (int t = cb + wave; t < ce; t += kWavesPerGroup)
+            colmax = umax64(colmax, record_key(sh, cb, (t - cb) * kWave + lane));
+        sh.lists[wave][lane] = wave_sort_desc(colmax, lane);
+        __syncthreads();
+        uint64_t m = sh.lists[0][lane];
 #pragma unroll
-            for (int w = 1; w < kWavesPerGroup; ++w) m = wave_merge_desc(m, sh.lists[w][lane], lane);
-            s.theta = umax64(s.theta, uniform64(lane_key(m, k - 1)));
-            __syncthreads();
+        for (int w = 1; w < kWavesPerGroup; ++w) m = wave_merge_desc(m, sh.lists[w][lane], lane);
+        if (cb != tb) m = wave_merge_desc(m, groups, lane);
+        const uint64_t theta0 = uniform64(lane_key(m, k - 1));
+        // list the chunk's records that reach theta0 (a wavefront at a time)
+        const bool col = colmax != 0 && colmax >= theta0;
+        if (__ballot(col)) {
+            for (int t = cb + wave; t < ce; t += kWavesPerGroup) {
+                const int at = (t - cb) * kWave + lane;
+                const uint64_t key = col ? record_key(sh, cb, at) : 0;
+                const bool c = key != 0 && key >= theta0;
+                const unsigned long long bal = __ballot(c);
+                if (!bal) continue;
+                int base = 0;
+                if (lane == 0) base = atomicAdd(&sh.ncand, __popcll(bal));
+                base = __builtin_amdgcn_readfirstlane(base);
+                if (c) sh.cand[base + __popcll(bal & ((1ull << lane) - 1))] = (uint16_t)at;
+            }
         }
+        __syncthreads();
+        // sort them, 64 per wavefront at a time, and merge with the earlier best
+        const int n = sh.ncand;
+        uint64_t wl = 0;
+        for (int b = wave * kWave; b < n; b += kThreads) {
+            const uint64_t sorted =
+                wave_sort_desc(b + lane < n ? record_key(sh, cb, sh.cand[b + lane]) : 0, lane);
+            wl = b == wave * kWave ? sorted : wave_merge_desc(wl, sorted, lane);
+        }
+        sh.lists[wave][lane] = wl;
+        __syncthreads();
+        const int used = min(kWavesPerGroup, (n + kWave - 1) / kWave);   // n >= 1 when any key is real
+        for (int w = 0; w < used; ++w)
+            groups = (w == 0 && cb == tb) ? sh.lists[0][lane] : wave_merge_desc(groups, sh.lists[w][lane], lane);
+        __syncthreads();   // the next chunk or pass overwrites the records and lists
     }
+    // every top-k entry's key is at least the k-th best group key
+    const uint64_t theta_g = uniform64(lane_key(groups, k - 1));
 
-    sh.lists[wave][lane] = s.list;
+    // ---- 3. re-read the candidate groups; keep the best k entries ----
+    // wavefront w takes group ranks 16w .. 16w + 15; lane j reads run j % 4
+    // (8 consecutive entries, one 16-byte load for bf16) of rank 16w + j / 4
+    const int rank = wave * (kWave / 4) + lane / 4;
+    const uint64_t gk = __shfl(groups, rank);
+    uint32_t w[kGroupElems * (int)sizeof(T) / 4] = {};
+    long long first = 0;
+    const bool mine = rank < k && gk != 0;
+    if (mine) {
+        const long long e0 = key_index(gk);
+        first = (e0 / kTileElems) * kTileElems + (lane % 4) * (kWave * kGroupElems) +
+                (e0 % (kWave * kGroupElems)) / kGroupElems * kGroupElems;
+        load_group<T, VEC>(row, first, V, first + kGroupElems <= (long long)V, w);
+    }
+    uint64_t out = 0, ot = 0;
+#pragma unroll
+    for (int e = 0; e < kGroupElems; ++e) {
+        float val;
+        if constexpr (sizeof(T) == 2)
+            val = (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
+        else
+            val = __uint_as_float(w[e]);
+        const uint64_t key = make_key(val, (uint32_t)(first + e));
+        ot = list_offer(out, (mine && first + e < V && key >= theta_g) ? key : 0, ot, k, lane);
+    }
+    sh.lists[wave][lane] = out;
     __syncthreads();
     if (wave == 0) {
         uint64_t x = sh.lists[0][lane];
 #pragma unroll
-        for (int w = 1; w < kWavesPerGroup; ++w) x = wave_merge_desc(x, sh.lists[w][lane], lane);
+        for (int w2 = 1; w2 < kWavesPerGroup; ++w2) x = wave_merge_desc(x, sh.lists[w2][lane], lane);
         sh.lists[0][lane] = x;
     }
 }
