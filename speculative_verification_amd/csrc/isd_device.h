@@ -24,41 +24,134 @@ __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+// Lane exchanges in the VALU: DPP row operations and the permlane16/32 swaps
+// move data between lanes in a few cycles, where ds_bpermute takes a round
+// trip through the LDS crossbar.  xor_lane<J>(v, lane) is v of lane lane ^ J:
+//   J = 1, 2   quad_perm [1,0,3,2] and [2,3,0,1];
+//   J = 4      row_ror:4 gives lane - 4 (mod 16), row_ror:12 lane + 4;
+//   J = 8      row_ror:8;
+//   J = 16, 32 the permlane swap of odd and even rows (or row pairs): with
+//              both operands v, the first result holds lane - J on the lanes
+//              with bit J set, the second lane + J on the others.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+    static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16 || J == 32, "lane mask");
+    if constexpr (J == 1) {
+        return dpp_u32<0xB1>(v);
+    } else if constexpr (J == 2) {
+        return dpp_u32<0x4E>(v);
+    } else if constexpr (J == 4) {
+        const uint32_t down = dpp_u32<0x124>(v), up = dpp_u32<0x12C>(v);
+        return (lane & 4) ? down : up;
+    } else if constexpr (J == 8) {
+        return dpp_u32<0x128>(v);
+    } else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane(uint64_t v, int lane) {
+    const uint32_t lo = xor_lane<J>((uint32_t)v, lane), hi = xor_lane<J>((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int J>
+__device__ __forceinline__ double xor_lane(double v, int lane) {
+    return __longlong_as_double((long long)xor_lane<J>((uint64_t)__double_as_longlong(v), lane));
+}
+
+template <int J>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+    return __uint_as_float(xor_lane<J>(__float_as_uint(v), lane));
+}
+
+// The same with a mask known only after unrolling.
+template <typename V>
+__device__ __forceinline__ V xor_lane_n(V v, int j, int lane) {
+    switch (j) {
+    case 1: return xor_lane<1>(v, lane);
+    case 2: return xor_lane<2>(v, lane);
+    case 4: return xor_lane<4>(v, lane);
+    case 8: return xor_lane<8>(v, lane);
+    case 16: return xor_lane<16>(v, lane);
+    default: return xor_lane<32>(v, lane);
+    }
+}
+
+// v of lane 63 - lane: row_mirror reverses each row of 16, then rows r and
+// 3 - r (lane ^ 48) are exchanged.
+__device__ __forceinline__ uint64_t reverse_lanes(uint64_t v, int lane) {
+    const uint32_t lo = dpp_u32<0x140>((uint32_t)v), hi = dpp_u32<0x140>((uint32_t)(v >> 32));
+    return xor_lane<16>(xor_lane<32>(((uint64_t)hi << 32) | lo, lane), lane);
+}
+
 // row_ror:n rotates within each row of 16 lanes; four rotations give every
 // lane its row's result, two cross-row exchanges finish the wavefront.  All
 // lanes end with bitwise-identical results.
 __device__ __forceinline__ float wave_max(float v) {
+    const int lane = (int)__lane_id();
     v = fmaxf(v, dpp<0x128>(v));
     v = fmaxf(v, dpp<0x124>(v));
     v = fmaxf(v, dpp<0x122>(v));
     v = fmaxf(v, dpp<0x121>(v));
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
+    v = fmaxf(v, xor_lane<16>(v, lane));
+    v = fmaxf(v, xor_lane<32>(v, lane));
     return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
+    const int lane = (int)__lane_id();
     v += dpp<0x128>(v);
     v += dpp<0x124>(v);
     v += dpp<0x122>(v);
     v += dpp<0x121>(v);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
+    v += xor_lane<16>(v, lane);
+    v += xor_lane<32>(v, lane);
     return v;
 }
 
+// Butterfly sum: every lane ends with the same bits (each exchange adds the
+// same two values in the same order on both lanes of a pair).
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    const int lane = (int)__lane_id();
+    v += xor_lane<32>(v, lane);
+    v += xor_lane<16>(v, lane);
+    v += xor_lane<8>(v, lane);
+    v += xor_lane<4>(v, lane);
+    v += xor_lane<2>(v, lane);
+    v += xor_lane<1>(v, lane);
     return v;
 }
 
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)u), hi = dpp_u32<CTRL, ROWS>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sum over the lanes: row_shr:1,2,4,8 scan each row of 16
+// (lanes with no source read 0), then row_bcast:15 adds row 0's total to
+// row 1 and row 2's to row 3, and row_bcast:31 adds the total of rows 0-1 to
+// rows 2-3.
 __device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        double n = __shfl_up(v, o);
-        if (lane >= o) v += n;
-    }
+    (void)lane;
+    v += dpp_d<0x111>(v);
+    v += dpp_d<0x112>(v);
+    v += dpp_d<0x114>(v);
+    v += dpp_d<0x118>(v);
+    v += dpp_d<0x142, 0xA>(v);
+    v += dpp_d<0x143, 0xC>(v);
     return v;
 }
 
@@ -303,8 +396,9 @@ __device__ __forceinline__ bool arg_better(float v, int i, float bv, int bi) {
 __device__ __forceinline__ void wave_argmax(float &bv, int &bi) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
+        const int lane = (int)__lane_id();
+        const float ov = xor_lane_n(bv, o, lane);
+        const int oi = (int)xor_lane_n((uint32_t)bi, o, lane);
         if (arg_better(ov, oi, bv, bi)) {
             bv = ov;
             bi = oi;

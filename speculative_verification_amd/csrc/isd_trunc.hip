@@ -75,7 +75,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
     for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t y = __shfl_xor(x, j);
+            const uint64_t y = xor_lane_n(x, j, lane);
             const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
             x = keep_max ? umax64(x, y) : umin64(x, y);
         }
@@ -87,10 +87,10 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
 // the lane-wise max of one list and the other reversed is bitonic and holds
 // them; a bitonic merge sorts it.
 __device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t b, int lane) {
-    uint64_t x = umax64(a, __shfl(b, kWave - 1 - lane));
+    uint64_t x = umax64(a, reverse_lanes(b, lane));
 #pragma unroll
     for (int j = kWave / 2; j > 0; j >>= 1) {
-        const uint64_t y = __shfl_xor(x, j);
+        const uint64_t y = xor_lane_n(x, j, lane);
         x = ((lane & j) == 0) ? umax64(x, y) : umin64(x, y);
     }
     return x;
@@ -192,10 +192,10 @@ __device__ __forceinline__ uint64_t record_key(const TruncShared<T> &sh, int cb,
     return ((uint64_t)o << 32) | (uint64_t)(uint32_t)~idx;
 }
 
-// Top k keys of tiles [tb, te) of `row`, merged over the workgroup into
-// sh.lists[0] (largest first; 0 past the end).  All threads call it.
+// Top k keys of tiles [tb, te) of `row`, largest first (0 past the end),
+// returned to wavefront 0 (the others get 0).  All threads call it.
 template <typename T, bool VEC>
-__device__ __forceinline__ void select_segment(const T *__restrict__ row, int tb, int te, int V,
+__device__ __forceinline__ uint64_t select_segment(const T *__restrict__ row, int tb, int te, int V,
                                                int k, int wave, int lane, TruncShared<T> &sh) {
     uint64_t groups = 0;   // the best group keys of the chunks so far (same in every wavefront)
     for (int cb = tb; cb < te; cb += kMaxSegTiles) {
@@ -291,12 +291,13 @@ __device__ __forceinline__ void select_segment(const T *__restrict__ row, int tb
     }
     sh.lists[wave][lane] = out;
     __syncthreads();
+    uint64_t x = 0;
     if (wave == 0) {
-        uint64_t x = sh.lists[0][lane];
+        x = out;
 #pragma unroll
         for (int w2 = 1; w2 < kWavesPerGroup; ++w2) x = wave_merge_desc(x, sh.lists[w2][lane], lane);
-        sh.lists[0][lane] = x;
     }
+    return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -327,7 +328,7 @@ __device__ __forceinline__ RowLaw truncated_law(uint64_t top, int k, double temp
         const double W = wave_sum_d(w);
         const double pi = W > 0.0 ? w / W : 0.0;
         const double incl = wave_incl_scan_d(pi, lane);
-        double before = __shfl_up(incl, 1);
+        double before = dpp_d<0x138>(incl);   // wave_shr:1
         if (lane == 0) before = 0.0;
         keep = real && before < top_p;
     }
@@ -519,7 +520,9 @@ __device__ __forceinline__ long long trunc_row_offset(const StepArgs &a, int c, 
 }
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void trunc_kernel(StepArgs a) {
+// Five waves per SIMD (at most 96 VGPRs): a wavefront finishing a row leaves
+// room for the next item's workgroup on its SIMD.
+__global__ __launch_bounds__(kThreads, 5) void trunc_kernel(StepArgs a) {
     __shared__ TruncShared<T> sh;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
@@ -581,14 +584,18 @@ __global__ __launch_bounds__(kThreads) void trunc_kernel(StepArgs a) {
     // ---- this segment's top k ----
     const int tb = seg * a.tpst;
     const int te = min(a.tiles_row, tb + a.tpst);
-    select_segment<T, VEC>(row, tb, te, a.V, k, wave, lane, sh);
-    if (wave == 0 && lane < k) st64(&seg_keys(a, rowid, seg)[lane], sh.lists[0][lane]);
-    if (!arrive(counter(a.tws.row_cnt, rowid), (uint32_t)a.St, &sh.flag)) return;
-    if (wave != 0) return;
+    const uint64_t seg_top = select_segment<T, VEC>(row, tb, te, a.V, k, wave, lane, sh);
 
     // ---- the row's top k, truncated law ----
     uint64_t top = 0;
-    {
+    if (a.St == 1) {
+        // the item holds the whole row
+        if (wave != 0) return;
+        top = lane < k ? seg_top : 0;
+    } else {
+        if (wave == 0 && lane < k) st64(&seg_keys(a, rowid, seg)[lane], seg_top);
+        if (!arrive(counter(a.tws.row_cnt, rowid), (uint32_t)a.St, &sh.flag)) return;
+        if (wave != 0) return;
         uint64_t rec[kMaxTruncSegments];
 #pragma unroll
         for (int s = 0; s < kMaxTruncSegments; ++s)
