@@ -368,25 +368,26 @@ __device__ __forceinline__ uint64_t ld_pair(const void *r) {
     return ld64(static_cast<const uint64_t *>(r));
 }
 
-// Completes this workgroup's share of a unit counted by `counter` (total
-// arrivals `total`).  All threads call it after their record stores; it
-// returns, to every thread, whether this was the last arrival.  The last one
-// resets the counter for the next launch.
-__device__ __forceinline__ bool arrive(uint32_t *counter, uint32_t total, int *s_flag) {
+// Counts the workgroup's arrival on `counter` (total arrivals `total`) once
+// every wavefront's record stores have completed, and returns true, on
+// wavefront 0 only, to the last arrival, which also resets the counter.  The
+// other wavefronts return false at once, without waiting for the count: every
+// finisher runs on wavefront 0.
+__device__ __forceinline__ bool arrive(uint32_t *counter, uint32_t total) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (threadIdx.x >= kWave) return false;
+    int last = 0;
     if (threadIdx.x == 0) {
         const uint32_t prev =
             __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = prev + 1 == total;
+        last = prev + 1 == total;
         if (last) st32(counter, 0u);
-        *s_flag = last ? 1 : 0;
     }
-    __syncthreads();
-    const bool last = *s_flag != 0;
+    last = __builtin_amdgcn_readfirstlane(last);
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return last;
+    return last != 0;
 }
 
 __device__ __forceinline__ bool arg_better(float v, int i, float bv, int bi) {

@@ -319,7 +319,6 @@ __device__ __forceinline__ long long row_offset(const StepArgs &a, int c, int k)
 }
 
 struct Shared {
-    int flag;
     float refs[kWavesPerGroup];
     double sums[kWavesPerGroup];
     float vals[kWavesPerGroup];
@@ -347,19 +346,23 @@ __device__ __forceinline__ void decide(const StepArgs &a, int c, int lane) {
         double sp = 0.0, sq = 0.0;
         double px = 0.0, qx = 0.0;
         if (valid) {
+            // the logits at x_k first: their loads overlap the record loads
+            float lp = 0.0f, lq = 0.0f;
+            if (!bad) {
+                const long long off = row_offset(a, c, kk) + xk;
+                lp = load_value<T>(static_cast<const T *>(a.p), off);
+                if (!a.q_onehot) lq = load_value<T>(static_cast<const T *>(a.q), off);
+            }
             take_segrecs(&a.ws.seg[((size_t)c * L + kk) * a.S], a.S, cp, sp);
             if (!a.q_onehot) take_segrecs(&a.ws.seg[((size_t)CL + (size_t)c * L + kk) * a.S], a.S, cq, sq);
             if (sp <= 0.0 || (!a.q_onehot && sq <= 0.0)) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
             if (!bad) {
-                const long long off = row_offset(a, c, kk) + xk;
-                const float lp = load_value<T>(static_cast<const T *>(a.p), off);
                 const double k2 = (double)a.k2;
                 if (sp > 0.0) px = exp2((double)lp * k2 - (double)cp) / sp;
                 if (a.q_onehot) {
                     qx = 1.0;   // the argmax pick's own law
-                } else {
-                    const float lq = load_value<T>(static_cast<const T *>(a.q), off);
-                    if (sq > 0.0) qx = exp2((double)lq * k2 - (double)cq) / sq;
+                } else if (sq > 0.0) {
+                    qx = exp2((double)lq * k2 - (double)cq) / sq;
                 }
             }
         }
@@ -541,7 +544,7 @@ __device__ __forceinline__ void pq_item(const StepArgs &a, int t, Shared &sh, in
         }
     }
 
-    if (!arrive(counter(a.ws.seq_cnt, c), (uint32_t)per_seq, &sh.flag)) return;
+    if (!arrive(counter(a.ws.seq_cnt, c), (uint32_t)per_seq)) return;
     if (wave == 0) decide<T, MODE>(a, c, lane);
 }
 
@@ -571,7 +574,7 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
             const float ts = wave_sum(s);
             if (lane == 0) st_pair(&tr[tile], pack2(sm.ref, ts));
         });
-        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.Sq, &sh.flag)) return;
+        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.Sq)) return;
         if (wave != 0) return;
 
         // ---- inverse-CDF draw over the whole row ----
@@ -598,6 +601,8 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
         };
         int token = 0;
         double S = 0.0;
+        float lv = 0.0f;     // logit of the drawn token
+        bool have_lv = false;
         if (cr == kNegInf) {
             if (lane == 0) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
         } else {
@@ -628,13 +633,27 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
             };
             const long long tok = search_tile(weight, tile, lane, before, tile_target);
             token = tok < 0 ? 0 : (int)tok;
+            if constexpr (sizeof(T) == 2) {
+                if (tok >= 0) {
+                    // the token lies in the crossing tile: take its logit from
+                    // the lane that holds it instead of reading it again (a
+                    // wave-uniform index into the lane's 16 words)
+                    const int off = (int)(tok - (long long)tile * kTileElems);
+                    const int owner = (off % (kWave * kGroupElems)) / kGroupElems;
+                    const int pos = off / (kWave * kGroupElems) * kGroupElems + off % kGroupElems;
+                    const uint32_t word = raw.w[pos >> 1];
+                    const float mine = __uint_as_float((pos & 1) ? (word & 0xFFFF0000u) : (word << 16));
+                    lv = __shfl(mine, owner);
+                    have_lv = true;
+                }
+            }
         }
         // the tile masses are consumed: return them to zero
         for (int t = lane; t < a.tiles_row; t += kWave) st_pair(&tr[t], 0);
         if (lane == 0) {
             a.next_tokens[rowid] = token;
             if (a.qnext_x) {
-                const float lv = load_value<T>(row, token);
+                if (S > 0.0 && !have_lv) lv = load_value<T>(row, token);
                 a.qnext_x[rowid] =
                     S > 0.0 ? (float)(exp2((double)lv * (double)a.k2 - (double)cr) / S) : 0.0f;
             }
@@ -662,7 +681,7 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
                 }
             st_pair(&recs[seg], pack2(v, i));
         }
-        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.Sq, &sh.flag)) return;
+        if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.Sq)) return;
         if (threadIdx.x == 0) {
             a.next_tokens[rowid] = take_argrecs(recs, a.Sq);
             if (a.qnext_x) a.qnext_x[rowid] = 1.0f;
@@ -878,7 +897,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         });
     }
 
-    if (!arrive(counter(a.ws.res_cnt, c), (uint32_t)a.r_blk, &sh.flag)) return;
+    if (!arrive(counter(a.ws.res_cnt, c), (uint32_t)a.r_blk)) return;
     if (wave != 0) return;
     if (j < L && a.sampler) {
         const int tok = gumbel_finish(a.ws.garg + (size_t)c * kMaxResidSegments * 2, a.Sr, lane);

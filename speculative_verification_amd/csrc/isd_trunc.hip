@@ -123,7 +123,6 @@ constexpr int kMaxCand = kMaxSegTiles / kWavesPerGroup * kMaxTopK;
 
 template <typename T>
 struct TruncShared {
-    int flag;
     int ncand;
     uint64_t lists[kWavesPerGroup][kWave];
     uint32_t gord[kMaxSegTiles * kWave];   // order bits of each group's best value (0: empty)
@@ -594,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 5) void trunc_kernel(StepArgs a) {
         top = lane < k ? seg_top : 0;
     } else {
         if (wave == 0 && lane < k) st64(&seg_keys(a, rowid, seg)[lane], seg_top);
-        if (!arrive(counter(a.tws.row_cnt, rowid), (uint32_t)a.St, &sh.flag)) return;
+        if (!arrive(counter(a.tws.row_cnt, rowid), (uint32_t)a.St)) return;
         if (wave != 0) return;
         uint64_t rec[kMaxTruncSegments];
 #pragma unroll

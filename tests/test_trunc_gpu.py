@@ -96,21 +96,38 @@ def test_truncated_ragged_and_small(isd, V, dtype):
         _case(isd, cfg, 950 + step, 50, 0.9, f"V={V} {dtype} step {step}")
 
 
+def _coarse(d):
+    """Logits rounded to a grid of 0.5 (frequent ties), with one constant row."""
+    from isd_inputs import f32_to_bf16_bits
+    for key in ("p", "q", "qn"):
+        v = O.decode_logits(d[key], "bf16")
+        v = np.round(v * 2) / 2
+        v[0, 1] = 1.0
+        d[key] = f32_to_bf16_bits(v.astype(np.float32))
+
+
 def test_truncated_ties_rank_lower_index_first(isd):
     """Logits rounded to a coarse grid tie often: ranks go to the lower index;
     constant rows keep their first k entries."""
     cfg = dict(CONFIGS[2], C=6, L=4, V=6000)
-
-    def coarse(d):
-        for key in ("p", "q", "qn"):
-            v = O.decode_logits(d[key], "bf16")
-            v = np.round(v * 2) / 2
-            v[0, 1] = 1.0                       # a constant row
-            from isd_inputs import f32_to_bf16_bits
-            d[key] = f32_to_bf16_bits(v.astype(np.float32))
-
     for step in range(2):
-        _case(isd, cfg, 970 + step, 16, 0.9, f"ties step {step}", mutate=coarse)
+        _case(isd, cfg, 970 + step, 16, 0.9, f"ties step {step}", mutate=_coarse)
+
+
+@pytest.mark.parametrize("segments,V", [(1, 200000), (1, 200003), (2, 200000)])
+def test_truncated_long_rows(isd, segments, V):
+    """Rows of 98 tiles.  In one segment the selection records its group
+    maxima in two LDS chunks (80 + 18 tiles) and carries the best group keys
+    across them; two segments take one chunk each.  V = 200003 takes the
+    scalar-load path.  Random and tie-heavy logits."""
+    cfg = dict(CONFIGS[2], C=2, L=3, V=V)
+    isd.set_trunc_tuning(segments)
+    try:
+        for step in range(2):
+            _case(isd, cfg, 1010 + step, 50, 0.95, f"V={V} St={segments} step {step}")
+        _case(isd, cfg, 1020, 64, 1.0, f"V={V} St={segments} ties", mutate=_coarse)
+    finally:
+        isd.set_trunc_tuning(0)
 
 
 @pytest.mark.parametrize("variant", [dict(q_onehot=True), dict(relax=0.5),
