@@ -155,6 +155,17 @@ __device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
     return v;
 }
 
+// Inclusive prefix sum of 32-bit counts over the lanes (same DPP pattern).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+    v += dpp_u32<0x111>(v);
+    v += dpp_u32<0x112>(v);
+    v += dpp_u32<0x114>(v);
+    v += dpp_u32<0x118>(v);
+    v += dpp_u32<0x142, 0xA>(v);
+    v += dpp_u32<0x143, 0xC>(v);
+    return v;
+}
+
 __device__ __forceinline__ int wave_first(unsigned long long mask) {
     return __ffsll((long long)mask) - 1;
 }

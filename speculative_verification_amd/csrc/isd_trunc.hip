@@ -108,9 +108,10 @@ __device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t b, int 
 //      order bits of its value and its position in the lane (32 + 8 bits),
 //      nothing else, so the stream never waits on selection work;
 //   2. from LDS: a threshold from the column maxima (below) leaves few
-//      records, which are compacted, sorted and merged; ranks 0..k-1 of the
-//      result are the candidate groups;
-//   3. re-read the candidate groups (k * 32 entries, at most one tile's
+//      records, which are compacted; when more than 64 remain (or the
+//      segment spans several chunks) they are sorted and merged, and ranks
+//      0..k-1 of the result are the candidate groups;
+//   3. re-read the candidate groups (at most 64 * 32 entries, one tile's
 //      worth) and keep the best k of their entries.
 // Passes 1 and 2 run over chunks of kMaxSegTiles tiles, so LDS bounds no
 // segment length.
@@ -136,49 +137,11 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Whole-wavefront shift by one lane (lane l gets lane l - 1; lane 0 keeps its
-// own value, which the caller never uses): DPP wave_shr:1.
-__device__ __forceinline__ uint64_t wave_shr1(uint64_t v) {
-    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, 0x138, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), 0x138,
-                                               0xF, 0xF, false);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
 // Key held by lane `l` (wave-uniform l).
 __device__ __forceinline__ uint64_t lane_key(uint64_t v, int l) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
     return ((uint64_t)hi << 32) | lo;
-}
-
-// Inserts a wave-uniform key into the sorted list (largest first); keys are
-// unique, so the lanes holding larger keys are exactly lanes 0..pos-1.
-__device__ __forceinline__ uint64_t list_insert(uint64_t list, uint64_t key, int lane) {
-    const int pos = __popcll(__ballot(list > key));
-    const uint64_t up = wave_shr1(list);
-    return lane < pos ? list : (lane == pos ? key : up);
-}
-
-// Offers one key per lane (0: none) to the sorted list whose threshold is
-// theta (the key of rank k-1, or 0): a batch with many candidates is sorted
-// and merged, a few are inserted one by one.  Returns the new threshold.
-__device__ __forceinline__ uint64_t list_offer(uint64_t &list, uint64_t key, uint64_t theta,
-                                               int k, int lane) {
-    const unsigned long long cand = __ballot(key > theta);
-    if (!cand) return theta;
-    if (__popcll(cand) > 8) {
-        list = wave_merge_desc(list, wave_sort_desc(key > theta ? key : 0, lane), lane);
-    } else {
-        for (unsigned long long m = cand; m; m &= m - 1) {
-            const uint64_t kk = lane_key(key, __ffsll((long long)m) - 1);
-            if (kk > theta) {
-                list = list_insert(list, kk, lane);
-                theta = umax64(theta, uniform64(lane_key(list, k - 1)));
-            }
-        }
-    }
-    return umax64(theta, uniform64(lane_key(list, k - 1)));
 }
 
 // Key of the group record at position `at` of the chunk starting at tile cb
@@ -191,15 +154,55 @@ __device__ __forceinline__ uint64_t record_key(const TruncShared<T> &sh, int cb,
     return ((uint64_t)o << 32) | (uint64_t)(uint32_t)~idx;
 }
 
+// Sorted list (largest first) of up to 64 keys, N offered per lane
+// (key(e) for e < N; 0 is not offered): the candidates are packed through
+// this wavefront's row of `stage` and sorted once; more than 64 are taken
+// 64 at a time and merged.  Uniform control flow.
+template <int N, typename Key>
+__device__ __forceinline__ uint64_t gather_sorted(Key &&key, uint64_t *stage, int lane) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) cnt += key(e) != 0 ? 1u : 0u;
+    const uint32_t incl = wave_incl_scan_u32(cnt);
+    const int total = __builtin_amdgcn_readlane((int)incl, kWave - 1);
+    uint64_t list = 0;
+    for (int b0 = 0; b0 < total; b0 += kWave) {
+        // candidates b0 .. b0 + 63 of the wavefront's order (lane, then entry)
+        int slot = (int)(incl - cnt) - b0;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            const uint64_t ke = key(e);
+            if (ke != 0) {
+                if (slot >= 0 && slot < kWave) stage[slot] = ke;
+                ++slot;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint64_t sorted = wave_sort_desc(b0 + lane < total ? stage[lane] : 0, lane);
+        list = b0 == 0 ? sorted : wave_merge_desc(list, sorted, lane);
+        __builtin_amdgcn_wave_barrier();   // the stage is rewritten next round
+    }
+    return list;
+}
+
+constexpr int kColRecs = kMaxSegTiles / kWavesPerGroup;   // records per column and chunk
+
 // Top k keys of tiles [tb, te) of `row`, largest first (0 past the end),
 // returned to wavefront 0 (the others get 0).  All threads call it.
 template <typename T, bool VEC>
 __device__ __forceinline__ uint64_t select_segment(const T *__restrict__ row, int tb, int te, int V,
                                                int k, int wave, int lane, TruncShared<T> &sh) {
     uint64_t groups = 0;   // the best group keys of the chunks so far (same in every wavefront)
+    bool direct = false;   // one chunk with at most 64 candidate records: re-read them all
+    uint64_t thr = 0;      // pass 3 keeps entries whose key reaches it
+    int ngroups = 0;
     for (int cb = tb; cb < te; cb += kMaxSegTiles) {
         const int ce = min(te, cb + kMaxSegTiles);
-        // ---- 1. stream: each group's best entry into LDS ----
+        // ---- 1. stream: each group's best entry into LDS; the column maximum ----
+        // A thread's records (lane `lane` of its wavefront's tiles) form a column.
+        uint64_t colmax = 0;
         stream_row<T, VEC>(row, cb, ce, V, wave, lane, [&](const TileRaw<T> &r, int tile) {
             float v[kLaneElems];
             unpack<T>(r, v);
@@ -207,46 +210,66 @@ __device__ __forceinline__ uint64_t select_segment(const T *__restrict__ row, in
             int fi = 0;   // first position holding the maximum: the lowest index among equals
 #pragma unroll
             for (int i = kLaneElems - 1; i >= 0; --i) fi = (v[i] == vmax) ? i : fi;
+            const long long idx = elem_index(tile, lane, fi);
+            const uint32_t o = idx < V ? ord_bits(vmax) : 0u;
             const int at = (tile - cb) * kWave + lane;
-            sh.gord[at] = elem_index(tile, lane, fi) < V ? ord_bits(vmax) : 0u;
+            sh.gord[at] = o;
             sh.gpos[at] = (uint8_t)fi;
+            if (o) colmax = umax64(colmax, ((uint64_t)o << 32) | (uint64_t)(uint32_t)~(uint32_t)idx);
         });
         if (threadIdx.x == 0) sh.ncand = 0;
-        __syncthreads();
-
-        // ---- 2. the k best group keys ----
-        // A thread's records (lane `lane` of its wavefront's tiles) form a
-        // column.  theta0, the k-th best of the column maxima and of the
-        // earlier chunks' best keys, is reached by at least k keys, so every
-        // top-k key reaches it; and at most k columns hold a key that does.
-        uint64_t colmax = 0;
-        for (int t = cb + wave; t < ce; t += kWavesPerGroup)
-            colmax = umax64(colmax, record_key(sh, cb, (t - cb) * kWave + lane));
         sh.lists[wave][lane] = wave_sort_desc(colmax, lane);
         __syncthreads();
+
+        // ---- 2. the candidate groups ----
+        // theta0, the k-th best of the column maxima and of the earlier
+        // chunks' best keys, is reached by at least k keys, so every top-k key
+        // reaches it; and at most k columns hold a key that does.
         uint64_t m = sh.lists[0][lane];
 #pragma unroll
         for (int w = 1; w < kWavesPerGroup; ++w) m = wave_merge_desc(m, sh.lists[w][lane], lane);
         if (cb != tb) m = wave_merge_desc(m, groups, lane);
         const uint64_t theta0 = uniform64(lane_key(m, k - 1));
-        // list the chunk's records that reach theta0 (a wavefront at a time)
-        const bool col = colmax != 0 && colmax >= theta0;
-        if (__ballot(col)) {
-            for (int t = cb + wave; t < ce; t += kWavesPerGroup) {
-                const int at = (t - cb) * kWave + lane;
-                const uint64_t key = col ? record_key(sh, cb, at) : 0;
-                const bool c = key != 0 && key >= theta0;
-                const unsigned long long bal = __ballot(c);
-                if (!bal) continue;
-                int base = 0;
-                if (lane == 0) base = atomicAdd(&sh.ncand, __popcll(bal));
-                base = __builtin_amdgcn_readfirstlane(base);
-                if (c) sh.cand[base + __popcll(bal & ((1ull << lane) - 1))] = (uint16_t)at;
+        // the chunk's records that reach theta0, packed into sh.cand
+        uint32_t cmask = 0;
+        if (colmax != 0 && colmax >= theta0) {
+            // order bits first; the position only where they equal theta0's
+            const uint32_t tord = (uint32_t)(theta0 >> 32);
+#pragma unroll
+            for (int i = 0; i < kColRecs; ++i) {
+                const int t = cb + wave + kWavesPerGroup * i;
+                if (t < ce) {
+                    const int at = (t - cb) * kWave + lane;
+                    const uint32_t o = sh.gord[at];
+                    if (o > tord || (o == tord && o != 0u && record_key(sh, cb, at) >= theta0))
+                        cmask |= 1u << i;
+                }
+            }
+        }
+        const uint32_t cnt = (uint32_t)__popc(cmask);
+        const uint32_t incl = wave_incl_scan_u32(cnt);
+        const int wtotal = __builtin_amdgcn_readlane((int)incl, kWave - 1);
+        if (wtotal > 0) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&sh.ncand, wtotal);
+            base = __builtin_amdgcn_readfirstlane(base) + (int)(incl - cnt);
+            for (uint32_t mm = cmask; mm; mm &= mm - 1) {
+                const int i = __ffs((int)mm) - 1;
+                sh.cand[base++] = (uint16_t)((wave + kWavesPerGroup * i) * kWave + lane);
             }
         }
         __syncthreads();
-        // sort them, 64 per wavefront at a time, and merge with the earlier best
         const int n = sh.ncand;
+        if (cb == tb && ce == te && n <= kWavesPerGroup * (kWave / 4)) {
+            // Every top-k entry reaches theta0 and lies in a group whose best
+            // key does: pass 3 can take all n candidate groups as they are,
+            // without sorting them first.
+            direct = true;
+            thr = theta0;
+            ngroups = n;
+            break;
+        }
+        // sort them, 64 per wavefront at a time, and merge with the earlier best
         uint64_t wl = 0;
         for (int b = wave * kWave; b < n; b += kThreads) {
             const uint64_t sorted =
@@ -260,34 +283,47 @@ __device__ __forceinline__ uint64_t select_segment(const T *__restrict__ row, in
             groups = (w == 0 && cb == tb) ? sh.lists[0][lane] : wave_merge_desc(groups, sh.lists[w][lane], lane);
         __syncthreads();   // the next chunk or pass overwrites the records and lists
     }
-    // every top-k entry's key is at least the k-th best group key
-    const uint64_t theta_g = uniform64(lane_key(groups, k - 1));
 
     // ---- 3. re-read the candidate groups; keep the best k entries ----
-    // wavefront w takes group ranks 16w .. 16w + 15; lane j reads run j % 4
-    // (8 consecutive entries, one 16-byte load for bf16) of rank 16w + j / 4
-    const int rank = wave * (kWave / 4) + lane / 4;
-    const uint64_t gk = __shfl(groups, rank);
+    // wavefront w takes candidate groups 16w .. 16w + 15; lane j reads run
+    // j % 4 (8 consecutive entries, one 16-byte load for bf16) of group 16w + j / 4
+    const int gi = wave * (kWave / 4) + lane / 4;
+    int gtile = 0, glane = 0;
+    bool mine;
+    if (direct) {
+        mine = gi < ngroups;
+        if (mine) {
+            const int at = sh.cand[gi];
+            gtile = tb + at / kWave;
+            glane = at % kWave;
+        }
+    } else {
+        // the k best group keys; every top-k entry's key is at least the k-th
+        thr = uniform64(lane_key(groups, k - 1));
+        const uint64_t gk = __shfl(groups, gi);
+        mine = gi < k && gk != 0;
+        if (mine) {
+            const uint32_t e0 = key_index(gk);
+            gtile = (int)(e0 / kTileElems);
+            glane = (int)(e0 % (kWave * kGroupElems)) / kGroupElems;
+        }
+    }
     uint32_t w[kGroupElems * (int)sizeof(T) / 4] = {};
     long long first = 0;
-    const bool mine = rank < k && gk != 0;
     if (mine) {
-        const long long e0 = key_index(gk);
-        first = (e0 / kTileElems) * kTileElems + (lane % 4) * (kWave * kGroupElems) +
-                (e0 % (kWave * kGroupElems)) / kGroupElems * kGroupElems;
+        first = (long long)gtile * kTileElems + (lane % 4) * (kWave * kGroupElems) + glane * kGroupElems;
         load_group<T, VEC>(row, first, V, first + kGroupElems <= (long long)V, w);
     }
-    uint64_t out = 0, ot = 0;
-#pragma unroll
-    for (int e = 0; e < kGroupElems; ++e) {
+    auto entry_key = [&](int e) -> uint64_t {
         float val;
         if constexpr (sizeof(T) == 2)
             val = (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
         else
             val = __uint_as_float(w[e]);
         const uint64_t key = make_key(val, (uint32_t)(first + e));
-        ot = list_offer(out, (mine && first + e < V && key >= theta_g) ? key : 0, ot, k, lane);
-    }
+        return (mine && first + e < V && key >= thr) ? key : 0;
+    };
+    const uint64_t out = gather_sorted<kGroupElems>(entry_key, sh.lists[wave], lane);   // lists are free here
     sh.lists[wave][lane] = out;
     __syncthreads();
     uint64_t x = 0;
@@ -519,9 +555,7 @@ __device__ __forceinline__ long long trunc_row_offset(const StepArgs &a, int c, 
 }
 
 template <typename T, bool VEC>
-// Five waves per SIMD (at most 96 VGPRs): a wavefront finishing a row leaves
-// room for the next item's workgroup on its SIMD.
-__global__ __launch_bounds__(kThreads, 5) void trunc_kernel(StepArgs a) {
+__global__ __launch_bounds__(kThreads) void trunc_kernel(StepArgs a) {
     __shared__ TruncShared<T> sh;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
