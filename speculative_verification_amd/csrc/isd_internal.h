@@ -36,7 +36,8 @@ constexpr uint32_t kErrWaitExpired = 1u << 2;  // a cross-workgroup wait gave up
 // Workspace records.  Counters and flags return to zero at the end of the
 // launch that uses them.
 struct Control {               // 256 B at offset 0
-    uint32_t reserved[2];
+    uint32_t ticket;           // step items taken past n_static (reset by the last taker)
+    uint32_t reserved;
     uint32_t seq_done;         // sequences whose decision is done (alpha mean)
     uint32_t error;            // kErr* bits, cleared by isd_check_device_error
     uint32_t pad[60];
@@ -143,6 +144,7 @@ struct StepArgs {
     int q_blk;                 // mask-row items per sequence (L*Sq or 0)
     int r_blk;                 // residual items per sequence (Sr or 0)
     int n_items;
+    int n_static;              // items taken by workgroup index; the rest by ticket
     int verify_outputs;        // write tokens / counts (0: alpha only)
     int order;                 // 0: per sequence [mask rows, residual]; 1: all mask rows first
     uint32_t spin_limit;

@@ -319,6 +319,7 @@ __device__ __forceinline__ long long row_offset(const StepArgs &a, int c, int k)
 }
 
 struct Shared {
+    int ticket;
     float refs[kWavesPerGroup];
     double sums[kWavesPerGroup];
     float vals[kWavesPerGroup];
@@ -966,7 +967,23 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     __shared__ Shared sh;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    const int t = (int)blockIdx.x;
+    int t = (int)blockIdx.x;
+    if (t >= a.n_static) {
+        // The last items go to whichever workgroups reach them first, so that
+        // an XCD running ahead takes more of them: each takes a ticket from a
+        // launch-wide counter.  The grid holds spare workgroups, which find
+        // the items gone and exit; the last one to take a ticket re-arms the
+        // counter.
+        if (threadIdx.x == 0) {
+            const uint32_t k =
+                __hip_atomic_fetch_add(&a.ws.ctl->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (k + 1 == gridDim.x - (uint32_t)a.n_static) st32(&a.ws.ctl->ticket, 0u);
+            sh.ticket = a.n_static + (int)k;
+        }
+        __syncthreads();
+        t = sh.ticket;
+        if (t >= a.n_items) return;
+    }
 
     if (t < a.n_pq) {
         pq_item<T, VEC, MODE>(a, t, sh, wave, lane);
@@ -1000,28 +1017,35 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
 
 }  // namespace
 
-hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStream_t stream) {
-    const dim3 grid((unsigned)a.n_items), block(kThreads);
-#define ISD_LAUNCH(T, V, M) hipLaunchKernelGGL((step_kernel<T, V, M>), grid, block, 0, stream, a)
-    if (dtype == kBf16) {
-        if (mode == kSample) {
-            if (vec) ISD_LAUNCH(uint16_t, true, kSample);
-            else ISD_LAUNCH(uint16_t, false, kSample);
-        } else {
-            if (vec) ISD_LAUNCH(uint16_t, true, kGreedy);
-            else ISD_LAUNCH(uint16_t, false, kGreedy);
-        }
-    } else {
-        if (mode == kSample) {
-            if (vec) ISD_LAUNCH(float, true, kSample);
-            else ISD_LAUNCH(float, false, kSample);
-        } else {
-            if (vec) ISD_LAUNCH(float, true, kGreedy);
-            else ISD_LAUNCH(float, false, kGreedy);
-        }
-    }
-#undef ISD_LAUNCH
+// Items at the end of the launch that take tickets, and spare workgroups in
+// percent of them.
+constexpr int kTicketItems = 512;
+constexpr int kSpareGroupsPct = 50;
+
+template <typename T, bool VEC, int MODE>
+hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
+    // Items that wait (residual items wait for their sequence's decision) wait
+    // only on verify items, which take their items by index and never wait;
+    // each XCD dispatches its workgroups in index order, so every verify item
+    // is dispatched before any ticket is taken on its XCD, and every wait ends.
+    StepArgs b = a;
+    const int dyn = min(kTicketItems, a.n_items - a.n_pq);
+    b.n_static = a.n_items - max(dyn, 0);
+    long long grid = a.n_items;
+    if (dyn > 0) grid += ((long long)dyn * kSpareGroupsPct + 99) / 100;
+    hipLaunchKernelGGL((step_kernel<T, VEC, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
     return hipGetLastError();
+}
+
+hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStream_t stream) {
+    if (dtype == kBf16) {
+        if (mode == kSample)
+            return vec ? launch_one<uint16_t, true, kSample>(a, stream) : launch_one<uint16_t, false, kSample>(a, stream);
+        return vec ? launch_one<uint16_t, true, kGreedy>(a, stream) : launch_one<uint16_t, false, kGreedy>(a, stream);
+    }
+    if (mode == kSample)
+        return vec ? launch_one<float, true, kSample>(a, stream) : launch_one<float, false, kSample>(a, stream);
+    return vec ? launch_one<float, true, kGreedy>(a, stream) : launch_one<float, false, kGreedy>(a, stream);
 }
 
 }  // namespace isd
