@@ -126,8 +126,12 @@ template <typename T>
 struct TruncShared {
     int ncand;
     uint64_t lists[kWavesPerGroup][kWave];
-    uint32_t gord[kMaxSegTiles * kWave];   // order bits of each group's best value (0: empty)
-    uint8_t gpos[kMaxSegTiles * kWave];    // its position among the lane's 32 entries
+    // Each group's record (0: empty group): the order bits of its best value
+    // and that entry's position among the lane's 32.  For bf16 the low 16
+    // order bits follow from the sign, so the position takes their place; for
+    // fp32 it has an array of its own.
+    uint32_t grec[kMaxSegTiles * kWave];
+    uint8_t gpos[sizeof(T) == 2 ? 1 : kMaxSegTiles * kWave];
     uint16_t cand[kMaxCand];               // records of a chunk that reach the threshold
 };
 
@@ -144,14 +148,38 @@ __device__ __forceinline__ uint64_t lane_key(uint64_t v, int l) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+template <typename T>
+__device__ __forceinline__ void put_record(TruncShared<T> &sh, int at, uint32_t ord, int pos) {
+    if constexpr (sizeof(T) == 2) {
+        sh.grec[at] = ord ? (ord & 0xFFFF0000u) | (uint32_t)pos : 0u;
+    } else {
+        sh.grec[at] = ord;
+        sh.gpos[at] = (uint8_t)pos;
+    }
+}
+
+// Order bits of a record (0 for an empty group).  A bf16 value's order bits
+// end in 0x0000 when it is positive and 0xFFFF when it is negative; no bf16
+// value has order bits that start 0x0000.
+template <typename T>
+__device__ __forceinline__ uint32_t record_ord(uint32_t rec) {
+    if constexpr (sizeof(T) == 2) {
+        if (rec == 0u) return 0u;
+        return (rec & 0xFFFF0000u) | ((rec & 0x80000000u) ? 0u : 0xFFFFu);
+    } else {
+        return rec;
+    }
+}
+
 // Key of the group record at position `at` of the chunk starting at tile cb
 // (0 for an empty group).
 template <typename T>
 __device__ __forceinline__ uint64_t record_key(const TruncShared<T> &sh, int cb, int at) {
-    const uint32_t o = sh.gord[at];
-    if (o == 0u) return 0;
-    const uint32_t idx = (uint32_t)elem_index(cb + at / kWave, at % kWave, sh.gpos[at]);
-    return ((uint64_t)o << 32) | (uint64_t)(uint32_t)~idx;
+    const uint32_t rec = sh.grec[at];
+    if (rec == 0u) return 0;
+    const int pos = sizeof(T) == 2 ? (int)(rec & 31u) : (int)sh.gpos[sizeof(T) == 2 ? 0 : at];
+    const uint32_t idx = (uint32_t)elem_index(cb + at / kWave, at % kWave, pos);
+    return ((uint64_t)record_ord<T>(rec) << 32) | (uint64_t)(uint32_t)~idx;
 }
 
 // Sorted list (largest first) of up to 64 keys, N offered per lane
@@ -204,17 +232,20 @@ __device__ __forceinline__ uint64_t select_segment(const T *__restrict__ row, in
         // A thread's records (lane `lane` of its wavefront's tiles) form a column.
         uint64_t colmax = 0;
         stream_row<T, VEC>(row, cb, ce, V, wave, lane, [&](const TileRaw<T> &r, int tile) {
-            float v[kLaneElems];
-            unpack<T>(r, v);
-            const float vmax = max32(v);
-            int fi = 0;   // first position holding the maximum: the lowest index among equals
+            // the lane's maximum and its first position (the lowest index
+            // among equals: a later entry replaces it only if larger)
+            float vmax = elem<T>(r, 0);
+            int fi = 0;
 #pragma unroll
-            for (int i = kLaneElems - 1; i >= 0; --i) fi = (v[i] == vmax) ? i : fi;
+            for (int i = 1; i < kLaneElems; ++i) {
+                const float x = elem<T>(r, i);
+                fi = x > vmax ? i : fi;
+                vmax = fmaxf(vmax, x);
+            }
             const long long idx = elem_index(tile, lane, fi);
             const uint32_t o = idx < V ? ord_bits(vmax) : 0u;
             const int at = (tile - cb) * kWave + lane;
-            sh.gord[at] = o;
-            sh.gpos[at] = (uint8_t)fi;
+            put_record(sh, at, o, fi);
             if (o) colmax = umax64(colmax, ((uint64_t)o << 32) | (uint64_t)(uint32_t)~(uint32_t)idx);
         });
         if (threadIdx.x == 0) sh.ncand = 0;
@@ -240,7 +271,7 @@ __device__ __forceinline__ uint64_t select_segment(const T *__restrict__ row, in
                 const int t = cb + wave + kWavesPerGroup * i;
                 if (t < ce) {
                     const int at = (t - cb) * kWave + lane;
-                    const uint32_t o = sh.gord[at];
+                    const uint32_t o = record_ord<T>(sh.grec[at]);
                     if (o > tord || (o == tord && o != 0u && record_key(sh, cb, at) >= theta0))
                         cmask |= 1u << i;
                 }
