@@ -1028,8 +1028,9 @@ hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     // only on verify items, which take their items by index and never wait;
     // each XCD dispatches its workgroups in index order, so every verify item
     // is dispatched before any ticket is taken on its XCD, and every wait ends.
+    // A launch small enough to be resident at once gains nothing from tickets.
     StepArgs b = a;
-    const int dyn = min(kTicketItems, a.n_items - a.n_pq);
+    const int dyn = a.n_items >= 4 * kTicketItems ? min(kTicketItems, a.n_items - a.n_pq) : 0;
     b.n_static = a.n_items - max(dyn, 0);
     long long grid = a.n_items;
     if (dyn > 0) grid += ((long long)dyn * kSpareGroupsPct + 99) / 100;
