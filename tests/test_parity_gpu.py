@@ -358,10 +358,13 @@ def test_out_of_range_proposal_is_flagged_not_faulting(isd):
 def test_workspace_returns_to_zero_across_shapes(isd):
     """The workspace contract: zero-filled before first use, zero again after
     every call, whatever the shape, mode or entry point, so one workspace can
-    serve calls of different shapes in turn."""
+    serve calls of different shapes in turn.  (64, 8, 60000) makes 2304 step
+    items, so its last 512 take tickets from the launch-wide counter, which
+    must be re-armed to zero as well."""
     import torch
     rng = np.random.default_rng(17)
-    shapes = [(8, 8, 10000), (64, 8, 4096), (3, 16, 151936), (1, 4, 1000), (64, 8, 30000)]
+    shapes = [(8, 8, 10000), (64, 8, 4096), (3, 16, 151936), (1, 4, 1000), (64, 8, 30000),
+              (64, 8, 60000)]
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     for C, L, V in shapes:
         d, bufs = _make_inputs(rng, C, L, V, "bf16")
