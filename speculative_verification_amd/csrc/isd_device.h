@@ -457,7 +457,10 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
 }
 
 // 1 / E for the 8 consecutive entries first, first + 1, ... (first % 8 == 0)
-// of correction position j under key (k0, k1).
+// of correction position j under key (k0, k1).  E is taken in units of
+// ln 2 (E = -log2 U, the hardware logarithm; U is a normal number): every
+// candidate's w / E then carries the same factor ln 2, which leaves the
+// argmax unchanged.
 __device__ __forceinline__ void inv_exp_noise8(uint32_t first, uint32_t j, uint32_t k0,
                                                uint32_t k1, float (&inv_e)[kGroupElems]) {
 #pragma unroll
@@ -468,7 +471,7 @@ __device__ __forceinline__ void inv_exp_noise8(uint32_t first, uint32_t j, uint3
         for (int e = 0; e < 4; ++e) {
             // U = (2 * (w >> 9) + 1) / 2^24: exact in fp32, strictly inside (0, 1)
             const float u = (float)(((w[e] >> 9) << 1) | 1u) * 0x1p-24f;
-            inv_e[b * 4 + e] = __builtin_amdgcn_rcpf(-logf(u));
+            inv_e[b * 4 + e] = __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(u));
         }
     }
 }
@@ -480,7 +483,7 @@ __device__ __forceinline__ float inv_exp_noise1(uint32_t i, uint32_t j, uint32_t
     const uint32_t sel = i & 3u;
     const uint32_t word = sel == 0 ? w[0] : sel == 1 ? w[1] : sel == 2 ? w[2] : w[3];
     const float u = (float)(((word >> 9) << 1) | 1u) * 0x1p-24f;
-    return __builtin_amdgcn_rcpf(-logf(u));
+    return __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(u));
 }
 
 }  // namespace
