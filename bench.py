@@ -322,6 +322,12 @@ def lora_workload(args):
 
 def main():
     args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps(dict(error="this build runs on one GPU: the ISD step is measured "
+                                    "on a single MI355X; multi-GPU runs are not supported",
+                              n_gpus=args.gpus)))
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return
@@ -331,12 +337,6 @@ def main():
     if args.config == 6:
         lora_workload(args)
         return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps(dict(error="this build runs on one GPU: the ISD step is measured "
-                                    "on a single MI355X; multi-GPU runs are not supported",
-                              n_gpus=args.gpus)))
-        sys.exit(2)
 
     import torch
 
