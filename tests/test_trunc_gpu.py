@@ -88,6 +88,14 @@ def test_truncated_step_midsize(isd, top_k, top_p):
     log(f"top-k {top_k} top-p {top_p}: accepted positions {acc}")
 
 
+@pytest.mark.parametrize("top_k,top_p", [(50, 0.95), (64, 1.0), (3, 0.5)])
+def test_truncated_one_segment_per_row(isd, top_k, top_p):
+    """C=64, L=8 makes 1536 rows, so every row is one workgroup (the item
+    finishes its row from registers); 3 tiles per row."""
+    cfg = dict(CONFIGS[2], C=64, L=8, V=5000)
+    _case(isd, cfg, 960, top_k, top_p, f"one segment k={top_k} p={top_p}")
+
+
 @pytest.mark.parametrize("V,dtype", [(5003, "bf16"), (4099, "f32"), (40, "bf16"), (2048, "bf16")])
 def test_truncated_ragged_and_small(isd, V, dtype):
     """Unaligned rows (scalar loads), fp32, a row shorter than k, one exact tile."""
