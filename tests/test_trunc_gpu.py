@@ -96,6 +96,14 @@ def test_truncated_one_segment_per_row(isd, top_k, top_p):
     _case(isd, cfg, 960, top_k, top_p, f"one segment k={top_k} p={top_p}")
 
 
+@pytest.mark.parametrize("V", [1, 7, 64, 65])
+def test_truncated_tiny_vocabularies(isd, V):
+    """Rows shorter than k (k is cut to V) and a single entry: every entry
+    survives top-k, and with one entry every law is a point mass."""
+    cfg = dict(CONFIGS[2], C=3, L=4, V=V)
+    _case(isd, cfg, 980, 50, 0.95, f"tiny V={V}")
+
+
 @pytest.mark.parametrize("V,dtype", [(5003, "bf16"), (4099, "f32"), (40, "bf16"), (2048, "bf16")])
 def test_truncated_ragged_and_small(isd, V, dtype):
     """Unaligned rows (scalar loads), fp32, a row shorter than k, one exact tile."""
