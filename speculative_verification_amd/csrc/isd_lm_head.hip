@@ -188,6 +188,7 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
     constexpr int kWN = BN / 64;                       // wavefronts along N
     constexpr int kAPer = kPBM * kPVecRow / kThr;      // A vectors per thread per step
     constexpr int kBPer = BN * kPVecRow / kThr;        // B vectors per thread per step
+    constexpr bool kDeep = BN == 256 && !STATS;        // two K steps of loads in flight
     // operand tiles; with STATS the same memory later stages the whole output
     // tile ([256][128 + 8] bf16, 68 KB: two workgroups still share a CU)
     constexpr int kStageLd = kPBN + 8;
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
     // thread tid moves the 16-byte vectors tid, tid + kThr, ... of each tile
     const int K = K1 + K2;
     uint4 ra[kAPer], rb[kBPer];
-    auto load_step = [&](int k0) {
+    auto load_into = [&](int k0, uint4 (&xa)[kAPer], uint4 (&xb)[kBPer]) {
         const bool first = k0 < K1;
         const uint16_t *src = first ? h : h2;
         const int lda = first ? K1 : K2;
@@ -219,29 +220,32 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
         for (int r = 0; r < kAPer; ++r) {
             const int v = tid + kThr * r;
             const int row = m0 + v / kPVecRow, kk = ka + (v % kPVecRow) * 8;
-            ra[r] = row < M ? *reinterpret_cast<const uint4 *>(src + (size_t)row * lda + kk)
+            xa[r] = row < M ? *reinterpret_cast<const uint4 *>(src + (size_t)row * lda + kk)
                             : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < kBPer; ++r) {
             const int v = tid + kThr * r;
             const int col = n0 + v / kPVecRow, kk = k0 + (v % kPVecRow) * 8;
-            rb[r] = col < N ? *reinterpret_cast<const uint4 *>(wt + (size_t)col * K + kk)
+            xb[r] = col < N ? *reinterpret_cast<const uint4 *>(wt + (size_t)col * K + kk)
                             : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_step = [&]() {
+    auto store_from = [&](const uint4 (&xa)[kAPer], const uint4 (&xb)[kBPer]) {
 #pragma unroll
         for (int r = 0; r < kAPer; ++r) {
             const int v = tid + kThr * r;
-            *reinterpret_cast<uint4 *>(&As[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = ra[r];
+            *reinterpret_cast<uint4 *>(&As[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = xa[r];
         }
 #pragma unroll
         for (int r = 0; r < kBPer; ++r) {
             const int v = tid + kThr * r;
-            *reinterpret_cast<uint4 *>(&Bs[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = rb[r];
+            *reinterpret_cast<uint4 *>(&Bs[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = xb[r];
         }
     };
+
+    auto load_step = [&](int k0) { load_into(k0, ra, rb); };
+    auto store_step = [&]() { store_from(ra, rb); };
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -251,12 +255,7 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
 
-    const int nk = K / kPBK;
-    load_step(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        store_step();
-        __syncthreads();
-        if (kt + 1 < nk) load_step((kt + 1) * kPBK);
+    auto mfma_step = [&]() {
 #pragma unroll
         for (int ks = 0; ks < kPBK / 16; ++ks) {
             const int kk = ks * 16 + 8 * (lane / 32);
@@ -276,7 +275,38 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
                     acc[mi][ni] =
                         __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
         }
-        __syncthreads();
+    };
+
+    const int nk = K / kPBK;
+    if constexpr (kDeep) {
+        // two K steps in flight: the loads of step kt + 2 are issued while
+        // step kt multiplies, so a load has two steps of MFMA work to return
+        uint4 ra2[kAPer], rb2[kBPer];
+        load_into(0, ra, rb);
+        if (nk > 1) load_into(kPBK, ra2, rb2);
+        for (int kt = 0; kt < nk; kt += 2) {
+            store_from(ra, rb);
+            __syncthreads();
+            if (kt + 2 < nk) load_into((kt + 2) * kPBK, ra, rb);
+            mfma_step();
+            __syncthreads();
+            if (kt + 1 < nk) {
+                store_from(ra2, rb2);
+                __syncthreads();
+                if (kt + 3 < nk) load_into((kt + 3) * kPBK, ra2, rb2);
+                mfma_step();
+                __syncthreads();
+            }
+        }
+    } else {
+        load_step(0);
+        for (int kt = 0; kt < nk; ++kt) {
+            store_step();
+            __syncthreads();
+            if (kt + 1 < nk) load_step((kt + 1) * kPBK);
+            mfma_step();
+            __syncthreads();
+        }
     }
 
     if constexpr (!STATS) {
