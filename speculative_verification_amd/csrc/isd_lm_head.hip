@@ -499,11 +499,11 @@ hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, in
 
 namespace {
 
-// Tile widths: the LM head (N = 151936) runs about 4% faster on 256-wide tiles,
-// one workgroup per CU; the narrower LoRA projection (N = 24576) on 128-wide
-// ones; the statistics variant is 128 wide.
+// Tile widths: the LM head (N = 151936) and the LoRA projection (N = 24576)
+// run on 256-wide tiles, one workgroup per CU with two K steps of loads in
+// flight; the statistics variant is 128 wide.
 constexpr int kHeadBN = 256;
-constexpr int kLoraBN = 128;
+constexpr int kLoraBN = 256;
 
 template <int BN, bool STATS>
 hipError_t launch_packed(const uint16_t *h, int K1, const uint16_t *h2, int K2, const uint16_t *wt,
