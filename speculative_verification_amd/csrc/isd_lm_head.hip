@@ -183,15 +183,15 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
     const uint16_t *__restrict__ h, int K1, const uint16_t *__restrict__ h2, int K2,
     const uint16_t *__restrict__ wt, int M, int N, uint16_t *__restrict__ out, int m_tiles,
     int total, int per_xcd, float k2, float *__restrict__ stats) {
-    static_assert(!STATS || BN == kPBN, "statistics are per 128-column tile");
+    static_assert(BN % kPBN == 0, "statistics are per 128-column tile");
     constexpr int kThr = BN * 2;                       // 4 or 8 wavefronts
     constexpr int kWN = BN / 64;                       // wavefronts along N
     constexpr int kAPer = kPBM * kPVecRow / kThr;      // A vectors per thread per step
     constexpr int kBPer = BN * kPVecRow / kThr;        // B vectors per thread per step
-    constexpr bool kDeep = BN == 256 && !STATS;        // two K steps of loads in flight
+    constexpr bool kDeep = BN == 256;                  // two K steps of loads in flight
     // operand tiles; with STATS the same memory later stages the whole output
-    // tile ([256][128 + 8] bf16, 68 KB: two workgroups still share a CU)
-    constexpr int kStageLd = kPBN + 8;
+    // tile ([256][BN + 8] bf16: 68 KB at BN = 128, 135 KB at BN = 256)
+    constexpr int kStageLd = BN + 8;
     constexpr int kOperands = (kPBM + BN) * kPLd;
     constexpr int kSmem = STATS && kPBM * kStageLd > kOperands ? kPBM * kStageLd : kOperands;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
@@ -343,8 +343,8 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
         // or unaligned edge
         const bool vec_out = (N % 8) == 0;
 #pragma unroll 4
-        for (int q = tid; q < kPBM * (kPBN / 8); q += kThreadsG) {
-            const int rl = q / (kPBN / 8), c8 = (q % (kPBN / 8)) * 8;
+        for (int q = tid; q < kPBM * (BN / 8); q += kThr) {
+            const int rl = q / (BN / 8), c8 = (q % (BN / 8)) * 8;
             const int grow = m0 + rl, gcol = n0 + c8;
             if (grow >= M) continue;
             const uint16_t *sp = &tileL[rl * kStageLd + c8];
@@ -357,9 +357,14 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
         }
     }
     if constexpr (STATS) {
+        // thread tid reduces 128 columns of row tid % 256: 128-column tile
+        // tid / 256 of the workgroup's BN columns
+        static_assert(kThr == kPBM * (BN / kPBN), "one thread per row and 128-column tile");
         const uint16_t *tileL = smem;
-        const int row = m0 + tid;
-        const uint16_t *src = &tileL[tid * kStageLd];
+        const int rl = tid % kPBM, sub = tid / kPBM;
+        const int row = m0 + rl;
+        const int c0 = n0 + sub * kPBN;
+        const uint16_t *src = &tileL[rl * kStageLd + sub * kPBN];
         const float neg = -__builtin_inff();
         float m = neg;
 #pragma unroll
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
             const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int c = n0 + q8 * 8 + 2 * e;
+                const int c = c0 + q8 * 8 + 2 * e;
                 if (c < N) m = fmaxf(m, __uint_as_float(w[e] << 16));
                 if (c + 1 < N) m = fmaxf(m, __uint_as_float(w[e] & 0xFFFF0000u));
             }
@@ -382,15 +387,15 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
                 const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int c = n0 + q8 * 8 + 2 * e;
+                    const int c = c0 + q8 * 8 + 2 * e;
                     if (c < N) sum += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(w[e] << 16), k2, -ref));
                     if (c + 1 < N)
                         sum += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(w[e] & 0xFFFF0000u), k2, -ref));
                 }
             }
         }
-        if (row < M) {
-            const size_t at = ((size_t)row * ((N + kPBN - 1) / kPBN) + n0 / kPBN) * 2;
+        if (row < M && c0 < N) {
+            const size_t at = ((size_t)row * ((N + kPBN - 1) / kPBN) + c0 / kPBN) * 2;
             stats[at] = ref;
             stats[at + 1] = sum;
         }
@@ -501,7 +506,7 @@ namespace {
 
 // Tile widths: the LM head (N = 151936) and the LoRA projection (N = 24576)
 // run on 256-wide tiles, one workgroup per CU with two K steps of loads in
-// flight; the statistics variant is 128 wide.
+// flight; so does the statistics variant.
 constexpr int kHeadBN = 256;
 constexpr int kLoraBN = 256;
 
@@ -545,7 +550,7 @@ hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStre
 
 hipError_t launch_lm_head_stats(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
                                 float k2, uint16_t *out, float *stats, hipStream_t stream) {
-    return launch_packed<kPBN, true>(h, K, nullptr, 0, wt, M, N, out, k2, stats, stream);
+    return launch_packed<kHeadBN, true>(h, K, nullptr, 0, wt, M, N, out, k2, stats, stream);
 }
 
 }  // namespace isd
