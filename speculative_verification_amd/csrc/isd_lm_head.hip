@@ -188,12 +188,14 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
     constexpr int kWN = BN / 64;                       // wavefronts along N
     constexpr int kAPer = kPBM * kPVecRow / kThr;      // A vectors per thread per step
     constexpr int kBPer = BN * kPVecRow / kThr;        // B vectors per thread per step
-    constexpr bool kDeep = BN == 256;                  // two K steps of loads in flight
-    // operand tiles; with STATS the same memory later stages the whole output
-    // tile ([256][BN + 8] bf16: 68 KB at BN = 128, 135 KB at BN = 256)
+    constexpr bool kDeep = BN == 256;                  // two K steps of loads, two LDS buffers
+    // operand tiles (two buffers of 72 KB at BN = 256); with STATS the same
+    // memory later stages the whole output tile ([256][BN + 8] bf16: 68 KB at
+    // BN = 128, 135 KB at BN = 256)
     constexpr int kStageLd = BN + 8;
     constexpr int kOperands = (kPBM + BN) * kPLd;
-    constexpr int kSmem = STATS && kPBM * kStageLd > kOperands ? kPBM * kStageLd : kOperands;
+    constexpr int kOperandBufs = kDeep ? 2 * kOperands : kOperands;
+    constexpr int kSmem = STATS && kPBM * kStageLd > kOperandBufs ? kPBM * kStageLd : kOperandBufs;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
     uint16_t *As = smem;
     uint16_t *Bs = smem + kPBM * kPLd;
@@ -231,7 +233,9 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
                             : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_from = [&](const uint4 (&xa)[kAPer], const uint4 (&xb)[kBPer]) {
+    auto store_from = [&](const uint4 (&xa)[kAPer], const uint4 (&xb)[kBPer], int bufi = 0) {
+        uint16_t *As = smem + bufi * kOperands;
+        uint16_t *Bs = As + kPBM * kPLd;
 #pragma unroll
         for (int r = 0; r < kAPer; ++r) {
             const int v = tid + kThr * r;
@@ -255,7 +259,9 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
 
-    auto mfma_step = [&]() {
+    auto mfma_step = [&](int bufi = 0) {
+        const uint16_t *As = smem + bufi * kOperands;
+        const uint16_t *Bs = As + kPBM * kPLd;
 #pragma unroll
         for (int ks = 0; ks < kPBK / 16; ++ks) {
             const int kk = ks * 16 + 8 * (lane / 32);
@@ -279,22 +285,28 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
 
     const int nk = K / kPBK;
     if constexpr (kDeep) {
-        // two K steps in flight: the loads of step kt + 2 are issued while
-        // step kt multiplies, so a load has two steps of MFMA work to return
+        // two K steps of loads in flight and two LDS buffers: step kt + 1 is
+        // stored into the other buffer while step kt multiplies, so one
+        // barrier per step separates them
         uint4 ra2[kAPer], rb2[kBPer];
         load_into(0, ra, rb);
         if (nk > 1) load_into(kPBK, ra2, rb2);
+        store_from(ra, rb, 0);
+        if (nk > 2) load_into(2 * kPBK, ra, rb);
+        __syncthreads();
         for (int kt = 0; kt < nk; kt += 2) {
-            store_from(ra, rb);
-            __syncthreads();
-            if (kt + 2 < nk) load_into((kt + 2) * kPBK, ra, rb);
-            mfma_step();
+            if (kt + 1 < nk) {
+                store_from(ra2, rb2, 1);
+                if (kt + 3 < nk) load_into((kt + 3) * kPBK, ra2, rb2);
+            }
+            mfma_step(0);
             __syncthreads();
             if (kt + 1 < nk) {
-                store_from(ra2, rb2);
-                __syncthreads();
-                if (kt + 3 < nk) load_into((kt + 3) * kPBK, ra2, rb2);
-                mfma_step();
+                if (kt + 2 < nk) {
+                    store_from(ra, rb, 0);
+                    if (kt + 4 < nk) load_into((kt + 4) * kPBK, ra, rb);
+                }
+                mfma_step(1);
                 __syncthreads();
             }
         }
