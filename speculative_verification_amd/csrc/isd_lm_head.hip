@@ -188,14 +188,11 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
     constexpr int kWN = BN / 64;                       // wavefronts along N
     constexpr int kAPer = kPBM * kPVecRow / kThr;      // A vectors per thread per step
     constexpr int kBPer = BN * kPVecRow / kThr;        // B vectors per thread per step
-    constexpr bool kDeep = BN == 256;                  // two K steps of loads, two LDS buffers
-    // operand tiles (two buffers of 72 KB at BN = 256); with STATS the same
-    // memory later stages the whole output tile ([256][BN + 8] bf16: 68 KB at
-    // BN = 128, 135 KB at BN = 256)
+    // operand tiles; with STATS the same memory later stages the whole output
+    // tile ([256][BN + 8] bf16: 68 KB at BN = 128, 135 KB at BN = 256)
     constexpr int kStageLd = BN + 8;
     constexpr int kOperands = (kPBM + BN) * kPLd;
-    constexpr int kOperandBufs = kDeep ? 2 * kOperands : kOperands;
-    constexpr int kSmem = STATS && kPBM * kStageLd > kOperandBufs ? kPBM * kStageLd : kOperandBufs;
+    constexpr int kSmem = STATS && kPBM * kStageLd > kOperands ? kPBM * kStageLd : kOperands;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
     uint16_t *As = smem;
     uint16_t *Bs = smem + kPBM * kPLd;
@@ -213,7 +210,7 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
     // thread tid moves the 16-byte vectors tid, tid + kThr, ... of each tile
     const int K = K1 + K2;
     uint4 ra[kAPer], rb[kBPer];
-    auto load_into = [&](int k0, uint4 (&xa)[kAPer], uint4 (&xb)[kBPer]) {
+    auto load_step = [&](int k0) {
         const bool first = k0 < K1;
         const uint16_t *src = first ? h : h2;
         const int lda = first ? K1 : K2;
@@ -222,34 +219,29 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
         for (int r = 0; r < kAPer; ++r) {
             const int v = tid + kThr * r;
             const int row = m0 + v / kPVecRow, kk = ka + (v % kPVecRow) * 8;
-            xa[r] = row < M ? *reinterpret_cast<const uint4 *>(src + (size_t)row * lda + kk)
+            ra[r] = row < M ? *reinterpret_cast<const uint4 *>(src + (size_t)row * lda + kk)
                             : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < kBPer; ++r) {
             const int v = tid + kThr * r;
             const int col = n0 + v / kPVecRow, kk = k0 + (v % kPVecRow) * 8;
-            xb[r] = col < N ? *reinterpret_cast<const uint4 *>(wt + (size_t)col * K + kk)
+            rb[r] = col < N ? *reinterpret_cast<const uint4 *>(wt + (size_t)col * K + kk)
                             : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_from = [&](const uint4 (&xa)[kAPer], const uint4 (&xb)[kBPer], int bufi = 0) {
-        uint16_t *As = smem + bufi * kOperands;
-        uint16_t *Bs = As + kPBM * kPLd;
+    auto store_step = [&]() {
 #pragma unroll
         for (int r = 0; r < kAPer; ++r) {
             const int v = tid + kThr * r;
-            *reinterpret_cast<uint4 *>(&As[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = xa[r];
+            *reinterpret_cast<uint4 *>(&As[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = ra[r];
         }
 #pragma unroll
         for (int r = 0; r < kBPer; ++r) {
             const int v = tid + kThr * r;
-            *reinterpret_cast<uint4 *>(&Bs[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = xb[r];
+            *reinterpret_cast<uint4 *>(&Bs[(v / kPVecRow) * kPLd + (v % kPVecRow) * 8]) = rb[r];
         }
     };
-
-    auto load_step = [&](int k0) { load_into(k0, ra, rb); };
-    auto store_step = [&]() { store_from(ra, rb); };
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -259,9 +251,12 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
 
-    auto mfma_step = [&](int bufi = 0) {
-        const uint16_t *As = smem + bufi * kOperands;
-        const uint16_t *Bs = As + kPBM * kPLd;
+    const int nk = K / kPBK;
+    load_step(0);
+    for (int kt = 0; kt < nk; ++kt) {
+        store_step();
+        __syncthreads();
+        if (kt + 1 < nk) load_step((kt + 1) * kPBK);
 #pragma unroll
         for (int ks = 0; ks < kPBK / 16; ++ks) {
             const int kk = ks * 16 + 8 * (lane / 32);
@@ -281,44 +276,7 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
                     acc[mi][ni] =
                         __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
         }
-    };
-
-    const int nk = K / kPBK;
-    if constexpr (kDeep) {
-        // two K steps of loads in flight and two LDS buffers: step kt + 1 is
-        // stored into the other buffer while step kt multiplies, so one
-        // barrier per step separates them
-        uint4 ra2[kAPer], rb2[kBPer];
-        load_into(0, ra, rb);
-        if (nk > 1) load_into(kPBK, ra2, rb2);
-        store_from(ra, rb, 0);
-        if (nk > 2) load_into(2 * kPBK, ra, rb);
         __syncthreads();
-        for (int kt = 0; kt < nk; kt += 2) {
-            if (kt + 1 < nk) {
-                store_from(ra2, rb2, 1);
-                if (kt + 3 < nk) load_into((kt + 3) * kPBK, ra2, rb2);
-            }
-            mfma_step(0);
-            __syncthreads();
-            if (kt + 1 < nk) {
-                if (kt + 2 < nk) {
-                    store_from(ra, rb, 0);
-                    if (kt + 4 < nk) load_into((kt + 4) * kPBK, ra, rb);
-                }
-                mfma_step(1);
-                __syncthreads();
-            }
-        }
-    } else {
-        load_step(0);
-        for (int kt = 0; kt < nk; ++kt) {
-            store_step();
-            __syncthreads();
-            if (kt + 1 < nk) load_step((kt + 1) * kPBK);
-            mfma_step();
-            __syncthreads();
-        }
     }
 
     if constexpr (!STATS) {
@@ -516,11 +474,11 @@ hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, in
 
 namespace {
 
-// Tile widths: the LM head (N = 151936) and the LoRA projection (N = 24576)
-// run on 256-wide tiles, one workgroup per CU with two K steps of loads in
-// flight; so does the statistics variant.
+// Tile widths: the LM head (N = 151936) and its statistics variant run on
+// 256-wide tiles, one workgroup per CU; the narrower LoRA projection
+// (N = 24576) on 128-wide ones.
 constexpr int kHeadBN = 256;
-constexpr int kLoraBN = 256;
+constexpr int kLoraBN = 128;
 
 template <int BN, bool STATS>
 hipError_t launch_packed(const uint16_t *h, int K1, const uint16_t *h2, int K2, const uint16_t *wt,
