@@ -53,7 +53,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed steps first; about 0.2 s of the serving step, which brings the "
+                         "GPU clock to its steady state (20 steps leave it ramping: +4-5%%)")
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6],
                     help="2 serving step, 3 greedy step, 4 LM head + step, 5 high concurrency, "
                          "6 segment-gated LoRA projection")
