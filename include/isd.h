@@ -340,10 +340,15 @@ isd_status_t isd_step_fused(const isd_shape_t *s, const void *p_logits, const vo
  *   t     [M, r]       written: the gated adapter activations gate * A x
  *                      (bf16, zero on clean rows); caller-owned scratch,
  *                      16-byte aligned
- *   out   [M, N]       written: h, fp32 accumulation rounded to bf16
- * K and r must be multiples of 64.  Two launches on `stream` (the shrink,
- * then one GEMM over the concatenated K); no host synchronisation, no
- * allocation, so the call can be captured in a graph.  Errors: ISD_ERR_ARG
+ *   out   [M, N]       written: h, fp32 accumulation rounded to bf16; must
+ *                      not overlap the other buffers.  When it is 16-byte
+ *                      aligned, r is a multiple of 128 and it can hold
+ *                      ceil(K / 256) * M * r floats, it first holds the
+ *                      shrink's partial sums (split over K)
+ * K and r must be multiples of 64.  Two or three launches on `stream` (the
+ * shrink, in one kernel or as partial sums and their sum, then one GEMM over
+ * the concatenated K); no host synchronisation, no allocation, so the call
+ * can be captured in a graph.  Errors: ISD_ERR_ARG
  * for bad sizes or pointers, ISD_ERR_DEVICE if a launch fails. */
 isd_status_t isd_lora_gemm(const void *x, const void *a, const void *wcat, const int32_t *mask,
                            int32_t M, int32_t K, int32_t N, int32_t r, void *t, void *out,

@@ -440,6 +440,105 @@ __global__ __launch_bounds__(kSWaves * 64) void lora_shrink_kernel(
     }
 }
 
+// Split-K form of the shrink, for calls whose output buffer can hold the
+// partial sums.  Workgroup (b, s, z) multiplies rows 64b .. 64b + 63 of x by
+// adapter channels 128z .. 128z + 127 of A over K slice s, both staged in LDS
+// with row-contiguous 16-byte loads, and writes the fp32 partial tile to
+// part[s][row][channel]; a second kernel adds the slices in order, applies the
+// gate and rounds to bf16.  The partials live in the projection's output
+// buffer, which the GEMM that follows overwrites.
+
+constexpr int kSpRows = 64, kSpCh = 128, kSpSlice = 256;
+constexpr int kSpLd = kSpSlice + 8;                         // LDS row length (bf16), padded
+
+__global__ __launch_bounds__(256) void lora_shrink_part_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ a, int M, int K, int r,
+    float *__restrict__ part) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kSpRows * kSpLd];
+    __shared__ __attribute__((aligned(16))) uint16_t as[kSpCh * kSpLd];
+    const int m0 = blockIdx.x * kSpRows, s = blockIdx.y, c0 = blockIdx.z * kSpCh;
+    const int k0 = s * kSpSlice;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    constexpr int kVec = kSpSlice / 8;                      // 16-byte vectors per row
+    // every load is issued before the first LDS store, so their latencies
+    // overlap; x rows past M and k past K read as zeros
+    constexpr int kXPer = kSpRows * kVec / 256, kAPer = kSpCh * kVec / 256;
+    uint4 vx[kXPer], va[kAPer];
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j) {
+        const int v = tid + 256 * j;
+        const int row = m0 + v / kVec, k = k0 + (v % kVec) * 8;
+        vx[j] = (row < M && k < K) ? *reinterpret_cast<const uint4 *>(x + (size_t)row * K + k)
+                                   : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+        const int v = tid + 256 * j;
+        const int k = k0 + (v % kVec) * 8;
+        va[j] = k < K ? *reinterpret_cast<const uint4 *>(a + (size_t)(c0 + v / kVec) * K + k)
+                      : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j) {
+        const int v = tid + 256 * j;
+        *reinterpret_cast<uint4 *>(&xs[(v / kVec) * kSpLd + (v % kVec) * 8]) = vx[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+        const int v = tid + 256 * j;
+        *reinterpret_cast<uint4 *>(&as[(v / kVec) * kSpLd + (v % kVec) * 8]) = va[j];
+    }
+    __syncthreads();
+    // wavefront w: rows 32 (w % 2) .., channels 64 (w / 2) .. as two 32 x 32 tiles
+    const int mt = wave % 2, nb = (wave / 2) * 2;
+    f32x16 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
+#pragma unroll 4
+    for (int ks = 0; ks < kSpSlice / 16; ++ks) {
+        const int kk = ks * 16 + 8 * (lane / 32);
+        const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&xs[(mt * 32 + lane % 32) * kSpLd + kk]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const bf16x8 bfr =
+                *reinterpret_cast<const bf16x8 *>(&as[((nb + j) * 32 + lane % 32) * kSpLd + kk]);
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[j], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = m0 + mt * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+            const int ch = c0 + (nb + j) * 32 + lane % 32;
+            if (row < M) part[((size_t)s * M + row) * r + ch] = acc[j][i];
+        }
+}
+
+// t[row, ch] = gate(row) * bf16(sum over the slices, in slice order).
+__global__ __launch_bounds__(256) void lora_shrink_sum_kernel(const float *__restrict__ part,
+                                                              const int32_t *__restrict__ mask,
+                                                              int M, int r, int slices,
+                                                              uint16_t *__restrict__ t) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long long)M * r) return;
+    const int row = (int)(i / r);
+    float acc = 0.0f;
+    int s = 0;
+    for (; s + 4 <= slices; s += 4) {   // four loads in flight, added in slice order
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = part[(size_t)(s + j) * M * r + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc += v[j];
+    }
+    for (; s < slices; ++s) acc += part[(size_t)s * M * r + i];
+    const bool gate = mask == nullptr || mask[row] != 0;
+    t[i] = gate ? bf16_rne(acc) : (uint16_t)0;
+}
+
 // wt[N, K] = w[K, N]^T through 64 x 64 LDS tiles (bit copies).
 __global__ __launch_bounds__(256) void pack_wt_kernel(const uint16_t *__restrict__ w,
                                                       uint16_t *__restrict__ wt, int K, int N) {
@@ -504,9 +603,22 @@ hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, i
 hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t *wcat,
                             const int32_t *mask, int M, int K, int N, int r, uint16_t *t,
                             uint16_t *out, hipStream_t stream) {
-    const dim3 sgrid((unsigned)((M + kSRows - 1) / kSRows), (unsigned)(r / kSCols));
-    hipLaunchKernelGGL(lora_shrink_kernel, sgrid, dim3(kSWaves * 64), 0, stream, x, a, mask, M, K,
-                       r, t);
+    // the split-K shrink when the output buffer can hold its fp32 partials
+    const int slices = (K + kSpSlice - 1) / kSpSlice;
+    const bool split = r % kSpCh == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0 &&
+                       (size_t)slices * M * r * sizeof(float) <= (size_t)M * N * sizeof(uint16_t);
+    if (split) {
+        float *part = reinterpret_cast<float *>(out);
+        const dim3 pgrid((unsigned)((M + kSpRows - 1) / kSpRows), (unsigned)slices, (unsigned)(r / kSpCh));
+        hipLaunchKernelGGL(lora_shrink_part_kernel, pgrid, dim3(256), 0, stream, x, a, M, K, r, part);
+        const long long n = (long long)M * r;
+        hipLaunchKernelGGL(lora_shrink_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           part, mask, M, r, slices, t);
+    } else {
+        const dim3 sgrid((unsigned)((M + kSRows - 1) / kSRows), (unsigned)(r / kSCols));
+        hipLaunchKernelGGL(lora_shrink_kernel, sgrid, dim3(kSWaves * 64), 0, stream, x, a, mask, M, K,
+                           r, t);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_packed<kLoraBN, false>(x, K, t, r, wcat, M, N, out, 0.0f, nullptr, stream);

@@ -102,6 +102,22 @@ def test_lora_no_mask_adapts_every_row(isd):
     _check(d, _host(h), _host(t), np.arange(ones.size), ones)
 
 
+def test_lora_split_shrink_ragged(isd):
+    """An output buffer large enough for the shrink's fp32 partial sums (the
+    split-K shrink): 42 rows (not a multiple of 64), K = 640 (three K slices,
+    the last one partial), r = 128."""
+    import torch
+    cfg = dict(LORA_CONFIGS["mid"], C=3, L=7, N=2048, K=640, r=128)
+    d = gen_lora(cfg, seed=6)
+    mask = d["mask"]
+    x, a = _dev(d["x"]), _dev(d["a"])
+    wcat = isd.lora_pack(_dev(d["w"]), _dev(d["b"]))
+    h, t = isd.lora_gemm(x, a, wcat, torch.from_numpy(mask).cuda())
+    torch.cuda.synchronize()
+    worst, t_worst = _check(d, _host(h), _host(t), np.arange(mask.size), mask)
+    log(f"lora split shrink: worst h err/bound {worst:.3f}, t err/bound {t_worst:.3f}")
+
+
 def test_lora_full_shape_sampled_rows(isd):
     """The MLP gate/up projection of an 8B model at the serving batch:
     M = 1024, K = 4096, N = 24576, r = 128; every adapter activation and
