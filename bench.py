@@ -253,6 +253,8 @@ def lm_head_workload(args):
                              f"C={C}, L={L} verify/propose", C=C, L=L, V=V, H=H,
                     head_layout="W packed once (untimed) to k-contiguous [V, H]",
                     step_input="LM-head tile statistics" if args.fused else "logits"),
+        roofline=dict(bound="mfma", achieved=round(gemm_tflops, 1), peak=2500.0,
+                      unit="TFLOP/s", frac=round(gemm_tflops / 2500.0, 4), traffic=None),
         gemm=dict(ms=round(float(gemm_ms), 4), tflops=round(gemm_tflops, 1),
                   mfma_util=round(gemm_tflops / 2500.0, 4), peak_tflops=2500.0),
         step=(dict(us=round(float(step_ms) * 1e3, 2),
