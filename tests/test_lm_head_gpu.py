@@ -121,3 +121,29 @@ def test_lm_head_packed_full_shape_sampled_rows(isd):
     worst, frac = _check(gpu, h_bits, w_bits, rows)
     log(f"lm_head_packed full shape, rows {rows.tolist()}: worst err/bound {worst:.3f}, "
         f"exact-rounded fraction {frac:.5f}")
+
+
+@pytest.mark.parametrize("N", [65280, 65536])
+def test_lm_head_packed_tile_width_threshold(isd, N):
+    """1024 rows give four 256-row tiles; N = 65280 makes 1020 tiles of 256 columns
+    (the packed head then runs on 128-wide tiles), N = 65536 exactly 1024 (256-wide).
+    Both widths must hold the oracle's bound on sampled rows and agree bit for bit with
+    the unpacked kernel, which accumulates in the same K order."""
+    import torch
+    M, K = 1024, 512
+    rng = np.random.default_rng(N)
+    h_bits = f32_to_bf16_bits(rng.normal(0, 1, (M, K)).astype(np.float32))
+    w_bits = f32_to_bf16_bits(rng.normal(0, 0.02, (K, N)).astype(np.float32))
+    w_dev = _dev_bf16(w_bits)
+    h_dev = _dev_bf16(h_bits)
+    packed = isd.lm_head_packed(h_dev, isd.lm_head_pack(w_dev))
+    plain = isd.lm_head(h_dev, w_dev)
+    torch.cuda.synchronize()
+    gp = packed.view(torch.int16).cpu().numpy().view(np.uint16)
+    gu = plain.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert gp.shape == (M, N)
+    rows = np.array([0, 1, 255, 256, 511, 767, 1000, 1023])
+    worst, frac = _check(gp, h_bits, w_bits, rows)
+    assert np.array_equal(gp, gu), "packed and unpacked heads differ"
+    log(f"lm_head_packed M={M} K={K} N={N}: worst err/bound {worst:.3f}, "
+        f"exact-rounded fraction {frac:.5f}, equal to the unpacked kernel")
