@@ -17,7 +17,7 @@ Sources (cited by page title and section):
   cycle: one proposal-only step, then verify-and-propose steps until a
   rejection.
 
-Reading (listed in the design doc): stride N means L = N - 1 proposals per step.
+Reading of the pages: stride N means L = N - 1 proposals per step.
 A sequence is in one of two states.  In the *recovery* state its step draws
 one token from its anchor row (the last clean position) and proposes L
 tokens; it then verifies.  In the *verify* state its step checks its L
