@@ -39,11 +39,14 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_isd_step_serving.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_verification_amd", "csrc", f)
                   for f in ("isd_step.hip", "isd_device.h", "isd_internal.h", "isd_api.hip")]
+HEAD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lm_head.json")
+HEAD_SOURCES = [os.path.join(ROOT, "speculative_verification_amd", "csrc", f)
+                for f in ("isd_lm_head.hip", "isd_internal.h", "isd_api.hip")]
 
 
-def kernel_digest() -> str:
+def kernel_digest(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES if sources is None else sources):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -254,7 +257,8 @@ def lm_head_workload(args):
                     head_layout="W packed once (untimed) to k-contiguous [V, H]",
                     step_input="LM-head tile statistics" if args.fused else "logits"),
         roofline=dict(bound="mfma", achieved=round(gemm_tflops, 1), peak=2500.0,
-                      unit="TFLOP/s", frac=round(gemm_tflops / 2500.0, 4), traffic=None),
+                      unit="TFLOP/s", frac=round(gemm_tflops / 2500.0, 4),
+                      traffic=head_traffic(M, H, V) if not args.fused else None),
         gemm=dict(ms=round(float(gemm_ms), 4), tflops=round(gemm_tflops, 1),
                   mfma_util=round(gemm_tflops / 2500.0, 4), peak_tflops=2500.0),
         step=(dict(us=round(float(step_ms) * 1e3, 2),
@@ -264,6 +268,19 @@ def lm_head_workload(args):
                    hbm_gbs=round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
                    frac=round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))),
         accept_len_mean_last=round(acc, 3))), flush=True)
+
+
+def head_traffic(M, H, V):
+    """HBM bytes per launch of the plain packed LM head from rocprofv3
+    FETCH_SIZE / WRITE_SIZE (copy-calibrated), when profiles/ holds counters
+    for the current GEMM source and this shape; else None."""
+    if not os.path.exists(HEAD_TRAFFIC_FILE):
+        return None
+    with open(HEAD_TRAFFIC_FILE) as f:
+        tr = json.load(f)
+    if tr.get("kernel_digest") != kernel_digest(HEAD_SOURCES) or tr.get("shape") != [M, H, V]:
+        return None
+    return tr.get("bytes_per_launch")
 
 
 def lora_workload(args):
