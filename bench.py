@@ -7,18 +7,31 @@ A step is one isd_step launch over one batch: verification of C*L proposals
 (mask rows qn).  The serving workload (C=64, L=8, V=151936, bf16 logits, T=1)
 is the default.  Inputs are resident in HBM before timing; steps cycle over
 `--sets` distinct logits sets (each larger than the 256 MB Infinity Cache)
-with fresh uniforms every step.  Prints one JSON line.
+with fresh uniforms every step (the tiny workload, --config 1, draws fresh
+inputs for every step).  Prints one JSON line.
+
+Order of work: inputs are generated and uploaded; the streaming-read probe
+reads a 1 GiB buffer for about 0.4 s (its rate is reported, and the GPU clock
+reaches its steady state meanwhile); W untimed steps; K timed steps, each
+writing its own output buffers; then the CPU oracle recomputes every sequence
+of the first timed steps from the same bytes and uniforms and the outputs of
+those launches are compared with it.
 
 Reported:
   value      verified positions per second = C*L / wall-clock time per step
+             (the tiny workload reports microseconds per step instead)
   roofline   the step kernel against the HBM peak: algorithmic bytes per
              launch (every logit read once: 3*C*L*V*2 B) over the kernel's
              average duration (two events on its stream around the K
              back-to-back launches); `traffic` is the HBM bytes per launch
              from rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated on a plain copy,
              when profiles/ holds counters for the current kernel source
-  cpu_baseline  the CPU oracle on a bounded sample of the same inputs,
-             across the host's cores (process pool), in positions per second
+  read_probe the probe's read rate and the step's fraction of it
+  check      the timed launches against the oracle: unflagged mismatches
+             (must be 0), near-boundary flags, the largest relative error of
+             the reported probabilities
+  cpu_baseline  the CPU oracle's rate on that sample across the host's cores
+             (process pool), with a one-core figure and the CPU model
 """
 
 from __future__ import annotations
@@ -56,12 +69,12 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=2000,
-                    help="untimed steps first; about 0.2 s of the serving step, which brings the "
-                         "GPU clock to its steady state (20 steps leave it ramping: +4-5%%)")
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6],
-                    help="2 serving step, 3 greedy step, 4 LM head + step, 5 high concurrency, "
-                         "6 segment-gated LoRA projection")
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps before the timed ones (the read probe before them has "
+                         "already brought the GPU clock to its steady state)")
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
+                    help="1 tiny step (latency), 2 serving step, 3 greedy step, 4 LM head + step, "
+                         "5 high concurrency, 6 segment-gated LoRA projection")
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -78,6 +91,8 @@ def parse():
                     help="config 4: the LM head writes softmax statistics and the step reads them")
     ap.add_argument("--trunc-segments", type=int, default=0,
                     help="workgroups per row on the truncated path (0: automatic)")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the streaming-read probe (1 GiB, the step's tile loader)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -100,54 +115,146 @@ def copy_calibration():
 
 
 # ---------------------------------------------------------------------------
-# CPU oracle baseline (forked workers share the host inputs copy-on-write)
+# Streaming-read probe (the device's practical read ceiling for the step's loop)
+# ---------------------------------------------------------------------------
+
+PROBE_BYTES = 1 << 30
+PROBE_SETTLE_S = 0.4
+
+
+def read_probe():
+    """Streams a 1 GiB buffer with the step kernel's tile loader until about
+    PROBE_SETTLE_S of device time has passed (which also brings the GPU clock
+    to its steady state before any step is timed), then times 20 reads with
+    two events.  Returns the read rate in GB/s."""
+    import torch
+
+    import speculative_verification_amd as isd
+    buf = torch.empty(PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < PROBE_SETTLE_S:
+        for _ in range(50):
+            isd.read_probe(buf, sink)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20
+    e0.record()
+    for _ in range(n):
+        isd.read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    del buf
+    return PROBE_BYTES / (ms * 1e-3) / 1e9
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle on the timed steps (forked workers share the host inputs)
 # ---------------------------------------------------------------------------
 
 _HOST = {}
 
 
-def _oracle_seq(args):
+def _oracle_job(job):
+    """Oracle outputs of sequence c of timed step i (the bytes and uniforms
+    that launch consumed)."""
     os.environ["OMP_NUM_THREADS"] = "1"
     from oracle import isd_oracle as O
-    s, c, dtype, mode, T = args
-    d = _HOST["sets"][s]
-    p = O.decode_logits(d["p"][c:c + 1], dtype)
-    qn = O.decode_logits(d["qn"][c:c + 1], dtype)
+    i, c = job
+    h = _HOST
+    d = h["sets"][h["set_of"][i]]
+    u = h["uni"][h["step_of"][i]]                      # [3, C, L]
+    dt, mode, T, a = h["dtype"], h["mode"], h["T"], h["args"]
+    p = O.decode_logits(d["p"][c:c + 1], dt)
+    qn = O.decode_logits(d["qn"][c:c + 1], dt)
+    x = d["x"][c:c + 1]
     if mode == "greedy":
-        O.verify_greedy(p, d["x"][c:c + 1])
-        O.propose_greedy(qn)
+        v = O.verify_greedy(p, x)
+        g = v["argmax"]
+        v.update(p_x=(x == g).astype(np.float64), q_x=np.ones(x.shape),
+                 flagged=np.zeros(1, bool), resid_flagged=np.zeros(1, bool))
+        tok, prob, nflag = O.propose_greedy(qn), np.ones(x.shape), np.zeros(x.shape, bool)
     else:
-        q = O.decode_logits(d["q"][c:c + 1], dtype)
-        O.verify_sample(p, q, d["x"][c:c + 1], d["ua"][c:c + 1], d["ur"][c:c + 1], T)
-        O.propose_sample(qn, d["up"][c:c + 1], T)
-    return 1
+        q = O.decode_logits(d["q"][c:c + 1], dt)
+        v = O.verify_sample(p, q, x, u[0, c:c + 1], u[1, c:c + 1], T, sampler=a["sampler"],
+                            seq_ids=np.array([c]), top_k=a["top_k"], top_p=a["top_p"])
+        tok, prob, _, nflag = O.propose_sample(qn, u[2, c:c + 1], T, top_k=a["top_k"],
+                                               top_p=a["top_p"])
+    return i, c, dict(accept_len=int(v["accept_len"][0]), out_tokens=v["out_tokens"][0],
+                      n_emitted=int(v["n_emitted"][0]), p_x=v["p_x"][0], q_x=v["q_x"][0],
+                      alpha=float(v["alpha"][0]), flagged=bool(v["flagged"][0]),
+                      resid_flagged=bool(v["resid_flagged"][0]), next_tokens=tok[0],
+                      qnext_x=prob[0], next_flagged=nflag[0])
 
 
-def cpu_baseline(host_sets, cfg, target_s):
+def _rel(g, o):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    den = np.where(np.abs(o) > 0, np.abs(o), 1.0)
+    return float(np.max(np.where(np.abs(o) > 0, np.abs(g - o) / den, np.abs(g - o)), initial=0.0))
+
+
+def check_and_time_oracle(gpu, n_timed, cfg, target_s):
+    """Runs the CPU oracle over every sequence of the first timed steps (as
+    many as fit about target_s of wall time on the host's cores), compares
+    each with the GPU outputs of the same launch, and times it.  Returns
+    (cpu_baseline, check)."""
     import multiprocessing as mp
-    cores = len(os.sched_getaffinity(0))
-    _HOST["sets"] = host_sets
     C, L = cfg["C"], cfg["L"]
-    jobs_all = [(s, c, cfg["dtype"], cfg["mode"], cfg["T"])
-                for s in range(len(host_sets)) for c in range(C)]
-    # calibrate on one sequence, then size the sample to about target_s of wall time
+    cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    _oracle_seq(jobs_all[0])
-    per_seq = time.perf_counter() - t0
-    n = int(max(cores, min(len(jobs_all) * 4, target_s * cores / max(per_seq, 1e-6))))
-    jobs = [jobs_all[i % len(jobs_all)] for i in range(n)]
+    _oracle_job((0, 0))
+    per_seq = time.perf_counter() - t0               # one sequence, one core
+    n_steps = int(max(1, min(n_timed, target_s * cores / max(per_seq * C, 1e-9))))
+    jobs = [(i, c) for i in range(n_steps) for c in range(C)]
     pool = mp.get_context("fork").Pool(cores)
     try:
         t0 = time.perf_counter()
-        done = sum(pool.imap_unordered(_oracle_seq, jobs, chunksize=1))
+        res = list(pool.imap_unordered(_oracle_job, jobs, chunksize=1))
         wall = time.perf_counter() - t0
     finally:
         pool.close()
         pool.join()
-    return dict(value=round(done * L / wall, 3), unit="positions/s", cores=cores, kind="oracle",
-                sample=f"{done} sequences ({done * L} positions) of the timed workload's "
-                       f"resident input sets, fp64 numpy oracle, one process per core, "
-                       f"{wall:.1f} s wall")
+    ck = dict(steps=n_steps, sequences=len(jobs), positions=len(jobs) * L, mismatches=0,
+              decision_flags=0, resid_flags=0, propose_flags=0, max_rel_err_prob=0.0)
+    for i, c, o in res:
+        g = {k: v[i] for k, v in gpu.items()}
+        ck["max_rel_err_prob"] = max(ck["max_rel_err_prob"], _rel(g["p_x"][c], o["p_x"]),
+                                     _rel(g["q_x"][c], o["q_x"]), _rel(g["alpha"][c], o["alpha"]))
+        ok_next = ~o["next_flagged"]
+        ck["propose_flags"] += int((~ok_next).sum())
+        ck["mismatches"] += int((g["next_tokens"][c][ok_next] != o["next_tokens"][ok_next]).sum())
+        if ok_next.any():
+            ck["max_rel_err_prob"] = max(ck["max_rel_err_prob"],
+                                         _rel(g["qnext_x"][c][ok_next], o["qnext_x"][ok_next]))
+        if o["flagged"]:
+            ck["decision_flags"] += 1
+            continue
+        j = o["accept_len"]
+        bad = g["accept_len"][c] != j or g["n_emitted"][c] != o["n_emitted"]
+        keep = np.ones(L, bool)
+        if j < L and o["resid_flagged"]:
+            ck["resid_flags"] += 1
+            keep[j] = False
+        bad = bad or not np.array_equal(g["out_tokens"][c][keep], o["out_tokens"][keep])
+        ck["mismatches"] += int(bad)
+    ck["max_rel_err_prob"] = float(f"{ck['max_rel_err_prob']:.3g}")
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    base = dict(value=round(len(jobs) * L / wall, 3), unit="positions/s", cores=cores,
+                kind="oracle",
+                sample=f"every sequence of the first {n_steps} timed steps ({len(jobs)} sequences, "
+                       f"{len(jobs) * L} positions, the launches' own inputs), fp64 numpy oracle, "
+                       f"one process per core, {wall:.1f} s wall",
+                value_1core=round(L / per_seq, 3), cpu_model=model)
+    return base, ck
 
 
 # ---------------------------------------------------------------------------
@@ -223,6 +330,7 @@ def lm_head_workload(args):
         head(hs[i % 2], i)
         outs[i % 2] = verify_propose(i)
 
+    probe_gbs = read_probe()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -267,6 +375,7 @@ def lm_head_workload(args):
               dict(us=round(float(step_ms) * 1e3, 2),
                    hbm_gbs=round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
                    frac=round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))),
+        read_probe=dict(gbs=round(probe_gbs, 1)),
         accept_len_mean_last=round(acc, 3))), flush=True)
 
 
@@ -323,6 +432,7 @@ def lora_workload(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t0) * 1e3 / args.steps
 
+    read_probe()
     base_ms, _ = timed(lambda: isd.lm_head_packed(x, w, out=out))
     lora_ms, wall_ms = timed(lambda: isd.lora_gemm(x, a, wcat, mask, out=out, t=t))
     gated = int((d["mask"] != 0).sum())
@@ -341,24 +451,8 @@ def lora_workload(args):
         adapter_overhead=round(lora_ms / base_ms - 1.0, 4))), flush=True)
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps(dict(error="this build runs on one GPU: the ISD step is measured "
-                                    "on a single MI355X; multi-GPU runs are not supported",
-                              n_gpus=args.gpus)))
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.config == 4:
-        lm_head_workload(args)
-        return
-    if args.config == 6:
-        lora_workload(args)
-        return
-
+def step_workload(args):
+    """Configs 1, 2, 3 and 5: the fused step over resident inputs."""
     import torch
 
     import speculative_verification_amd as isd
@@ -366,40 +460,66 @@ def main():
 
     cfg = CONFIGS[args.config]
     C, L, V, mode, T = cfg["C"], cfg["L"], cfg["V"], cfg["mode"], cfg["T"]
+    dt = cfg["dtype"]
+    es = 2 if dt == "bf16" else 4
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     isd.set_tuning(args.segments, args.resid_segments, 0, args.propose_segments)
     isd.set_trunc_tuning(args.trunc_segments)
 
-    nsets = max(1, args.sets)
+    total = args.warmup + args.steps
+    # the tiny workload draws fresh inputs for every step; the large ones cycle
+    # over a few resident sets, each larger than the 256 MB Infinity Cache
+    tiny = args.config == 1
+    nsets = total if tiny else max(1, args.sets)
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     t_gen = time.perf_counter()
     host_sets, dev_sets = [], []
     for s in range(nsets):
-        d = gen_step(args.config, s, workers=workers)
+        d = gen_step(args.config, s, workers=1 if tiny else workers)
         host_sets.append(d)
         t = {}
         for key in ("p", "q", "qn"):
-            t[key] = torch.from_numpy(d[key].view(np.int16)).to(dev).view(torch.bfloat16)
+            a = np.ascontiguousarray(d[key])
+            t[key] = (torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+                      if dt == "bf16" else torch.from_numpy(a).to(dev))
         t["x"] = torch.from_numpy(d["x"]).to(dev)
         dev_sets.append(t)
-    total = args.warmup + args.steps
-    uni = torch.from_numpy(gen_uniforms(args.config, total)).to(dev)   # [steps, 3, C, L]
+    uni_host = gen_uniforms(args.config, total)          # [steps, 3, C, L]
+    uni = torch.from_numpy(uni_host).to(dev)
+
+    def outputs():
+        return dict(accept_len=torch.empty((C,), dtype=torch.int32, device=dev),
+                    out_tokens=torch.empty((C, L), dtype=torch.int32, device=dev),
+                    n_emitted=torch.empty((C,), dtype=torch.int32, device=dev),
+                    p_x=torch.empty((C, L), dtype=torch.float32, device=dev),
+                    q_x=torch.empty((C, L), dtype=torch.float32, device=dev),
+                    alpha=torch.empty((C,), dtype=torch.float32, device=dev),
+                    next_tokens=torch.empty((C, L), dtype=torch.int32, device=dev),
+                    qnext_x=torch.empty((C, L), dtype=torch.float32, device=dev))
+
+    timed_out = [outputs() for _ in range(args.steps)]   # every timed launch keeps its outputs
     torch.cuda.synchronize()
-    gen_s = time.perf_counter() - t_gen
-    print(f"# inputs ready: {nsets} sets x {3 * C * L * V * 2 / 1e6:.1f} MB, {gen_s:.1f} s",
-          file=sys.stderr, flush=True)
+    print(f"# inputs ready: {nsets} sets x {3 * C * L * V * es / 1e6:.2f} MB, "
+          f"{time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    probe_gbs = read_probe()
 
     d0 = dev_sets[0]
     call = isd.StepCall(d0["p"], d0["q"], d0["x"], uni[0, 0], uni[0, 1], d0["qn"], uni[0, 2],
                         mode=mode, temperature=T, sampler=args.sampler, top_k=args.top_k,
                         top_p=args.top_p)
+    tails = []
+    for o in timed_out:
+        call.bind_out(o)
+        tails.append(call._tail)
 
     def bind(i):
         t = dev_sets[i % nsets]
         call.bind(t["p"], t["q"], t["x"], uni[i, 0], uni[i, 1], t["qn"], uni[i, 2])
 
     stream = torch.cuda.current_stream()
+    call.bind_out(outputs())
     for i in range(args.warmup):
         bind(i)
         call()
@@ -412,8 +532,9 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
-        bind(args.warmup + i)
+    for n in range(args.steps):
+        bind(args.warmup + n)
+        call._tail = tails[n]
         call()
     ev1.record(stream)
     torch.cuda.synchronize()
@@ -421,21 +542,11 @@ def main():
     isd.check_device_error(call.ws)
     kernel_avg_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # untimed pass over the same steps for workload statistics
-    n_stat = min(args.steps, 50)
-    accept = torch.empty((n_stat, C), dtype=torch.int32, device=dev)
-    alphas = torch.empty((n_stat, C), dtype=torch.float32, device=dev)
-    for i in range(n_stat):
-        bind(args.warmup + i)
-        call()
-        accept[i].copy_(call.out["accept_len"])
-        alphas[i].copy_(call.out["alpha"])
-    torch.cuda.synchronize()
-
+    gpu = {k: np.stack([o[k].cpu().numpy() for o in timed_out]) for k in timed_out[0]}
     ms_per_step = wall * 1e3 / args.steps
     positions = C * L
     # rows the step reads once: anchor p, proposal q (sample mode only), mask qn
-    bytes_alg = (2 if mode == "greedy" else 3) * C * L * V * 2
+    bytes_alg = (2 if mode == "greedy" else 3) * C * L * V * es
     achieved = bytes_alg / (kernel_avg_ms * 1e-3) / 1e9
 
     traffic = None
@@ -446,41 +557,72 @@ def main():
                 and tr.get("sampler", "cdf") == args.sampler and args.top_k == 0):
             traffic = tr.get("bytes_per_launch")
 
-    acc = accept.cpu().numpy()
-    result = dict(
-        metric="ISD verified positions/sec at C=64,L=8,V=151936 bf16; achieved HBM GB/s"
-        if args.config == 2 else f"ISD verified positions/sec ({cfg['name']} workload)",
-        value=round(positions / (ms_per_step * 1e-3), 1),
-        unit="positions/s",
-        n_gpus=1,
-        steps=args.steps,
-        warmup=args.warmup,
-        ms_per_step=round(ms_per_step, 5),
-        higher_is_better=True,
-        scaling="weak",
-        vs_baseline=None,
-        dtype="f32",
-        data="synthetic",
-        config=dict(workload=f"{cfg['name']} ISD step: C={C}, L={L}, V={V}, bf16 logits, "
-                             f"{'greedy' if mode == 'greedy' else f'T={T}'}",
-                    C=C, L=L, V=V, logits_dtype="bf16", mode=mode, sampler=args.sampler,
-                    top_k=args.top_k, top_p=args.top_p,
-                    input_sets=nsets,
-                    parallelism="single GPU"),
+    hist = np.bincount(gpu["accept_len"].ravel().clip(0, L), minlength=L + 1)
+    workload = (f"{cfg['name']} ISD step: C={C}, L={L}, V={V}, {dt} logits, "
+                f"{'greedy' if mode == 'greedy' else f'T={T}'}")
+    if tiny:
+        us = ms_per_step * 1e3
+        result = dict(metric="ISD step latency, tiny workload (C=1, L=4, V=1000, fp32 logits)",
+                      value=round(us, 3), unit="us/step", higher_is_better=False)
+    else:
+        result = dict(metric="ISD verified positions/sec at C=64,L=8,V=151936 bf16; achieved HBM GB/s"
+                      if args.config == 2 else f"ISD verified positions/sec ({cfg['name']} workload)",
+                      value=round(positions / (ms_per_step * 1e-3), 1), unit="positions/s",
+                      higher_is_better=True)
+    result.update(
+        n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=round(ms_per_step, 5),
+        scaling="weak", vs_baseline=None, dtype="f32", data="synthetic",
+        config=dict(workload=workload, C=C, L=L, V=V, logits_dtype=dt, mode=mode,
+                    sampler=args.sampler, top_k=args.top_k, top_p=args.top_p,
+                    input_sets=nsets, parallelism="single GPU"),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic),
+        read_probe=dict(gbs=round(probe_gbs, 1), frac_of_peak=round(probe_gbs / HBM_PEAK_GBS, 4),
+                        step_frac_of_probe=round(achieved / probe_gbs, 4)),
         hbm_gbs_wall=round(bytes_alg / (ms_per_step * 1e-3) / 1e9, 1),
         kernel_us_avg=round(kernel_avg_ms * 1e3, 2),
         bytes_per_step=bytes_alg,
-        accept_len_mean=round(float(acc.mean()), 4),
-        alpha_mean=round(float(alphas.mean().item()), 5),
+        accept_len_mean=round(float(gpu["accept_len"].mean()), 4),
+        accept_len_hist=hist.tolist(),
+        alpha_mean=round(float(gpu["alpha"].mean()), 5),
     )
     if not args.no_cpu_baseline:
-        print("# timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(host_sets, cfg, args.cpu_seconds)
+        print("# running the CPU oracle on the timed steps", file=sys.stderr, flush=True)
+        _HOST.update(sets=host_sets, uni=uni_host, dtype=dt, mode=mode, T=T,
+                     args=dict(sampler=args.sampler, top_k=args.top_k, top_p=args.top_p),
+                     set_of=[(args.warmup + n) % nsets for n in range(args.steps)],
+                     step_of=[args.warmup + n for n in range(args.steps)])
+        result["cpu_baseline"], result["check"] = check_and_time_oracle(
+            gpu, args.steps, cfg, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps(dict(error="this build runs on one GPU: the ISD step is measured "
+                                    "on a single MI355X; multi-GPU runs are not supported",
+                              n_gpus=args.gpus)))
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.probe:
+        gbs = read_probe()
+        print(json.dumps(dict(metric="streaming read rate, step tile loader, 1 GiB",
+                              value=round(gbs, 1), unit="GB/s",
+                              frac_of_peak=round(gbs / HBM_PEAK_GBS, 4))), flush=True)
+        return
+    if args.config == 4:
+        lm_head_workload(args)
+        return
+    if args.config == 6:
+        lora_workload(args)
+        return
+    step_workload(args)
 
 
 if __name__ == "__main__":

@@ -33,8 +33,14 @@
  * Workspace.  Size it with isd_workspace_bytes() for the same shape.  It must
  *   be zero-filled before its first use; every call leaves it zero-filled
  *   again once its kernels have finished (it holds work counters and
- *   per-row partial results).  One workspace serves one call at a time:
- *   calls that share a workspace must be ordered on one stream.
+ *   per-row partial results).  So the workspace carries state from one call
+ *   to the next: its zero state.  A decision published inside a launch is
+ *   tagged with that launch's epoch (a library-wide counter), so a record
+ *   left behind by a launch that flagged the device error word can never be
+ *   taken for a later launch's; the workspace must still be zero-filled again
+ *   after isd_check_device_error() returns ISD_ERR_DEVICE.  One workspace
+ *   serves one call at a time: calls that share a workspace must be ordered
+ *   on one stream; calls that overlap on one workspace race.
  * Asynchrony.  Every call validates its arguments on the host, enqueues its
  *   kernels on `stream` (a hipStream_t; NULL is the null stream) and returns;
  *   outputs are valid once the stream has reached that point.
@@ -43,9 +49,13 @@
  *   proposals are inverse-CDF draws over ascending vocab index: the token is
  *   the smallest i whose running weight sum exceeds u * (total weight).
  * Precision.  Streaming sums are fp32 per 32-element lane block, accumulated
- *   in fp64; decisions use fp64 ratios.  Results match an exact fp64
- *   evaluation up to ~1e-7 relative, so only draws within ~1e-6 of a
- *   decision boundary can come out differently.
+ *   in fp64; decisions use fp64 ratios.  Residual weights are formed as
+ *   a_i - rho*b_i with the ratio of the two rows' denominators carried as a
+ *   pair of fp32 numbers, so no row-wide rounding enters the difference.
+ *   Probabilities match an exact fp64 evaluation to ~1e-7 relative; a
+ *   residual draw's cumulative weights agree to ~1e-7 * P_max / Z (P_max the
+ *   anchor row's largest probability, Z the residual mass), so only draws
+ *   within ~1e-6 of a boundary come out differently unless Z is below ~0.01.
  * Errors.  On a non-OK status nothing has been enqueued and no output or
  *   workspace byte is touched; isd_last_error() then describes the problem.
  *     ISD_ERR_ARG          bad shape (C < 1, L not in [1, 64], V < 1, ld < V,
@@ -286,7 +296,23 @@ isd_status_t isd_lm_head_pack(const void *w, int32_t K, int32_t N, void *wt, voi
  * must be zero-filled again before reuse. */
 isd_status_t isd_check_device_error(void *workspace, size_t ws_bytes, void *stream);
 
-/* Tuning knobs, process-wide; 0 restores the automatic choice.
+/* Measurement: a streaming-read probe.  Reads the `bytes` bytes at `buf`
+ * (device memory, 16-byte aligned; bytes a multiple of 4096 and at most
+ * 2^31 elements of 2 bytes) once, with the step kernel's own tile loader:
+ * each workgroup streams `tiles_per_group` consecutive 4 KiB tiles (the
+ * step's verify segments are 38).  Nothing is written except, with
+ * negligible probability, one word at `sink` (device memory).  Its time over
+ * `bytes` is the read rate the step's loop can reach on the device, the
+ * practical ceiling beside the HBM peak ("Introspective Diffusion Language
+ * Models | Summary", section 2: decoding speed is bound by memory
+ * bandwidth).  ISD_ERR_ARG for bad sizes or pointers, ISD_ERR_DEVICE if the
+ * launch fails. */
+isd_status_t isd_read_probe(const void *buf, size_t bytes, int32_t tiles_per_group,
+                            uint32_t *sink, void *stream);
+
+/* Tuning knobs, process-wide (they apply to every later call of every
+ * thread; the calls themselves stay reentrant); 0 restores the automatic
+ * choice.
  *   segments          workgroups sharing one verify row (1..32)
  *   propose_segments  workgroups sharing one mask row (1..32)
  *   resid_segments    workgroups sharing one residual row pair (1..64)

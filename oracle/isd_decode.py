@@ -7,9 +7,10 @@ and it imports nothing from the product path.
 Sources (cited by page title and section):
 
 * "Introspective Diffusion Language Models | Summary", section 3.2
-  "Introspective Strided Decoding (ISD)": when every proposal passes, one more
-  token can be drawn from the final causal anchor; after a rejection the next
-  step only proposes, with no speculative suffix to verify.
+  "Introspective Strided Decoding (ISD)": the loop around the step.  A step
+  whose L proposals all pass (accept_len == L) also yields a bonus token from
+  its anchor row L; a step with a rejection leaves the sequence in a state
+  whose next step verifies nothing and only makes proposals.
 * same page, section 3.2 (tokens per forward) and appendix B "TPF and Compute
   Overhead Analysis": with cumulative acceptance probabilities P_k the tokens
   per forward of stride N are (2 + P_1 + ... + P_{N-2}) / (2 - P_{N-1}); under

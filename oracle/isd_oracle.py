@@ -96,6 +96,18 @@ def softmax(logits: np.ndarray, temperature: float = 1.0) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def cdf_interval(weights: np.ndarray, index: int):
+    """The interval [cum_{i-1} / Z, cum_i / Z] of token i in the inverse-CDF
+    draw over ``weights`` [V] (cum the running sum in ascending index, Z the
+    total, cum_{-1} = 0): the uniforms u for which the draw picks i are those
+    with cum_{i-1} <= u Z < cum_i."""
+    w = np.asarray(weights, dtype=np.float64)
+    cum = np.cumsum(w)
+    total = cum[-1]
+    lo = cum[index - 1] if index > 0 else 0.0
+    return lo / total, cum[index] / total
+
+
 def inverse_cdf(weights: np.ndarray, u: np.ndarray):
     """Inverse-CDF draw over ascending index, batched over leading axes.
 
@@ -263,6 +275,17 @@ def accept_ratio(px: np.ndarray, qx: np.ndarray) -> np.ndarray:
 # Sample mode
 # ---------------------------------------------------------------------------
 
+def residual_weights(P, Q):
+    """Weights of the correction draw ("Introspective Diffusion Language
+    Models | Summary", section 3.2): R = max(0, P - Q) over the last axis,
+    unnormalised.  Returns (W, fallback): where the residual mass is 0 (P and
+    Q equal) W is P instead and fallback is True."""
+    P = np.asarray(P, dtype=np.float64)
+    R = np.maximum(0.0, P - np.asarray(Q, dtype=np.float64))
+    fallback = R.sum(axis=-1) == 0
+    return np.where(fallback[..., None], P, R), fallback
+
+
 def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False,
                   sampler="cdf", seq_ids=None, top_k=0, top_p=1.0):
     """ISD verification of proposals ``x`` against the anchor, batched.
@@ -329,12 +352,8 @@ def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False,
     rows = np.nonzero(j < L)[0]
     if rows.size:
         jj = j[rows]
-        Pj = P[rows, jj]
-        Qj = Q[rows, jj]
-        R = np.maximum(0.0, Pj - Qj)
-        Z = R.sum(axis=-1)
-        resid_fallback[rows] = Z == 0
-        W = np.where((Z == 0)[:, None], Pj, R)
+        W, fallback = residual_weights(P[rows, jj], Q[rows, jj])
+        resid_fallback[rows] = fallback
         if sampler == "gumbel":
             ids = np.arange(B) if seq_ids is None else np.asarray(seq_ids)
             bits = np.asarray(ur, dtype=np.float32).view(np.uint32)
@@ -350,7 +369,7 @@ def verify_sample(p, q, x, ua, ur, temperature=1.0, relax=0.0, q_onehot=False,
         else:
             raise ValueError(f"unknown sampler {sampler!r}")
         out[rows, jj] = tok
-        resid_margin[rows] = np.where(Z == 0, 0.0, margin)
+        resid_margin[rows] = np.where(fallback, 0.0, margin)
 
     flagged = (decision_margin < TIE_WINDOW) | (trunc_margin < TRUNC_WINDOW)
     resid_flagged = (resid_margin < TIE_WINDOW) | resid_fallback

@@ -29,6 +29,7 @@ from .isd import (  # noqa: F401
     make_shape,
     propose,
     propose_masked,
+    read_probe,
     set_trunc_tuning,
     set_tuning,
     step,

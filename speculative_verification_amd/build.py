@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libisd.so")
 SOURCES = ["isd_step.hip", "isd_trunc.hip", "isd_fused.hip", "isd_lm_head.hip", "isd_decode.hip",
-           "isd_api.hip"]
+           "isd_probe.hip", "isd_api.hip"]
 ARCH = "gfx950"
 
 

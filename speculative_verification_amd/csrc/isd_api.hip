@@ -38,6 +38,15 @@ constexpr int kResidTilesPerSeg = 8;
 constexpr int kTruncTargetItems = 1024;
 constexpr int kItemOrder = 0;
 std::atomic<long long> g_spin_limit{0};
+// Launch epochs: every launch that publishes decisions takes the next nonzero
+// value, so decisions of two launches that share a workspace never match.
+std::atomic<uint32_t> g_epoch{0};
+
+uint32_t next_epoch() {
+    uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    while (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    return e;
+}
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -209,6 +218,7 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
     const long long spin = g_spin_limit.load();
     a.spin_limit = spin > 0 ? (uint32_t)(spin < (long long)UINT32_MAX ? spin : (long long)UINT32_MAX)
                             : kDefaultSpinLimit;
+    a.epoch = next_epoch();
 
     const bool vec = vec_ok(s, a.p, a.q, a.qn);
     hipError_t e = hipSuccess;
@@ -697,6 +707,23 @@ isd_status_t isd_set_trunc_tuning(int32_t segments) {
     if (segments < 0 || segments > kMaxTruncSegments)
         return fail(ISD_ERR_ARG, "segments must be in [0, %d]", kMaxTruncSegments);
     g_trunc_segments.store(segments);
+    return ISD_OK;
+}
+
+isd_status_t isd_read_probe(const void *buf, size_t bytes, int32_t tiles_per_group,
+                            uint32_t *sink, void *stream) {
+    ISD_TRY(check_ptr(buf, "buf", 16));
+    ISD_TRY(check_ptr(sink, "sink", 4));
+    const size_t tile_bytes = (size_t)kTileElems * 2;
+    if (bytes == 0 || bytes % tile_bytes)
+        return fail(ISD_ERR_ARG, "bytes must be a positive multiple of %zu", tile_bytes);
+    if (bytes / tile_bytes > (size_t)INT32_MAX / kTileElems)
+        return fail(ISD_ERR_ARG, "bytes too large (%zu)", bytes);
+    if (tiles_per_group < 1 || tiles_per_group > 4096)
+        return fail(ISD_ERR_ARG, "tiles_per_group must be in [1, 4096]");
+    const hipError_t e = launch_read_probe(buf, (long long)(bytes / tile_bytes), tiles_per_group,
+                                           sink, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "probe launch failed: %s", hipGetErrorString(e));
     return ISD_OK;
 }
 

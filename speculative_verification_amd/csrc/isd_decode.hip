@@ -1,8 +1,10 @@
 // Bookkeeping of the multi-step decoding loop around the ISD step
-// ("Introspective Diffusion Language Models | Summary", section 3.2: after all
-// proposals pass, one more token comes from the final causal anchor; after a
-// rejection the next step only proposes).  One thread per sequence; the
-// step, bonus and anchor draws themselves are the step kernel's.
+// ("Introspective Diffusion Language Models | Summary", section 3.2).  A
+// sequence in the verify state that keeps all L proposals (accept_len == L)
+// also takes a bonus token from its anchor row L; one that rejects moves to
+// the recovery state, whose next step draws no verification and only makes
+// proposals.  One thread per sequence; the step, bonus and anchor draws
+// themselves are the step kernel's.
 
 #include "isd_internal.h"
 

@@ -422,6 +422,32 @@ __device__ __forceinline__ uint32_t *counter(uint32_t *base, int i) {
     return base + (size_t)i * kCounterStride;
 }
 
+// Publishes sequence c's decision for its residual items (one lane): j, the
+// residual draw's uniform, the references and denominators of rows p[c, j]
+// and q[c, j], and their ratio Sp / Sq as rho_hi + rho_lo (both fp32, the
+// second holding what the first rounds away), then the flag.  The flag holds
+// the launch's epoch, so a flag left over from an earlier launch never
+// releases a wait of this one.
+__device__ __forceinline__ void publish_decision(const StepArgs &a, int c, int j, float u, float cp, float cq,
+                                 double sp, double sq, int xj) {
+    SeqInfo *si = &a.ws.info[c];
+    const double rho = sq > 0.0 ? sp / sq : 0.0;
+    const float rho_hi = (float)rho;
+    const float rho_lo = (float)(rho - (double)rho_hi);
+    st32(reinterpret_cast<uint32_t *>(&si->j), (uint32_t)j);
+    st32(reinterpret_cast<uint32_t *>(&si->u), __float_as_uint(u));
+    st32(reinterpret_cast<uint32_t *>(&si->cp), __float_as_uint(cp));
+    st32(reinterpret_cast<uint32_t *>(&si->cq), __float_as_uint(cq));
+    st32(reinterpret_cast<uint32_t *>(&si->inv_sp), __float_as_uint(sp > 0.0 ? (float)(1.0 / sp) : 0.0f));
+    st32(reinterpret_cast<uint32_t *>(&si->inv_sq), __float_as_uint(sq > 0.0 ? (float)(1.0 / sq) : 0.0f));
+    st32(reinterpret_cast<uint32_t *>(&si->xj), (uint32_t)xj);
+    st32(reinterpret_cast<uint32_t *>(&si->rho_hi), __float_as_uint(rho_hi));
+    st32(reinterpret_cast<uint32_t *>(&si->rho_lo), __float_as_uint(rho_lo));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    st32(counter(a.ws.flag, c), a.epoch);
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10
 // ---------------------------------------------------------------------------

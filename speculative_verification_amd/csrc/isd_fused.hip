@@ -163,19 +163,7 @@ __global__ __launch_bounds__(kDecideWaves * kWave) void fused_decide_kernel(Step
     const double jsp = __shfl(sp, src), jsq = __shfl(sq, src);
     const int jx = __shfl(xk, src);
     if (lane == 0) {
-        SeqInfo *si = &a.ws.info[c];
-        st32(reinterpret_cast<uint32_t *>(&si->j), (uint32_t)j);
-        st32(reinterpret_cast<uint32_t *>(&si->u), __float_as_uint(j < L ? a.ur[c * L + j] : 0.0f));
-        st32(reinterpret_cast<uint32_t *>(&si->cp), __float_as_uint(jcp));
-        st32(reinterpret_cast<uint32_t *>(&si->cq), __float_as_uint(jcq));
-        st32(reinterpret_cast<uint32_t *>(&si->inv_sp),
-             __float_as_uint(jsp > 0.0 ? (float)(1.0 / jsp) : 0.0f));
-        st32(reinterpret_cast<uint32_t *>(&si->inv_sq),
-             __float_as_uint(jsq > 0.0 ? (float)(1.0 / jsq) : 0.0f));
-        st32(reinterpret_cast<uint32_t *>(&si->xj), (uint32_t)jx);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_s_waitcnt(0);
-        st32(counter(a.ws.flag, c), 1u);
+        publish_decision(a, c, j, j < L ? a.ur[c * L + j] : 0.0f, jcp, jcq, jsp, jsq, jx);
         if (a.alpha) a.alpha[c] = alpha;
         a.accept_len[c] = j;
         a.n_emitted[c] = j + (j < L ? 1 : 0);

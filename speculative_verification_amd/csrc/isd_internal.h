@@ -59,7 +59,7 @@ struct TileRec {               // mass of one 2048-element tile of a mask row
     float sum;                 // sum of 2^(x*k2 - ref) over the tile
 };
 
-struct ResTile {               // masses of one tile of a residual row pair
+struct ResTile {               // masses of one tile of a residual row pair, in units of 1/Sp
     float r;                   // sum of max(0, P - Q)
     float p;                   // sum of P (used only if the residual is empty)
 };
@@ -71,13 +71,14 @@ struct SeqInfo {               // per-sequence decision, read by residual items
     float inv_sp, inv_sq;      // 1 / softmax denominators of those rows
     float alpha;
     int32_t xj;                // x[c, j] (the argmax pick removed from the residual)
+    float rho_hi, rho_lo;      // Sp / Sq of those rows as an unevaluated fp32 sum
 };
 
 struct Workspace {
     Control *ctl;
     uint32_t *seq_cnt;         // [C]     pq items finished per sequence      (strided)
     uint32_t *res_cnt;         // [C]     residual items finished per sequence (strided)
-    uint32_t *flag;            // [C]     decision published (1) for sequence c (strided)
+    uint32_t *flag;            // [C]     decision published for sequence c: the launch's epoch (strided)
     uint32_t *row_cnt;         // [C*L]   mask-row items finished per row      (strided)
     SegRec *seg;               // [2*C*L*Smax] sample: p rows then q rows
     ArgRec *arg;               // [2*C*L*Smax] greedy: p rows then mask rows (aliases seg)
@@ -148,6 +149,7 @@ struct StepArgs {
     int verify_outputs;        // write tokens / counts (0: alpha only)
     int order;                 // 0: per sequence [mask rows, residual]; 1: all mask rows first
     uint32_t spin_limit;
+    uint32_t epoch;            // nonzero tag of this launch: the value a published decision carries
     // truncated path
     int St, tpst;              // segments per row, tiles per segment
     TruncWorkspace tws;
@@ -194,6 +196,11 @@ hipError_t launch_lm_head_stats(const uint16_t *h, const uint16_t *wt, int M, in
 hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t *wcat,
                             const int32_t *mask, int M, int K, int N, int r, uint16_t *t,
                             uint16_t *out, hipStream_t stream);
+
+// Streaming-read probe over n_tiles 2048-element bf16 tiles (4 KiB each),
+// tiles_per_group consecutive tiles per workgroup.
+hipError_t launch_read_probe(const void *buf, long long n_tiles, int tiles_per_group,
+                             uint32_t *sink, hipStream_t stream);
 
 // LM-head GEMM (bf16 in, fp32 accumulate, bf16 out).
 hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, int N,

@@ -310,8 +310,8 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
         __syncthreads();
         // the logits leave the staged tile as 16-byte row chunks (a row's 16
         // chunks are consecutive threads), or element by element at a ragged
-        // or unaligned edge
-        const bool vec_out = (N % 8) == 0;
+        // edge or when the output rows are not 16-byte aligned
+        const bool vec_out = (N % 8) == 0 && ((uintptr_t)out % 16) == 0;
 #pragma unroll 4
         for (int q = tid; q < kPBM * (BN / 8); q += kThr) {
             const int rl = q / (BN / 8), c8 = (q % (BN / 8)) * 8;

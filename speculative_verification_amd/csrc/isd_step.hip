@@ -390,22 +390,9 @@ __device__ __forceinline__ void decide(const StepArgs &a, int c, int lane) {
             const float jcp = __shfl(cp, src), jcq = __shfl(cq, src);
             const double jsp = __shfl(sp, src), jsq = __shfl(sq, src);
             const int jx = __shfl(xk, src);
-            if (lane == 0) {
-                SeqInfo *si = &a.ws.info[c];
-                st32(reinterpret_cast<uint32_t *>(&si->j), (uint32_t)j);
-                st32(reinterpret_cast<uint32_t *>(&si->u),
-                     __float_as_uint((j < L && a.ur) ? a.ur[c * L + j] : 0.0f));
-                st32(reinterpret_cast<uint32_t *>(&si->cp), __float_as_uint(jcp));
-                st32(reinterpret_cast<uint32_t *>(&si->cq), __float_as_uint(jcq));
-                st32(reinterpret_cast<uint32_t *>(&si->inv_sp),
-                     __float_as_uint(jsp > 0.0 ? (float)(1.0 / jsp) : 0.0f));
-                st32(reinterpret_cast<uint32_t *>(&si->inv_sq),
-                     __float_as_uint(jsq > 0.0 ? (float)(1.0 / jsq) : 0.0f));
-                st32(reinterpret_cast<uint32_t *>(&si->xj), (uint32_t)jx);
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                __builtin_amdgcn_s_waitcnt(0);
-                st32(counter(a.ws.flag, c), 1u);
-            }
+            if (lane == 0)
+                publish_decision(a, c, j, (j < L && a.ur) ? a.ur[c * L + j] : 0.0f, jcp, jcq, jsp,
+                                 jsq, jx);
         }
         if (lane == 0 && a.verify_outputs) {
             a.accept_len[c] = j;
@@ -763,6 +750,35 @@ __device__ __forceinline__ int gumbel_finish(ArgRec *rec, int n, int lane) {
     return tok == INT_MAX ? 0 : tok;
 }
 
+// ---------------------------------------------------------------------------
+// Residual weights
+// ---------------------------------------------------------------------------
+//
+// The correction draws from max(0, P - Q) over row j.  In units of the anchor
+// row's denominator Sp the weight of entry i is d_i = a_i - rho * b_i, with
+// a_i = 2^(p_i*k2 - cp), b_i = 2^(q_i*k2 - cq) and rho = Sp / Sq; a_i is the
+// entry's weight under P.  Where P and Q nearly agree, d_i is a small
+// difference of two large terms, and a rounding of the row constant would
+// shift every entry of the residual the same way: rho enters as
+// rho_hi + rho_lo (two fused multiply-adds), so no row-wide rounding is left
+// and the error of d_i is that of the entry's own two exponentials.
+
+struct ResidForm {
+    float k2, cp, cq, rho_hi, rho_lo;
+};
+
+__device__ __forceinline__ ResidForm resid_form(const SeqInfo &inf, float k2) {
+    return ResidForm{k2, inf.cp, inf.cq, inf.rho_hi, inf.rho_lo};
+}
+
+// Residual weight max(0, d) of one entry; a_out gets its P weight a.
+__device__ __forceinline__ float resid_weight(float vp, float vq, const ResidForm &f, float &a_out) {
+    const float a = fast_exp2(fmaf(vp, f.k2, -f.cp));
+    const float b = fast_exp2(fmaf(vq, f.k2, -f.cq));
+    a_out = a;
+    return fmaxf(fmaf(-f.rho_lo, b, fmaf(-f.rho_hi, b, a)), 0.0f);
+}
+
 template <typename T, bool VEC>
 __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shared &sh, int wave,
                                          int lane) {
@@ -772,7 +788,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         uint32_t polls = 0;
         bool ok = true;
         uint32_t *flag = counter(a.ws.flag, c);
-        while (ld32(flag) == 0u) {
+        while (ld32(flag) != a.epoch) {
             __builtin_amdgcn_s_sleep(4);
             if (++polls > a.spin_limit) {
                 atomicOr(&a.ws.ctl->error, kErrWaitExpired);
@@ -789,6 +805,8 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         sh.info.inv_sp = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->inv_sp)));
         sh.info.inv_sq = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->inv_sq)));
         sh.info.xj = (int)ld32(reinterpret_cast<uint32_t *>(&si->xj));
+        sh.info.rho_hi = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->rho_hi)));
+        sh.info.rho_lo = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->rho_lo)));
     }
     __syncthreads();
     const SeqInfo inf = sh.info;
@@ -831,6 +849,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
                 }
             });
         } else {
+            const ResidForm rf = resid_form(inf, a.k2);
             stream_rows2<T, VEC>(prow, qrow, tb, te, a.V, wave, lane,
                                  [&](const TileRaw<T> &rp, const TileRaw<T> &rq, int tile) {
 #pragma unroll
@@ -839,9 +858,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
 #pragma unroll
                     for (int e = 0; e < kGroupElems; ++e) {
                         const int i = g * kGroupElems + e;
-                        P[e] = fast_exp2(fmaf(elem<T>(rp, i), a.k2, -inf.cp)) * inf.inv_sp;
-                        const float Q = fast_exp2(fmaf(elem<T>(rq, i), a.k2, -inf.cq)) * inf.inv_sq;
-                        R[e] = fmaxf(P[e] - Q, 0.0f);
+                        R[e] = resid_weight(elem<T>(rp, i), elem<T>(rq, i), rf, P[e]);
                     }
                     take(P, R, tile, g);
                 }
@@ -875,6 +892,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
     } else if (j < L) {
         const int tb = seg * a.tpsr;
         const int te = min(a.tiles_row, tb + a.tpsr);
+        const ResidForm rf = resid_form(inf, a.k2);
         stream_rows2<T, VEC>(prow, qrow, tb, te, a.V, wave, lane,
                              [&](const TileRaw<T> &rp, const TileRaw<T> &rq, int tile) {
             float lr = 0.0f, lp = 0.0f;
@@ -884,10 +902,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
 #pragma unroll
                 for (int e = 0; e < kGroupElems; ++e) {
                     const int i = g * kGroupElems + e;
-                    const float P = fast_exp2(fmaf(elem<T>(rp, i), a.k2, -inf.cp)) * inf.inv_sp;
-                    const float Q = fast_exp2(fmaf(elem<T>(rq, i), a.k2, -inf.cq)) * inf.inv_sq;
-                    er[e] = fmaxf(P - Q, 0.0f);
-                    ep[e] = P;
+                    er[e] = resid_weight(elem<T>(rp, i), elem<T>(rq, i), rf, ep[e]);
                 }
                 lr += tree_sum(er);
                 lp += tree_sum(ep);
@@ -935,12 +950,17 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
             if (!a.q_onehot) load_tile<T, VEC>(qrow, tile, a.V, lane, rq);
             const float k2 = a.k2;
             const bool onehot = a.q_onehot != 0;
+            const ResidForm rf = resid_form(inf, k2);
+            // the weights the tile masses summed, entry by entry
             auto weight = [&](int i) -> double {
-                const float P = fast_exp2(fmaf(elem<T>(rp, i), k2, -inf.cp)) * inf.inv_sp;
-                if (use_p) return (double)P;
-                if (onehot) return elem_index(tile, lane, i) == (long long)inf.xj ? 0.0 : (double)P;
-                const float Q = fast_exp2(fmaf(elem<T>(rq, i), k2, -inf.cq)) * inf.inv_sq;
-                return (double)fmaxf(P - Q, 0.0f);
+                if (onehot) {
+                    const float P = fast_exp2(fmaf(elem<T>(rp, i), k2, -inf.cp)) * inf.inv_sp;
+                    if (use_p) return (double)P;
+                    return elem_index(tile, lane, i) == (long long)inf.xj ? 0.0 : (double)P;
+                }
+                float P;
+                const float R = resid_weight(elem<T>(rp, i), elem<T>(rq, i), rf, P);
+                return use_p ? (double)P : (double)R;
             };
             tok = search_tile(weight, tile, lane, before, tile_target);
             if (tok < 0) tok = 0;
@@ -958,6 +978,8 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         st32(reinterpret_cast<uint32_t *>(&si->inv_sp), 0u);
         st32(reinterpret_cast<uint32_t *>(&si->inv_sq), 0u);
         st32(reinterpret_cast<uint32_t *>(&si->xj), 0u);
+        st32(reinterpret_cast<uint32_t *>(&si->rho_hi), 0u);
+        st32(reinterpret_cast<uint32_t *>(&si->rho_lo), 0u);
         st32(counter(a.ws.flag, c), 0u);
     }
 }

@@ -63,6 +63,7 @@ _SIGS = {
     "isd_step_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 10 + [_i64, _i64] +
                        [_vp] * 8 + [_vp, _sz, _vp]),
     "isd_lora_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "isd_read_probe": (ctypes.c_int, [_vp, _sz, _i32, _vp, _vp]),
     "isd_last_error": (ctypes.c_char_p, []),
 }
 
@@ -263,15 +264,26 @@ class StepCall:
         self.ws = workspace(self.shape, dev) if ws is None else ws
         self._fn = lib().isd_step
         self._shape_ref = ctypes.byref(self.shape)
-        o = self.out
-        self._tail = [_ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o["n_emitted"]),
-                      _ptr(o["p_x"]), _ptr(o["q_x"]), _ptr(o["alpha"]), _ptr(o["next_tokens"]),
-                      _ptr(o["qnext_x"]), _ptr(self.ws), self.ws.numel()]
+        self.bind_out(self.out)
         self.bind(p, q, x, ua, ur, qn, up)
 
     def bind(self, p, q, x, ua, ur, qn, up):
         """Point the call at new input tensors of the same shapes."""
         self._head = [_ptr(p), _ptr(q), _ptr(x), _ptr(ua), _ptr(ur), _ptr(qn), _ptr(up)]
+
+    def bind_out(self, o: dict):
+        """Point the call at other output tensors of the same shapes (every key
+        of the constructor's outputs); later calls write there."""
+        C, L = self.shape.C, self.shape.L
+        for key, shape in (("accept_len", (C,)), ("out_tokens", (C, L)), ("n_emitted", (C,)),
+                           ("p_x", (C, L)), ("q_x", (C, L)), ("alpha", (C,)),
+                           ("next_tokens", (C, L)), ("qnext_x", (C, L))):
+            if tuple(o[key].shape) != shape or not o[key].is_contiguous():
+                raise ValueError(f"output {key} must be a contiguous {shape} tensor")
+        self.out = o
+        self._tail = [_ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o["n_emitted"]),
+                      _ptr(o["p_x"]), _ptr(o["q_x"]), _ptr(o["alpha"]), _ptr(o["next_tokens"]),
+                      _ptr(o["qnext_x"]), _ptr(self.ws), self.ws.numel()]
 
     def __call__(self, stream=None):
         s = _stream() if stream is None else ctypes.c_void_p(stream)
@@ -427,8 +439,24 @@ def lm_head_packed(h, wt, out=None):
 
 
 def check_device_error(ws: torch.Tensor):
-    """Synchronise and raise IsdError if a kernel flagged undefined input."""
-    _check(lib().isd_check_device_error(_ptr(ws), ws.numel(), _stream()))
+    """Synchronise and raise IsdError if a kernel flagged undefined input or
+    an expired wait.  A launch that flagged one may have left records in the
+    workspace, so the workspace is zero-filled again before the error is
+    raised (the library's contract for ISD_ERR_DEVICE)."""
+    status = lib().isd_check_device_error(_ptr(ws), ws.numel(), _stream())
+    if status == ISD_ERR_DEVICE:
+        message = lib().isd_last_error().decode()
+        ws.zero_()
+        torch.cuda.current_stream().synchronize()
+        raise IsdError(status, message)
+    _check(status)
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, tiles_per_group: int = 38):
+    """One streaming read of `buf` (a contiguous device tensor, 16-byte
+    aligned, a multiple of 4096 bytes) with the step's tile loader."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().isd_read_probe(_ptr(buf), nbytes, tiles_per_group, _ptr(sink), _stream()))
 
 
 def set_tuning(segments: int = 0, resid_segments: int = 0, spin_limit: int = 0,

@@ -244,3 +244,23 @@ def test_fused_and_stats_validation(isd):
     assert lib.isd_lm_head_stats(FAKE, FAKE, 8, 100, 64, ctypes.c_float(1.0), FAKE, FAKE, None) == 1
     assert lib.isd_lm_head_stats(FAKE, FAKE, 8, 128, 64, ctypes.c_float(0.0), FAKE, FAKE, None) == 1
     assert "temperature" in lib.isd_last_error().decode()
+
+
+@pytest.mark.parametrize("nbytes,tpg,msg", [
+    (0, 38, "multiple of 4096"),
+    (4095, 38, "multiple of 4096"),
+    (4096 * 10 + 2, 38, "multiple of 4096"),
+    (4096, 0, "tiles_per_group"),
+    (4096, 5000, "tiles_per_group"),
+])
+def test_read_probe_rejects_bad_sizes(isd, nbytes, tpg, msg):
+    st = isd.lib().isd_read_probe(FAKE, nbytes, tpg, FAKE, None)
+    assert st == 1
+    assert msg in isd.lib().isd_last_error().decode()
+
+
+def test_read_probe_rejects_misaligned_or_null(isd):
+    assert isd.lib().isd_read_probe(ctypes.c_void_p(0x10008), 4096, 38, FAKE, None) == 1
+    assert "aligned" in isd.lib().isd_last_error().decode()
+    assert isd.lib().isd_read_probe(FAKE, 4096, 38, None, None) == 1
+    assert "NULL" in isd.lib().isd_last_error().decode()

@@ -13,14 +13,18 @@ test also checks that the GPU wrote exactly those bits.
   and with isd_step on the same logits (the path that reads every row).
 """
 
+import os
+
 import numpy as np
 import pytest
 
 from isd_inputs import bf16_bits_to_f32, f32_to_bf16_bits, gen_exact_head
 from oracle import isd_oracle as O
-from tests.isd_testlib import compare, log, to_host
+from tests.isd_testlib import compare, log, oracle_step, to_host
 
 pytestmark = pytest.mark.gpu
+
+WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 LOG2E = 1.4426950408889634
 
@@ -115,18 +119,11 @@ def _run(isd, C, L, K, V, T, seed, check_rows=None, **variant):
     plain = to_host(isd.step(*args, temperature=T, **variant))
     torch.cuda.synchronize()
 
-    d = dict(p=oc[:, :L], q=op[:, L:], qn=oc[:, L:], x=x[seqs], ua=ua[seqs], ur=ur[seqs],
-             up=up[seqs])
-    ref = {}
-    v = O.verify_sample(O.decode_logits(d["p"], "bf16"),
-                        None if variant.get("q_onehot") else O.decode_logits(d["q"], "bf16"), d["x"],
-                        d["ua"], d["ur"], T, relax=variant.get("relax", 0.0),
-                        q_onehot=variant.get("q_onehot", False),
-                        sampler=variant.get("sampler", "cdf"), seq_ids=seqs)
-    tok, prob, _, pflag = O.propose_sample(O.decode_logits(d["qn"], "bf16"), d["up"], T)
-    ref = dict(accept_len=v["accept_len"], out_tokens=v["out_tokens"], n_emitted=v["n_emitted"],
-               p_x=v["p_x"], q_x=v["q_x"], alpha=v["alpha"], flagged=v["flagged"],
-               resid_flagged=v["resid_flagged"], next_tokens=tok, qnext_x=prob, next_flagged=pflag)
+    d = dict(p=np.ascontiguousarray(oc[:, :L]), q=np.ascontiguousarray(op[:, L:]),
+             qn=np.ascontiguousarray(oc[:, L:]), x=x[seqs], ua=ua[seqs], ur=ur[seqs], up=up[seqs])
+    ref = oracle_step(d, "bf16", "sample", T, relax=variant.get("relax", 0.0),
+                      q_onehot=variant.get("q_onehot", False), sampler=variant.get("sampler", "cdf"),
+                      seq_ids=seqs, workers=WORKERS)
     sub = lambda o: {k: val[seqs] for k, val in o.items()}  # noqa: E731
     st1 = compare(sub(fused), ref, label="fused vs oracle")
     compare(sub(plain), ref, label="plain vs oracle")
@@ -143,20 +140,15 @@ def test_stats_and_fused_step_midsize(isd, T):
 
 
 def test_fused_step_serving_shape(isd):
-    """The serving shape: C=64, L=8, V=151936 from an H=4096 head; every
-    sequence against isd_step on the same logits, two against the oracle."""
-    fused, plain, ref, st, _ = _run(isd, 64, 8, 4096, 151936, 1.0, seed=5, check_rows=[3, 40])
-    ok = ~ref["flagged"]
-    for key in ("accept_len", "n_emitted"):
-        diff = np.nonzero(fused[key] != plain[key])[0]
-        assert diff.size <= 1, f"{key}: fused and plain differ at {diff}"
-    same_next = np.mean(fused["next_tokens"] == plain["next_tokens"])
-    assert same_next >= 0.995, same_next
+    """The serving shape: C=64, L=8, V=151936 from an H=4096 head.  Every
+    sequence of both paths (statistics and plain) against the oracle under
+    the tolerance rule, with flagged cases validated; their probabilities
+    agree with each other to 1e-5."""
+    fused, plain, ref, st, _ = _run(isd, 64, 8, 4096, 151936, 1.0, seed=5)
     np.testing.assert_allclose(fused["p_x"], plain["p_x"], rtol=1e-5, atol=1e-30)
     np.testing.assert_allclose(fused["q_x"], plain["q_x"], rtol=1e-5, atol=1e-30)
     np.testing.assert_allclose(fused["alpha"], plain["alpha"], rtol=1e-5)
-    log(f"fused serving shape: oracle {st}, next tokens equal to the plain path {same_next:.4f}, "
-        f"{int(ok.sum())} unflagged sequences of {ok.size} checked against the oracle")
+    log(f"fused serving shape, all 64 sequences against the oracle: {st}")
 
 
 @pytest.mark.parametrize("variant", [dict(sampler="gumbel"), dict(q_onehot=True, relax=0.5),

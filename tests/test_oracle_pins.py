@@ -430,3 +430,27 @@ def test_bf16_decoding_known_patterns():
     assert vals[4] == 0.0 and vals[5] == 0.0 and np.signbit(vals[5])
     assert vals[6] == 1.5
     assert vals[7] == 2.0 ** -133
+
+
+def test_cdf_interval_hand_case_and_inverse_cdf():
+    # weights 1, 2, 3, 4 (total 10): token i owns [cum_{i-1}, cum_i) / 10
+    w = np.array([1.0, 2.0, 3.0, 4.0])
+    for i, (lo, hi) in enumerate([(0.0, 0.1), (0.1, 0.3), (0.3, 0.6), (0.6, 1.0)]):
+        a, b = O.cdf_interval(w, i)
+        assert abs(a - lo) < 1e-15 and abs(b - hi) < 1e-15
+    # every uniform of a token's interval draws that token
+    rng = np.random.default_rng(3)
+    w = rng.random(50) * (rng.random(50) < 0.7)
+    for u in rng.random(400):
+        t = int(O.inverse_cdf(w, np.array(u))[0])
+        lo, hi = O.cdf_interval(w, t)
+        assert lo <= u < hi and w[t] > 0
+
+
+def test_residual_weights_hand_case_and_fallback():
+    P = np.array([[0.5, 0.3, 0.2, 0.0], [0.25, 0.25, 0.25, 0.25]])
+    Q = np.array([[0.2, 0.4, 0.1, 0.3], [0.25, 0.25, 0.25, 0.25]])
+    W, fb = O.residual_weights(P, Q)
+    np.testing.assert_allclose(W[0], [0.3, 0.0, 0.1, 0.0], atol=1e-15)
+    assert not fb[0] and fb[1]
+    np.testing.assert_array_equal(W[1], P[1])       # equal laws: the draw falls back to P

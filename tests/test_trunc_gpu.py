@@ -57,24 +57,9 @@ def _case(isd, cfg, seed, top_k, top_p, label, *, x_from_q=True, mutate=None, **
 
 def _oracle(d, cfg, top_k, top_p, chunk=8, **variant):
     """oracle_step with truncation (verify and propose both truncated)."""
-    n = d["x"].shape[0]
-    parts = []
-    for s0 in range(0, n, chunk):
-        sl = slice(s0, min(n, s0 + chunk))
-        p = O.decode_logits(d["p"][sl], cfg["dtype"])
-        qn = O.decode_logits(d["qn"][sl], cfg["dtype"])
-        q = None if variant.get("q_onehot") else O.decode_logits(d["q"][sl], cfg["dtype"])
-        v = O.verify_sample(p, q, d["x"][sl], d["ua"][sl], d["ur"][sl], cfg["T"],
-                            relax=variant.get("relax", 0.0), q_onehot=variant.get("q_onehot", False),
-                            sampler=variant.get("sampler", "cdf"),
-                            seq_ids=np.arange(sl.start, sl.stop), top_k=top_k, top_p=top_p)
-        tok, prob, _, pflag = O.propose_sample(qn, d["up"][sl], cfg["T"], top_k=top_k, top_p=top_p)
-        parts.append(dict(accept_len=v["accept_len"], out_tokens=v["out_tokens"],
-                          n_emitted=v["n_emitted"], p_x=v["p_x"], q_x=v["q_x"],
-                          alpha=v["alpha"], flagged=v["flagged"],
-                          resid_flagged=v["resid_flagged"], next_tokens=tok,
-                          qnext_x=prob, next_flagged=pflag))
-    return {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+    return oracle_step(d, cfg["dtype"], "sample", cfg["T"], chunk=chunk,
+                       relax=variant.get("relax", 0.0), q_onehot=variant.get("q_onehot", False),
+                       sampler=variant.get("sampler", "cdf"), top_k=top_k, top_p=top_p)
 
 
 @pytest.mark.parametrize("top_k,top_p", [(50, 0.95), (8, 1.0), (64, 0.5), (1, 1.0), (20, 0.8)])
