@@ -296,6 +296,32 @@ isd_status_t isd_lm_head_pack(const void *w, int32_t K, int32_t N, void *wt, voi
  * must be zero-filled again before reuse. */
 isd_status_t isd_check_device_error(void *workspace, size_t ws_bytes, void *stream);
 
+/* isd_step for callers that cannot allocate or pass memory for a workspace
+ * (code under stream capture into a graph, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, outputs and conventions as
+ * isd_step without workspace and ws_bytes; the kernels keep their counters
+ * and partial results in a fixed 16 MiB device array of the library instead,
+ * one per device, held until the process ends.  The first call on a device
+ * zero-fills that array (one kernel on the null stream, waited for); every
+ * call leaves it zero again.  No call allocates or frees memory.
+ *   device_error  NULL, or device memory for one uint32: after the step, a
+ *                 small kernel on `stream` moves the device error word there
+ *                 (the bits isd_check_device_error describes: 1 proposal id
+ *                 out of range, 2 row without a finite logit, 4 expired
+ *                 wait) and clears it; 0 means none.
+ * Every call on one device shares that device's array: calls that overlap
+ * on one device (other streams or threads) race and must be ordered by the
+ * caller.  Shapes whose isd_workspace_bytes() exceeds 16 MiB are rejected
+ * with ISD_ERR_WORKSPACE before anything is enqueued (the serving step needs
+ * about 1 MiB, C=256, L=16 about 7.4 MiB). */
+isd_status_t isd_step_noalloc(const isd_shape_t *s, const void *p_logits, const void *q_logits,
+                              const int32_t *proposals, const float *u_accept,
+                              const float *u_resid, const void *qnext_logits,
+                              const float *u_propose, int32_t *accept_len, int32_t *out_tokens,
+                              int32_t *n_emitted, float *p_x, float *q_x, float *alpha,
+                              int32_t *next_tokens, float *qnext_x, uint32_t *device_error,
+                              void *stream);
+
 /* Measurement: a streaming-read probe.  Reads the `bytes` bytes at `buf`
  * (device memory, 16-byte aligned; bytes a multiple of 4096 and at most
  * 2^31 elements of 2 bytes) once, with the step kernel's own tile loader:

@@ -35,6 +35,7 @@ from .isd import (  # noqa: F401
     step,
     step_fused,
     step_masked,
+    step_noalloc,
     verify_step,
     workspace,
     workspace_bytes,

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 namespace isd {
 namespace {
@@ -420,14 +421,19 @@ isd_status_t isd_step(const isd_shape_t *s, const void *p_logits, const void *q_
                            q_x, alpha, next_tokens, qnext_x, workspace, ws_bytes, stream);
 }
 
-isd_status_t isd_step_masked(const isd_shape_t *s, const void *p_logits, const void *q_logits,
-                             const int32_t *proposals, const float *u_accept,
-                             const float *u_resid, const void *qnext_logits,
-                             const float *u_propose, const int32_t *verify_mask,
-                             const int32_t *propose_mask, int32_t *accept_len,
-                             int32_t *out_tokens, int32_t *n_emitted, float *p_x, float *q_x,
-                             float *alpha, int32_t *next_tokens, float *qnext_x, void *workspace,
-                             size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace isd {
+namespace {
+
+// Validates the arguments of a fused step and fills `a` with them.
+isd_status_t step_args(const isd_shape_t *s, const void *p_logits, const void *q_logits,
+                       const int32_t *proposals, const float *u_accept, const float *u_resid,
+                       const void *qnext_logits, const float *u_propose,
+                       const int32_t *verify_mask, const int32_t *propose_mask,
+                       int32_t *accept_len, int32_t *out_tokens, int32_t *n_emitted, float *p_x,
+                       float *q_x, float *alpha, int32_t *next_tokens, float *qnext_x,
+                       StepArgs &a) {
     ISD_TRY(check_shape(s, true));
     if (verify_mask) ISD_TRY(check_ptr(verify_mask, "verify_mask", 4));
     if (propose_mask) ISD_TRY(check_ptr(propose_mask, "propose_mask", 4));
@@ -446,7 +452,7 @@ isd_status_t isd_step_masked(const isd_shape_t *s, const void *p_logits, const v
     ISD_TRY(check_ptr(out_tokens, "out_tokens", 4));
     ISD_TRY(check_ptr(n_emitted, "n_emitted", 4));
     ISD_TRY(check_ptr(next_tokens, "next_tokens", 4));
-    StepArgs a = blank_args();
+    a = blank_args();
     a.p = p_logits;
     a.q = (sample && !s->q_onehot) ? q_logits : nullptr;
     a.qn = qnext_logits;
@@ -464,9 +470,33 @@ isd_status_t isd_step_masked(const isd_shape_t *s, const void *p_logits, const v
     a.qnext_x = qnext_x;
     a.vmask = verify_mask;
     a.pmask = propose_mask;
+    return ISD_OK;
+}
+
+Plan step_plan() {
     Plan plan;
     plan.verify = plan.propose = plan.residual = plan.verify_outputs = true;
-    return run(s, plan, a, workspace, ws_bytes, stream);
+    return plan;
+}
+
+}  // namespace
+}  // namespace isd
+
+extern "C" {
+
+isd_status_t isd_step_masked(const isd_shape_t *s, const void *p_logits, const void *q_logits,
+                             const int32_t *proposals, const float *u_accept,
+                             const float *u_resid, const void *qnext_logits,
+                             const float *u_propose, const int32_t *verify_mask,
+                             const int32_t *propose_mask, int32_t *accept_len,
+                             int32_t *out_tokens, int32_t *n_emitted, float *p_x, float *q_x,
+                             float *alpha, int32_t *next_tokens, float *qnext_x, void *workspace,
+                             size_t ws_bytes, void *stream) {
+    StepArgs a;
+    ISD_TRY(step_args(s, p_logits, q_logits, proposals, u_accept, u_resid, qnext_logits,
+                      u_propose, verify_mask, propose_mask, accept_len, out_tokens, n_emitted,
+                      p_x, q_x, alpha, next_tokens, qnext_x, a));
+    return run(s, step_plan(), a, workspace, ws_bytes, stream);
 }
 
 isd_status_t isd_step_fused(const isd_shape_t *s, const void *p_logits, const void *q_logits,
@@ -730,3 +760,105 @@ isd_status_t isd_read_probe(const void *buf, size_t bytes, int32_t tiles_per_gro
 const char *isd_last_error(void) { return g_err; }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The fused step without a caller workspace
+// ---------------------------------------------------------------------------
+//
+// Its kernels keep their counters and partial results in `scratch`, a
+// file-scope device array of fixed size instead of a workspace argument.
+// Each device that runs the library holds its own copy until the process
+// ends.  In host code the array's name only stands for the symbol: the
+// device address comes from hipGetSymbolAddress, taken once per device at
+// that device's first call and kept in scratch_ptr; every kernel argument
+// and copy uses that address.
+
+namespace isd {
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxScratchDevices = 64;
+}  // namespace isd
+
+static __device__ __align__(256) unsigned char scratch[isd::kScratchBytes];
+
+namespace isd {
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+__global__ void scratch_clear_kernel(uint4 *p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Moves the device error word of the scratch to *out and clears it.
+__global__ void scratch_take_error_kernel(Control *ctl, uint32_t *out) {
+    if (threadIdx.x == 0) {
+        const uint32_t e = __hip_atomic_load(&ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctl->error, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *out = e;
+    }
+}
+
+// The current device's scratch address.  The first call on a device takes
+// the symbol's address and zero-fills the array (a kernel on the null
+// stream, waited for, so that every later launch on any stream sees zeros).
+isd_status_t current_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(ISD_ERR_UNSUPPORTED, "device %d: the allocation-free step serves devices 0..%d",
+                    dev, kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(ISD_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        hipLaunchKernelGGL(scratch_clear_kernel, dim3(1024), dim3(256), 0, (hipStream_t)0,
+                           static_cast<uint4 *>(ptr), kScratchBytes / 16);
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)0);
+        if (e != hipSuccess)
+            return fail(ISD_ERR_DEVICE, "clearing the scratch failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ISD_OK;
+}
+
+}  // namespace
+}  // namespace isd
+
+extern "C" isd_status_t isd_step_noalloc(const isd_shape_t *s, const void *p_logits,
+                                         const void *q_logits, const int32_t *proposals,
+                                         const float *u_accept, const float *u_resid,
+                                         const void *qnext_logits, const float *u_propose,
+                                         int32_t *accept_len, int32_t *out_tokens,
+                                         int32_t *n_emitted, float *p_x, float *q_x, float *alpha,
+                                         int32_t *next_tokens, float *qnext_x,
+                                         uint32_t *device_error, void *stream) {
+    StepArgs a;
+    ISD_TRY(step_args(s, p_logits, q_logits, proposals, u_accept, u_resid, qnext_logits,
+                      u_propose, nullptr, nullptr, accept_len, out_tokens, n_emitted, p_x, q_x,
+                      alpha, next_tokens, qnext_x, a));
+    if (device_error) ISD_TRY(check_ptr(device_error, "device_error", 4));
+    const size_t need = workspace_layout(s->C, s->L, s->V, truncated(s)).total;
+    if (need > kScratchBytes)
+        return fail(ISD_ERR_WORKSPACE,
+                    "this shape needs %zu bytes of scratch; the allocation-free step holds %zu "
+                    "(use isd_step with a workspace)", need, kScratchBytes);
+    void *ws = nullptr;
+    ISD_TRY(current_scratch(&ws));
+    ISD_TRY(run(s, step_plan(), a, ws, kScratchBytes, stream));
+    if (device_error) {
+        hipLaunchKernelGGL(scratch_take_error_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                           static_cast<Control *>(ws), device_error);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(ISD_ERR_DEVICE, "error-word launch failed: %s", hipGetErrorString(e));
+    }
+    return ISD_OK;
+}

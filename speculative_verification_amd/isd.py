@@ -64,6 +64,7 @@ _SIGS = {
                        [_vp] * 8 + [_vp, _sz, _vp]),
     "isd_lora_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "isd_read_probe": (ctypes.c_int, [_vp, _sz, _i32, _vp, _vp]),
+    "isd_step_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 16 + [_vp]),
     "isd_last_error": (ctypes.c_char_p, []),
 }
 
@@ -297,6 +298,33 @@ def step(p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, relax=0.0, 
     return StepCall(p, q, x, ua, ur, qn, up, mode=mode, temperature=temperature, relax=relax,
                     q_onehot=q_onehot, sampler=sampler, top_k=top_k, top_p=top_p, out=out,
                     ws=ws)()
+
+
+def step_noalloc(p, q, x, ua, ur, qn, up, *, mode="sample", temperature=1.0, relax=0.0,
+                 q_onehot=False, sampler="cdf", top_k=0, top_p=1.0, out=None, device_error=None):
+    """isd_step on the library's own device scratch (no workspace is passed
+    or allocated by the library).  device_error: optional int32 [1] device
+    tensor that receives the step's device error bits."""
+    m = _mode_code(mode)
+    shape = make_shape(p, m, temperature, relax, q_onehot, sampler, top_k, top_p)
+    _same_layout(shape, qn, "qn", m, temperature)
+    if m == MODE_SAMPLE:
+        _same_layout(shape, q, "q", m, temperature)
+    C, L, dev = shape.C, shape.L, p.device
+    o = dict(accept_len=_out(out, "accept_len", (C,), torch.int32, dev),
+             out_tokens=_out(out, "out_tokens", (C, L), torch.int32, dev),
+             n_emitted=_out(out, "n_emitted", (C,), torch.int32, dev),
+             p_x=_out(out, "p_x", (C, L), torch.float32, dev),
+             q_x=_out(out, "q_x", (C, L), torch.float32, dev),
+             alpha=_out(out, "alpha", (C,), torch.float32, dev),
+             next_tokens=_out(out, "next_tokens", (C, L), torch.int32, dev),
+             qnext_x=_out(out, "qnext_x", (C, L), torch.float32, dev))
+    _check(lib().isd_step_noalloc(ctypes.byref(shape), _ptr(p), _ptr(q), _ptr(x), _ptr(ua),
+                                  _ptr(ur), _ptr(qn), _ptr(up), _ptr(o["accept_len"]),
+                                  _ptr(o["out_tokens"]), _ptr(o["n_emitted"]), _ptr(o["p_x"]),
+                                  _ptr(o["q_x"]), _ptr(o["alpha"]), _ptr(o["next_tokens"]),
+                                  _ptr(o["qnext_x"]), _ptr(device_error), _stream()))
+    return o
 
 
 def step_masked(p, q, x, ua, ur, qn, up, verify_mask=None, propose_mask=None, *, mode="sample",

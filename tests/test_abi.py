@@ -264,3 +264,24 @@ def test_read_probe_rejects_misaligned_or_null(isd):
     assert "aligned" in isd.lib().isd_last_error().decode()
     assert isd.lib().isd_read_probe(FAKE, 4096, 38, None, None) == 1
     assert "NULL" in isd.lib().isd_last_error().decode()
+
+
+def test_step_noalloc_rejects_shapes_beyond_its_scratch(isd):
+    # C=256, L=16 with top-k 50 needs about 65 MiB of records: refused before any device call
+    shape = isd.Shape(256, 16, 151936, 151936, 0, 0, 1.0, 0, 0.0, 0, 0, 50, 0.0)
+    st = isd.lib().isd_step_noalloc(ctypes.byref(shape), *([FAKE] * 15), None, None)
+    assert st == 3
+    msg = isd.lib().isd_last_error().decode()
+    assert "allocation-free" in msg and str(16 << 20) in msg
+
+
+def test_step_noalloc_validates_pointers_first(isd):
+    shape = _shape(isd)
+    args = [FAKE] * 15
+    args[8] = None                                   # out_tokens
+    assert isd.lib().isd_step_noalloc(ctypes.byref(shape), *args, None, None) == 1
+    assert "NULL" in isd.lib().isd_last_error().decode()
+    args = [FAKE] * 15
+    assert isd.lib().isd_step_noalloc(ctypes.byref(shape), *args, ctypes.c_void_p(0x10002),
+                                      None) == 1
+    assert "device_error" in isd.lib().isd_last_error().decode()
