@@ -122,6 +122,7 @@ int64_t seq_stride(const isd_shape_t *s) { return s->ldc ? s->ldc : (int64_t)s->
 
 bool vec_ok(const isd_shape_t *s, const void *a, const void *b, const void *c) {
     const size_t es = elem_size(s);
+    if (s->V % kGroupElems) return false;   // the vector path takes whole 8-element groups only
     if (((size_t)s->ld * es) % 16) return false;
     if (((size_t)seq_stride(s) * es) % 16) return false;
     for (const void *p : {a, b, c})

@@ -155,6 +155,31 @@ __device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
     return v;
 }
 
+// Four independent inclusive prefix sums over the lanes, step by step, so
+// that their DPP chains overlap.
+__device__ __forceinline__ void wave_incl_scan4_d(double (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += dpp_d<0x111>(v[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += dpp_d<0x112>(v[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += dpp_d<0x114>(v[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += dpp_d<0x118>(v[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += dpp_d<0x142, 0xA>(v[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += dpp_d<0x143, 0xC>(v[i]);
+}
+
+// v of lane l (l wave-uniform), read through the scalar unit.
+__device__ __forceinline__ double lane_read_d(double v, int l) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Inclusive prefix sum of 32-bit counts over the lanes (same DPP pattern).
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
     v += dpp_u32<0x111>(v);
@@ -204,22 +229,33 @@ __device__ __forceinline__ uint32_t load_bits(const T *p) {
 
 // One lane's 8-element group at element offset i of `row` (8 consecutive
 // elements); elements at or past V read as -inf and are never loaded.  With
-// VEC the group is one or two 16-byte non-temporal loads when it lies wholly
-// below V: the logits are streamed once, and non-temporal loads keep them
-// from displacing useful cache lines and measurably raise the read rate.
+// VEC the group is one or two 16-byte non-temporal loads: the logits are
+// streamed once, and non-temporal loads keep them from displacing useful
+// cache lines and measurably raise the read rate.  The VEC form is used only
+// for rows whose length V is a multiple of 8, so a group lies either wholly
+// below V (`whole`) or wholly at or past it and needs no element-wise bound
+// checks, whose code would otherwise be inlined at every tile load.
 template <typename T, bool VEC>
 __device__ __forceinline__ void load_group(const T *__restrict__ row, long long i, int V, bool whole,
                                            uint32_t *w) {
     constexpr int kVecPerGroup = kGroupElems * (int)sizeof(T) / 16;   // 1 (bf16) or 2 (fp32)
-    if (VEC && whole) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(row + i);
+    constexpr int kWordsPerGroup = kGroupElems * (int)sizeof(T) / 4;
+    if constexpr (VEC) {
+        if (whole) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(row + i);
 #pragma unroll
-        for (int h = 0; h < kVecPerGroup; ++h) {
-            const u32x4 v = __builtin_nontemporal_load(&src[h]);
-            w[h * 4 + 0] = v.x;
-            w[h * 4 + 1] = v.y;
-            w[h * 4 + 2] = v.z;
-            w[h * 4 + 3] = v.w;
+            for (int h = 0; h < kVecPerGroup; ++h) {
+                const u32x4 v = __builtin_nontemporal_load(&src[h]);
+                w[h * 4 + 0] = v.x;
+                w[h * 4 + 1] = v.y;
+                w[h * 4 + 2] = v.z;
+                w[h * 4 + 3] = v.w;
+            }
+        } else {
+            const uint32_t ninf = sizeof(T) == 2 ? (neg_inf_bits<T>() | (neg_inf_bits<T>() << 16))
+                                                 : neg_inf_bits<T>();
+#pragma unroll
+            for (int k = 0; k < kWordsPerGroup; ++k) w[k] = ninf;
         }
     } else {
 #pragma unroll

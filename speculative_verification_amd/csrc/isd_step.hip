@@ -57,23 +57,45 @@ __device__ __forceinline__ void ld_seg(const SegRec *r, float &ref, double &sum)
     ref = lo_f(ld64(reinterpret_cast<const uint64_t *>(r)));
     sum = __longlong_as_double((long long)ld64(reinterpret_cast<const uint64_t *>(r) + 1));
 }
+// Largest of a lane's 32 elements of a tile, read from the packed words.
+template <typename T>
+__device__ __forceinline__ float tile_max(const TileRaw<T> &r) {
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i += 2) m = fmaxf(m, fmaxf(elem<T>(r, i), elem<T>(r, i + 1)));
+    return m;
+}
+
+// Sum over a lane's 32 elements of 2^(x*k2 - ref): pairwise within each
+// 8-element group, then over the four groups.
+template <typename T>
+__device__ __forceinline__ float tile_exp_sum(const TileRaw<T> &r, float k2, float ref) {
+    float g[kGroupsPerTile];
+#pragma unroll
+    for (int q = 0; q < kGroupsPerTile; ++q) {
+        float e[kGroupElems];
+#pragma unroll
+        for (int i = 0; i < kGroupElems; ++i) e[i] = fast_exp2(fmaf(elem<T>(r, q * kGroupElems + i), k2, -ref));
+        g[q] = tree_sum(e);
+    }
+    return tree_sum(g);
+}
+
 struct LaneSoftmax {
     float ref = kNegInf;   // wavefront-uniform
     double acc = 0.0;      // lane sum relative to 2^ref
 
     // Folds one tile; returns the lane's fp32 tile sum (0 if nothing finite yet).
-    __device__ __forceinline__ float add(const float (&v)[kLaneElems], float k2) {
-        const float lm = max32(v);
+    template <typename T>
+    __device__ __forceinline__ float add(const TileRaw<T> &r, float k2) {
+        const float lm = tile_max<T>(r);
         if (__ballot(lm * k2 > ref)) {
             const float nref = ceilf(wave_max(lm) * k2);
             if (ref != kNegInf) acc *= pow2_int(ref - nref);
             ref = nref;
         }
         if (ref == kNegInf) return 0.0f;
-        float e[kLaneElems];
-#pragma unroll
-        for (int i = 0; i < kLaneElems; ++i) e[i] = fast_exp2(fmaf(v[i], k2, -ref));
-        const float s = tree_sum(e);
+        const float s = tile_exp_sum<T>(r, k2, ref);
         acc += (double)s;
         return s;
     }
@@ -160,13 +182,15 @@ __device__ __forceinline__ void argmax_tile(const TileRaw<T> &r, int tile, int l
 // ---------------------------------------------------------------------------
 //
 // A finisher runs at the tail of the work it completes, so its cost is the
-// number of dependent memory round trips, not bandwidth.  Tile records are
-// visited in chunks of 512 tiles with lane l holding tiles 8l..8l+7 of the
-// chunk (all loaded at once); the crossing tile is loaded once into
-// registers.  A row of up to 512 tiles (V <= 1,048,576) costs two round
-// trips: its records, then its crossing tile.
+// number of dependent memory round trips and the length of its dependent
+// instruction chain, not bandwidth.  Tile records are visited in chunks of
+// 128 tiles with lane l holding tiles 2l and 2l+1 of the chunk (loaded at
+// once); the crossing tile is loaded once into registers.  A row of up to
+// 128 tiles (V <= 262,144) costs two round trips, its records and then its
+// crossing tile, and one wavefront scan over the records gives both the
+// row's total and the crossing tile.
 
-constexpr int kRecPerLane = 8;
+constexpr int kRecPerLane = 2;
 constexpr int kRecChunk = kWave * kRecPerLane;
 
 struct RecChunk {
@@ -261,43 +285,83 @@ __device__ __forceinline__ int row_last_positive(int n, Get &&get, int lane, Mas
     return best;
 }
 
+// The tile where the running mass of the row first exceeds u * total, the
+// mass before it and the target u * total; -1 if rounding leaves the target
+// unreached.  total gets the row's mass.  A row of one chunk takes a single
+// scan; longer rows take a pass for the total, then one to find the tile.
+template <typename Get, typename MassOf>
+__device__ __forceinline__ int row_draw(int n, Get &&get, int lane, MassOf &&mass_of, double u,
+                                        double &total, double &before, double &target) {
+    if (n > kRecChunk) {
+        total = row_total(n, get, lane, mass_of);
+        target = u * total;
+        return row_find(n, get, lane, mass_of, target, before);
+    }
+    RecChunk c;
+    get(0, c);
+    double m[kRecPerLane];
+    const double ls = chunk_masses(c, n, 0, lane, mass_of, m);
+    const double inc = wave_incl_scan_d(ls, lane);
+    total = lane_read_d(inc, kWave - 1);
+    target = u * total;
+    double run = inc - ls;
+    int first = -1;
+    double fb = 0.0;
+#pragma unroll
+    for (int i = 0; i < kRecPerLane; ++i) {
+        if (first < 0 && run + m[i] > target) {
+            first = i;
+            fb = run;
+        }
+        run += m[i];
+    }
+    const unsigned long long hit = __ballot(first >= 0);
+    if (!hit) return -1;
+    const int l = wave_first(hit);
+    before = lane_read_d(fb, l);
+    return l * kRecPerLane + __builtin_amdgcn_readlane(first, l);
+}
+
 // Within one tile held in registers, finds the first vocab index where
-// before + running weight exceeds target; weight(i) is the weight of the
-// lane's element i (group-major, 0..31; 0 past the end of the row).  If
-// rounding leaves the target unreached, returns the last index with positive
-// weight (-1 if none).
+// before + scale * (running weight) exceeds target; weight(i) is the fp32
+// weight of the lane's element i (group-major, 0..31; 0 past the end of the
+// row) and scale a power of two.  Groups are walked in vocab order, eight
+// weights live at a time (a finisher shares the kernel's register budget).
+// If rounding leaves the target unreached, returns the last index with
+// positive weight (-1 if none).
 template <typename W>
 __device__ __forceinline__ long long search_tile(W &&weight, int tile, int lane, double before,
-                                                 double target) {
-    double run = before;
+                                                 double target, double scale = 1.0) {
+    double base = before;
 #pragma unroll
     for (int g = 0; g < kGroupsPerTile; ++g) {
-        double w[kGroupElems];
-        double lsum = 0.0;
+        float w[kGroupElems];
+        double gs = 0.0;
 #pragma unroll
         for (int e = 0; e < kGroupElems; ++e) {
             w[e] = weight(g * kGroupElems + e);
-            lsum += w[e];
+            gs += (double)w[e];
         }
-        const double inc = wave_incl_scan_d(lsum, lane);
-        double c = run + (inc - lsum);
+        const double inc = wave_incl_scan_d(gs, lane);
+        const double rel = (target - base) / scale;   // compared with unscaled running weights
+        double c = inc - gs;
         int first = -1;
 #pragma unroll
         for (int e = 0; e < kGroupElems; ++e) {
-            c += w[e];
-            if (first < 0 && c > target) first = e;
+            c += (double)w[e];
+            if (first < 0 && c > rel) first = e;
         }
         const unsigned long long hit = __ballot(first >= 0);
         if (hit) {
             const int l = wave_first(hit);
-            return elem_index(tile, l, g * kGroupElems + __shfl(first, l));
+            return elem_index(tile, l, g * kGroupElems + __builtin_amdgcn_readlane(first, l));
         }
-        run += __shfl(inc, kWave - 1);
+        base += lane_read_d(inc, kWave - 1) * scale;
     }
     long long last = -1;
 #pragma unroll
     for (int i = 0; i < kLaneElems; ++i)
-        if (weight(i) > 0.0) {
+        if (weight(i) > 0.0f) {
             const long long ei = elem_index(tile, lane, i);
             last = ei > last ? ei : last;
         }
@@ -492,9 +556,7 @@ __device__ __forceinline__ void pq_item(const StepArgs &a, int t, Shared &sh, in
     if (MODE == kSample) {
         LaneSoftmax sm;
         stream_row<T, VEC>(row, tb, te, a.V, wave, lane, [&](const TileRaw<T> &r, int) {
-            float v[kLaneElems];
-            unpack<T>(r, v);
-            sm.add(v, a.k2);
+            sm.add<T>(r, a.k2);
         });
         const double ws = wave_sum_d(sm.acc);
         if (lane == 0) {
@@ -556,9 +618,7 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
         TileRec *tr = a.ws.tiles + (size_t)rowid * a.tiles_row;
         LaneSoftmax sm;
         stream_row<T, VEC>(row, tb, te, a.V, wave, lane, [&](const TileRaw<T> &r, int tile) {
-            float v[kLaneElems];
-            unpack<T>(r, v);
-            const float s = sm.add(v, a.k2);
+            const float s = sm.add<T>(r, a.k2);
             const float ts = wave_sum(s);
             if (lane == 0) st_pair(&tr[tile], pack2(sm.ref, ts));
         });
@@ -589,16 +649,13 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
         };
         int token = 0;
         double S = 0.0;
-        float lv = 0.0f;     // logit of the drawn token
-        bool have_lv = false;
+        double q_tok = 0.0;   // Qn(token) * S
         if (cr == kNegInf) {
             if (lane == 0) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
         } else {
-            S = row_total(nt, get, lane, mass);
-            const double target = (double)a.up[rowid] * S;
-            double before = 0.0;
+            double before = 0.0, target = 0.0;
+            int tile = row_draw(nt, get, lane, mass, (double)a.up[rowid], S, before, target);
             double tile_target = target;
-            int tile = row_find(nt, get, lane, mass, target, before);
             if (tile < 0) {
                 // rounding left the target unreached: clamp to the last positive weight
                 tile = max(0, row_last_positive(nt, get, lane, mass));
@@ -611,40 +668,36 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
 #pragma unroll
             for (int i = 0; i < kRecPerLane; ++i)
                 if (i == tile % kRecPerLane) trec = tc.r[i];
-            const float tref = lo_f(__shfl(trec, owner));
+            const float tref = __uint_as_float(__builtin_amdgcn_readlane((int)(uint32_t)trec, owner));
             const double scale = pow2_int(tref - cr);
             TileRaw<T> raw;
             load_tile<T, VEC>(row, tile, a.V, lane, raw);
             const float k2 = a.k2;
-            auto weight = [&](int i) -> double {
-                return (double)fast_exp2(fmaf(elem<T>(raw, i), k2, -tref)) * scale;
-            };
-            const long long tok = search_tile(weight, tile, lane, before, tile_target);
-            token = tok < 0 ? 0 : (int)tok;
-            if constexpr (sizeof(T) == 2) {
-                if (tok >= 0) {
-                    // the token lies in the crossing tile: take its logit from
-                    // the lane that holds it instead of reading it again (a
-                    // wave-uniform index into the lane's 16 words)
-                    const int off = (int)(tok - (long long)tile * kTileElems);
-                    const int owner = (off % (kWave * kGroupElems)) / kGroupElems;
-                    const int pos = off / (kWave * kGroupElems) * kGroupElems + off % kGroupElems;
-                    const uint32_t word = raw.w[pos >> 1];
-                    const float mine = __uint_as_float((pos & 1) ? (word & 0xFFFF0000u) : (word << 16));
-                    lv = __shfl(mine, owner);
-                    have_lv = true;
-                }
+            auto weight = [&](int i) -> float { return fast_exp2(fmaf(elem<T>(raw, i), k2, -tref)); };
+            const long long tok = search_tile(weight, tile, lane, before, tile_target, scale);
+            if (tok >= 0) {
+                token = (int)tok;
+                // the token lies in the crossing tile: its weight comes from
+                // the lane that holds it (a select over the lane's words:
+                // indexing the array with a run-time value would move it out
+                // of registers)
+                const int off = (int)(tok - (long long)tile * kTileElems);
+                const int holder = (off % (kWave * kGroupElems)) / kGroupElems;
+                const int pos = off / (kWave * kGroupElems) * kGroupElems + off % kGroupElems;
+                float mine = 0.0f;
+#pragma unroll
+                for (int q = 0; q < kLaneElems; ++q) mine = q == pos ? elem<T>(raw, q) : mine;
+                const float lv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), holder));
+                q_tok = (double)fast_exp2(fmaf(lv, k2, -tref)) * scale;
+            } else {
+                q_tok = (double)fast_exp2(fmaf(load_value<T>(row, 0), k2, -cr));
             }
         }
         // the tile masses are consumed: return them to zero
         for (int t = lane; t < a.tiles_row; t += kWave) st_pair(&tr[t], 0);
         if (lane == 0) {
             a.next_tokens[rowid] = token;
-            if (a.qnext_x) {
-                if (S > 0.0 && !have_lv) lv = load_value<T>(row, token);
-                a.qnext_x[rowid] =
-                    S > 0.0 ? (float)(exp2((double)lv * (double)a.k2 - (double)cr) / S) : 0.0f;
-            }
+            if (a.qnext_x) a.qnext_x[rowid] = S > 0.0 ? (float)(q_tok / S) : 0.0f;
         }
     } else {
         float bv = kNegInf;
@@ -750,6 +803,9 @@ __device__ __forceinline__ int gumbel_finish(ArgRec *rec, int n, int lane) {
     return tok == INT_MAX ? 0 : tok;
 }
 
+constexpr int kVarGumbel = 1;   // correction by Gumbel-max (else inverse CDF)
+constexpr int kVarOnehot = 2;   // proposals were argmax picks: Q = onehot(x)
+
 // ---------------------------------------------------------------------------
 // Residual weights
 // ---------------------------------------------------------------------------
@@ -779,9 +835,11 @@ __device__ __forceinline__ float resid_weight(float vp, float vq, const ResidFor
     return fmaxf(fmaf(-f.rho_lo, b, fmaf(-f.rho_hi, b, a)), 0.0f);
 }
 
-template <typename T, bool VEC>
+// VAR bit 0: Gumbel-max correction; bit 1: one-hot proposal law (q not read).
+template <typename T, bool VEC, int VAR>
 __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shared &sh, int wave,
                                          int lane) {
+    constexpr bool GUMBEL = (VAR & kVarGumbel) != 0, ONEHOT = (VAR & kVarOnehot) != 0;
     if (a.vmask && a.vmask[c] == 0) return;   // no decision is taken for c
     // wait for sequence c's decision
     if (threadIdx.x == 0) {
@@ -816,7 +874,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
     const T *prow = static_cast<const T *>(a.p) + row_offset(a, c, j < L ? j : 0);
     const T *qrow = static_cast<const T *>(a.q) + row_offset(a, c, j < L ? j : 0);
 
-    if (j < L && a.sampler) {
+    if (GUMBEL && j < L) {
         // Gumbel-max partials of this segment: best R / E and best P / E
         const uint32_t k0 = __float_as_uint(inf.u), k1 = (uint32_t)c;
         float br = 0.0f, bp = 0.0f;
@@ -834,7 +892,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         };
         const int tb = seg * a.tpsr;
         const int te = min(a.tiles_row, tb + a.tpsr);
-        if (a.q_onehot) {
+        if (ONEHOT) {
             stream_row<T, VEC>(prow, tb, te, a.V, wave, lane, [&](const TileRaw<T> &rp, int tile) {
 #pragma unroll
                 for (int g = 0; g < kGroupsPerTile; ++g) {
@@ -866,7 +924,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         }
         gumbel_publish(sh, wave, lane, br, ir, bp, ip,
                        a.ws.garg + ((size_t)c * kMaxResidSegments + seg) * 2);
-    } else if (j < L && a.q_onehot) {
+    } else if (ONEHOT && j < L) {
         // Q is one-hot at x_j: the residual is P with x_j removed
         const int tb = seg * a.tpsr;
         const int te = min(a.tiles_row, tb + a.tpsr);
@@ -915,7 +973,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
 
     if (!arrive(counter(a.ws.res_cnt, c), (uint32_t)a.r_blk)) return;
     if (wave != 0) return;
-    if (j < L && a.sampler) {
+    if (GUMBEL && j < L) {
         const int tok = gumbel_finish(a.ws.garg + (size_t)c * kMaxResidSegments * 2, a.Sr, lane);
         if (lane == 0 && a.verify_outputs) a.out_tokens[c * L + j] = tok;
     } else if (j < L) {
@@ -930,14 +988,11 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         };
         auto mass_r = [&](uint64_t rc) -> double { return (double)lo_f(rc); };
         auto mass_p = [&](uint64_t rc) -> double { return (double)hi_f(rc); };
-        double Z = row_total(nt, get, lane, mass_r);
+        double Z = 0.0, before = 0.0, target = 0.0;
+        int tile = row_draw(nt, get, lane, mass_r, (double)inf.u, Z, before, target);
         const bool use_p = !(Z > 0.0);
-        if (use_p) Z = row_total(nt, get, lane, mass_p);
-        const double target = (double)inf.u * Z;
-        double before = 0.0;
+        if (use_p) tile = row_draw(nt, get, lane, mass_p, (double)inf.u, Z, before, target);
         double tile_target = target;
-        int tile = use_p ? row_find(nt, get, lane, mass_p, target, before)
-                         : row_find(nt, get, lane, mass_r, target, before);
         if (tile < 0) {
             tile = use_p ? row_last_positive(nt, get, lane, mass_p)
                          : row_last_positive(nt, get, lane, mass_r);
@@ -947,20 +1002,19 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         if (tile >= 0) {
             TileRaw<T> rp, rq;
             load_tile<T, VEC>(prow, tile, a.V, lane, rp);
-            if (!a.q_onehot) load_tile<T, VEC>(qrow, tile, a.V, lane, rq);
+            if (!ONEHOT) load_tile<T, VEC>(qrow, tile, a.V, lane, rq);
             const float k2 = a.k2;
-            const bool onehot = a.q_onehot != 0;
             const ResidForm rf = resid_form(inf, k2);
             // the weights the tile masses summed, entry by entry
-            auto weight = [&](int i) -> double {
-                if (onehot) {
+            auto weight = [&](int i) -> float {
+                if (ONEHOT) {
                     const float P = fast_exp2(fmaf(elem<T>(rp, i), k2, -inf.cp)) * inf.inv_sp;
-                    if (use_p) return (double)P;
-                    return elem_index(tile, lane, i) == (long long)inf.xj ? 0.0 : (double)P;
+                    if (use_p) return P;
+                    return elem_index(tile, lane, i) == (long long)inf.xj ? 0.0f : P;
                 }
                 float P;
                 const float R = resid_weight(elem<T>(rp, i), elem<T>(rq, i), rf, P);
-                return use_p ? (double)P : (double)R;
+                return use_p ? P : R;
             };
             tok = search_tile(weight, tile, lane, before, tile_target);
             if (tok < 0) tok = 0;
@@ -984,7 +1038,10 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
     }
 }
 
-template <typename T, bool VEC, int MODE>
+// VAR selects the correction's variant (sample mode): the Gumbel-max draw
+// and the one-hot proposal law are separate instantiations, so that the
+// default kernel carries neither their code nor their registers.
+template <typename T, bool VEC, int MODE, int VAR>
 __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     __shared__ Shared sh;
     const int wave = threadIdx.x / kWave;
@@ -1032,7 +1089,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
             const int k = w / a.Sq;
             qn_item<T, VEC, MODE>(a, c, k, w - k * a.Sq, sh, wave, lane);
         } else if (MODE == kSample) {
-            res_item<T, VEC>(a, c, w - a.q_blk, sh, wave, lane);
+            res_item<T, VEC, VAR>(a, c, w - a.q_blk, sh, wave, lane);
         }
     }
 }
@@ -1044,7 +1101,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
 constexpr int kTicketItems = 512;
 constexpr int kSpareGroupsPct = 50;
 
-template <typename T, bool VEC, int MODE>
+template <typename T, bool VEC, int MODE, int VAR>
 hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     // Items that wait (residual items wait for their sequence's decision) wait
     // only on verify items, which take their items by index and never wait;
@@ -1056,19 +1113,25 @@ hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     b.n_static = a.n_items - max(dyn, 0);
     long long grid = a.n_items;
     if (dyn > 0) grid += ((long long)dyn * kSpareGroupsPct + 99) / 100;
-    hipLaunchKernelGGL((step_kernel<T, VEC, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
+    hipLaunchKernelGGL((step_kernel<T, VEC, MODE, VAR>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
     return hipGetLastError();
 }
 
-hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStream_t stream) {
-    if (dtype == kBf16) {
-        if (mode == kSample)
-            return vec ? launch_one<uint16_t, true, kSample>(a, stream) : launch_one<uint16_t, false, kSample>(a, stream);
-        return vec ? launch_one<uint16_t, true, kGreedy>(a, stream) : launch_one<uint16_t, false, kGreedy>(a, stream);
+template <typename T, bool VEC>
+hipError_t launch_typed(const StepArgs &a, int mode, hipStream_t stream) {
+    if (mode != kSample) return launch_one<T, VEC, kGreedy, 0>(a, stream);
+    switch ((a.sampler ? kVarGumbel : 0) | (a.q_onehot ? kVarOnehot : 0)) {
+    case 0: return launch_one<T, VEC, kSample, 0>(a, stream);
+    case kVarGumbel: return launch_one<T, VEC, kSample, kVarGumbel>(a, stream);
+    case kVarOnehot: return launch_one<T, VEC, kSample, kVarOnehot>(a, stream);
+    default: return launch_one<T, VEC, kSample, kVarGumbel | kVarOnehot>(a, stream);
     }
-    if (mode == kSample)
-        return vec ? launch_one<float, true, kSample>(a, stream) : launch_one<float, false, kSample>(a, stream);
-    return vec ? launch_one<float, true, kGreedy>(a, stream) : launch_one<float, false, kGreedy>(a, stream);
+}
+
+hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStream_t stream) {
+    if (dtype == kBf16)
+        return vec ? launch_typed<uint16_t, true>(a, mode, stream) : launch_typed<uint16_t, false>(a, mode, stream);
+    return vec ? launch_typed<float, true>(a, mode, stream) : launch_typed<float, false>(a, mode, stream);
 }
 
 }  // namespace isd
