@@ -205,9 +205,12 @@ def check_and_time_oracle(gpu, n_timed, cfg, target_s):
     import multiprocessing as mp
     C, L = cfg["C"], cfg["L"]
     cores = len(os.sched_getaffinity(0))
+    _oracle_job((0, 0))                               # first call: imports and page-in
     t0 = time.perf_counter()
-    _oracle_job((0, 0))
-    per_seq = time.perf_counter() - t0               # one sequence, one core
+    n1 = min(C, 4)
+    for c in range(n1):
+        _oracle_job((0, c))
+    per_seq = (time.perf_counter() - t0) / n1         # one sequence, one core, warm
     n_steps = int(max(1, min(n_timed, target_s * cores / max(per_seq * C, 1e-9))))
     jobs = [(i, c) for i in range(n_steps) for c in range(C)]
     pool = mp.get_context("fork").Pool(cores)

@@ -271,6 +271,26 @@ __device__ __forceinline__ void load_group(const T *__restrict__ row, long long 
     }
 }
 
+// Lane `lane`'s 32 elements of a tile that lies wholly below V, on the vector
+// path: four (bf16) or eight (fp32) unconditional 16-byte non-temporal loads.
+template <typename T>
+__device__ __forceinline__ void load_tile_full(const T *__restrict__ row, int tile, int lane,
+                                               TileRaw<T> &r) {
+    constexpr int kWordsPerGroup = kGroupElems * (int)sizeof(T) / 4;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(row + (long long)tile * kTileElems +
+                                                       lane * kGroupElems);
+#pragma unroll
+    for (int g = 0; g < kGroupsPerTile; ++g)
+#pragma unroll
+        for (int h = 0; h < kWordsPerGroup / 4; ++h) {
+            const u32x4 v = __builtin_nontemporal_load(&src[g * (kWave * kGroupElems * (int)sizeof(T) / 16) + h]);
+            r.w[g * kWordsPerGroup + h * 4 + 0] = v.x;
+            r.w[g * kWordsPerGroup + h * 4 + 1] = v.y;
+            r.w[g * kWordsPerGroup + h * 4 + 2] = v.z;
+            r.w[g * kWordsPerGroup + h * 4 + 3] = v.w;
+        }
+}
+
 // Lane `lane`'s 32 elements of tile `tile` of `row`; elements at or past V
 // read as -inf and are never loaded.  In the last, partial tile of a row the
 // groups wholly below V still take the vector path, so that tile costs about
@@ -298,6 +318,16 @@ __device__ __forceinline__ float elem(const TileRaw<T> &r, int idx) {
     } else {
         return __uint_as_float(r.w[idx]);
     }
+}
+
+// max(a, b, c) by the hardware instruction.  fmaxf would first quiet each
+// operand that does not come from arithmetic (one extra max per element of a
+// tile, since the elements come from bit operations); NaN logits are
+// undefined input, so the quieting buys nothing here.
+__device__ __forceinline__ float max3_hw(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 // Vocab index of element idx of lane `lane` in tile `tile`.
@@ -339,34 +369,110 @@ __device__ __forceinline__ float tree_sum(float (&e)[N]) {
     return e[0];
 }
 
-// Streams tiles tile_begin + wave, + kWavesPerGroup, ... < tile_end of `row`,
-// keeping the loads of the next AHEAD tiles in flight while `f` consumes the
-// current one.
-template <typename T, bool VEC, typename F>
+// Streams tiles tile_begin + wave, + kWavesPerGroup, ... < tile_end of `row`
+// (wave is wavefront-uniform), keeping the next tile's loads in flight while
+// `f` consumes the current one.  On the vector path the tiles wholly below V
+// run in a loop whose loads are all unconditional and whose two tile buffers
+// alternate roles (the loop is unrolled twice): a load under a branch the
+// wavefront might skip, or a copy of a buffer still being loaded, would make
+// the compiler wait for every load in flight, the prefetch included, before
+// the current tile is used.  A row's last, partial tile is taken on its own.
+// SPLIT = false keeps the single loop with per-group load checks, which holds
+// fewer registers (for a heavy f) but keeps only one tile in flight.
+template <typename T, bool VEC, bool SPLIT = true, typename F>
 __device__ __forceinline__ void stream_row(const T *__restrict__ row, int tile_begin, int tile_end,
                                            int V, int wave, int lane, F &&f) {
     int t = tile_begin + wave;
     if (t >= tile_end) return;
-    TileRaw<T> cur;
-    load_tile<T, VEC>(row, t, V, lane, cur);
-    for (;;) {
-        const int tn = t + kWavesPerGroup;
-        const bool more = tn < tile_end;
-        TileRaw<T> nxt;
-        if (more) load_tile<T, VEC>(row, tn, V, lane, nxt);
-        f(cur, t);
-        if (!more) break;
-        cur = nxt;
-        t = tn;
+    if constexpr (VEC && SPLIT) {
+        const int full_end = min(tile_end, V / kTileElems);   // tiles below it are whole
+        if (t < full_end) {
+            TileRaw<T> a, b;
+            load_tile_full<T>(row, t, lane, a);
+            for (;;) {
+                if (t + kWavesPerGroup >= full_end) {
+                    f(a, t);
+                    t += kWavesPerGroup;
+                    break;
+                }
+                load_tile_full<T>(row, t + kWavesPerGroup, lane, b);
+                f(a, t);
+                t += kWavesPerGroup;
+                if (t + kWavesPerGroup >= full_end) {
+                    f(b, t);
+                    t += kWavesPerGroup;
+                    break;
+                }
+                load_tile_full<T>(row, t + kWavesPerGroup, lane, a);
+                f(b, t);
+                t += kWavesPerGroup;
+            }
+        }
+        if (t < tile_end) {   // the row's partial last tile
+            TileRaw<T> a;
+            load_tile<T, VEC>(row, t, V, lane, a);
+            f(a, t);
+        }
+    } else {
+        TileRaw<T> cur;
+        load_tile<T, VEC>(row, t, V, lane, cur);
+        for (;;) {
+            const int tn = t + kWavesPerGroup;
+            const bool more = tn < tile_end;
+            TileRaw<T> nxt;
+            if (more) load_tile<T, VEC>(row, tn, V, lane, nxt);
+            f(cur, t);
+            if (!more) break;
+            cur = nxt;
+            t = tn;
+        }
     }
 }
 
-// Streams the same tiles of two rows together (one tile of each in flight).
-template <typename T, bool VEC, typename F>
+// Lane `lane`'s 32 elements of the same whole tile of two rows, the loads of
+// the two rows interleaved group by group (the first group of both is needed
+// first).
+template <typename T>
+__device__ __forceinline__ void load_tile_pair_full(const T *__restrict__ ra, const T *__restrict__ rb,
+                                                    int tile, int lane, TileRaw<T> &ca,
+                                                    TileRaw<T> &cb) {
+    constexpr int kWordsPerGroup = kGroupElems * (int)sizeof(T) / 4;
+    const long long off = (long long)tile * kTileElems + lane * kGroupElems;
+    const u32x4 *sa = reinterpret_cast<const u32x4 *>(ra + off);
+    const u32x4 *sb = reinterpret_cast<const u32x4 *>(rb + off);
+    constexpr int kStride = kWave * kGroupElems * (int)sizeof(T) / 16;   // u32x4 per group row
+#pragma unroll
+    for (int g = 0; g < kGroupsPerTile; ++g)
+#pragma unroll
+        for (int h = 0; h < kWordsPerGroup / 4; ++h) {
+            const u32x4 va = __builtin_nontemporal_load(&sa[g * kStride + h]);
+            const u32x4 vb = __builtin_nontemporal_load(&sb[g * kStride + h]);
+            uint32_t *wa = &ca.w[g * kWordsPerGroup + h * 4];
+            uint32_t *wb = &cb.w[g * kWordsPerGroup + h * 4];
+            wa[0] = va.x; wa[1] = va.y; wa[2] = va.z; wa[3] = va.w;
+            wb[0] = vb.x; wb[1] = vb.y; wb[2] = vb.z; wb[3] = vb.w;
+        }
+}
+
+// Streams the same tiles of two rows together (one tile of each in flight);
+// on the vector path the whole tiles take unconditional loads and a row's
+// partial last tile is taken on its own.
+// SPLIT = false keeps one loop with per-group load checks (fewer registers
+// live at once, for a heavy f).
+template <typename T, bool VEC, bool SPLIT = true, typename F>
 __device__ __forceinline__ void stream_rows2(const T *__restrict__ ra, const T *__restrict__ rb,
                                              int tile_begin, int tile_end, int V, int wave,
                                              int lane, F &&f) {
-    for (int t = tile_begin + wave; t < tile_end; t += kWavesPerGroup) {
+    int t = tile_begin + wave;
+    if constexpr (VEC && SPLIT) {
+        const int full_end = min(tile_end, V / kTileElems);
+        for (; t < full_end; t += kWavesPerGroup) {
+            TileRaw<T> ca, cb;
+            load_tile_pair_full<T>(ra, rb, t, lane, ca, cb);
+            f(ca, cb, t);
+        }
+    }
+    for (; t < tile_end; t += kWavesPerGroup) {
         TileRaw<T> ca, cb;
         load_tile<T, VEC>(ra, t, V, lane, ca);
         load_tile<T, VEC>(rb, t, V, lane, cb);

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kDecideWaves * kWave) void fused_decide_kernel(Step
     __shared__ float s_c[2][kMaxL];
     __shared__ double s_s[2][kMaxL];
     const int c = blockIdx.x;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int L = a.L;
     // one wavefront per row: p rows (which = 0), then q rows (which = 1)
     const int rows = a.q_onehot ? L : 2 * L;
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kDecideWaves * kWave) void fused_decide_kernel(Step
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void fused_propose_kernel(StepArgs a) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int rowid = blockIdx.x * kWavesPerGroup + wave;   // c * L + k
     if (rowid >= a.C * a.L) return;
     const int c = rowid / a.L, k = rowid - c * a.L;

@@ -16,7 +16,7 @@ namespace {
 __global__ __launch_bounds__(kThreads) void read_probe_kernel(const uint16_t *__restrict__ buf,
                                                               int n_tiles, int tiles_per_group,
                                                               uint32_t *__restrict__ sink) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int t0 = (int)blockIdx.x * tiles_per_group;
     const int t1 = min(n_tiles, t0 + tiles_per_group);
     uint32_t acc = 0;

@@ -57,13 +57,14 @@ __device__ __forceinline__ void ld_seg(const SegRec *r, float &ref, double &sum)
     ref = lo_f(ld64(reinterpret_cast<const uint64_t *>(r)));
     sum = __longlong_as_double((long long)ld64(reinterpret_cast<const uint64_t *>(r) + 1));
 }
-// Largest of a lane's 32 elements of a tile, read from the packed words.
+// Largest of a lane's 32 elements of a tile, read from the packed words:
+// sixteen three-way maxima.
 template <typename T>
 __device__ __forceinline__ float tile_max(const TileRaw<T> &r) {
-    float m = kNegInf;
+    float m = max3_hw(elem<T>(r, 0), elem<T>(r, 1), elem<T>(r, 2));
 #pragma unroll
-    for (int i = 0; i < kLaneElems; i += 2) m = fmaxf(m, fmaxf(elem<T>(r, i), elem<T>(r, i + 1)));
-    return m;
+    for (int i = 3; i + 1 < kLaneElems; i += 2) m = max3_hw(m, elem<T>(r, i), elem<T>(r, i + 1));
+    return max3_hw(m, elem<T>(r, kLaneElems - 1), elem<T>(r, kLaneElems - 1));
 }
 
 // Sum over a lane's 32 elements of 2^(x*k2 - ref): pairwise within each
@@ -908,8 +909,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
             });
         } else {
             const ResidForm rf = resid_form(inf, a.k2);
-            stream_rows2<T, VEC>(prow, qrow, tb, te, a.V, wave, lane,
-                                 [&](const TileRaw<T> &rp, const TileRaw<T> &rq, int tile) {
+            auto body = [&](const TileRaw<T> &rp, const TileRaw<T> &rq, int tile) {
 #pragma unroll
                 for (int g = 0; g < kGroupsPerTile; ++g) {
                     float P[kGroupElems], R[kGroupElems];
@@ -920,7 +920,8 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
                     }
                     take(P, R, tile, g);
                 }
-            });
+            };
+            stream_rows2<T, VEC, false>(prow, qrow, tb, te, a.V, wave, lane, body);
         }
         gumbel_publish(sh, wave, lane, br, ir, bp, ip,
                        a.ws.garg + ((size_t)c * kMaxResidSegments + seg) * 2);
@@ -1044,7 +1045,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
 template <typename T, bool VEC, int MODE, int VAR>
 __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     __shared__ Shared sh;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     int t = (int)blockIdx.x;
     if (t >= a.n_static) {
@@ -1098,8 +1099,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
 
 // Items at the end of the launch that take tickets, and spare workgroups in
 // percent of them.
-constexpr int kTicketItems = 512;
-constexpr int kSpareGroupsPct = 50;
+constexpr int kTicketItems = 256;
+constexpr int kSpareGroupsPct = 25;
 
 template <typename T, bool VEC, int MODE, int VAR>
 hipError_t launch_one(const StepArgs &a, hipStream_t stream) {

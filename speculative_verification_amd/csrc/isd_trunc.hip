@@ -231,7 +231,7 @@ __device__ __forceinline__ uint64_t select_segment(const T *__restrict__ row, in
         // ---- 1. stream: each group's best entry into LDS; the column maximum ----
         // A thread's records (lane `lane` of its wavefront's tiles) form a column.
         uint64_t colmax = 0;
-        stream_row<T, VEC>(row, cb, ce, V, wave, lane, [&](const TileRaw<T> &r, int tile) {
+        stream_row<T, VEC, false>(row, cb, ce, V, wave, lane, [&](const TileRaw<T> &r, int tile) {
             // the lane's maximum and its first position (the lowest index
             // among equals: a later entry replaces it only if larger)
             float vmax = elem<T>(r, 0);
@@ -588,7 +588,7 @@ __device__ __forceinline__ long long trunc_row_offset(const StepArgs &a, int c, 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void trunc_kernel(StepArgs a) {
     __shared__ TruncShared<T> sh;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int t = (int)blockIdx.x;
     const int L = a.L;
