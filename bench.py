@@ -68,7 +68,9 @@ def kernel_digest(sources=None) -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: the workload's own count: 100 tiny, 1000 serving "
+                         "and greedy, 500 high concurrency, 200 otherwise)")
     ap.add_argument("--warmup", type=int, default=20,
                     help="untimed steps before the timed ones (the read probe before them has "
                          "already brought the GPU clock to its steady state)")
@@ -95,7 +97,10 @@ def parse():
                     help="only run the streaming-read probe (1 GiB, the step's tile loader)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = {1: 100, 2: 1000, 3: 1000, 5: 500}.get(args.config, 200)
+    return args
 
 
 def copy_calibration():
