@@ -363,6 +363,7 @@ def lm_head_workload(args):
     step_bytes = 3 * C * L * V * 2   # what the step would read without the statistics
     ms_per_step = wall * 1e3 / args.steps
     acc = outs[(args.warmup + args.steps - 1) % 2]["accept_len"].float().mean().item()
+    counters = head_counters(M, H, V)
     print(json.dumps(dict(
         metric="ISD verified positions/sec with the LM-head projection (h @ W on MFMA) in the step",
         value=round(C * L / (ms_per_step * 1e-3), 1), unit="positions/s", n_gpus=1,
@@ -374,9 +375,11 @@ def lm_head_workload(args):
                     step_input="LM-head tile statistics" if args.fused else "logits"),
         roofline=dict(bound="mfma", achieved=round(gemm_tflops, 1), peak=2500.0,
                       unit="TFLOP/s", frac=round(gemm_tflops / 2500.0, 4),
-                      traffic=head_traffic(M, H, V) if not args.fused else None),
+                      traffic=(counters or {}).get("bytes_per_launch") if not args.fused else None),
         gemm=dict(ms=round(float(gemm_ms), 4), tflops=round(gemm_tflops, 1),
-                  mfma_util=round(gemm_tflops / 2500.0, 4), peak_tflops=2500.0),
+                  flop_frac=round(gemm_tflops / 2500.0, 4), peak_tflops=2500.0,
+                  mfma_busy=((counters or {}).get("mfma") or {}).get("busy_frac")
+                  if not args.fused else None),
         step=(dict(us=round(float(step_ms) * 1e3, 2),
                    note="reads the residual rows and one 128-column tile per proposal")
               if args.fused else
@@ -387,17 +390,18 @@ def lm_head_workload(args):
         accept_len_mean_last=round(acc, 3))), flush=True)
 
 
-def head_traffic(M, H, V):
-    """HBM bytes per launch of the plain packed LM head from rocprofv3
-    FETCH_SIZE / WRITE_SIZE (copy-calibrated), when profiles/ holds counters
-    for the current GEMM source and this shape; else None."""
+def head_counters(M, H, V):
+    """rocprofv3 counters of the plain packed LM head, when profiles/ holds
+    them for the current GEMM source and this shape, else None:
+    bytes_per_launch (FETCH_SIZE / WRITE_SIZE, copy-calibrated) and mfma
+    (SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles GRBM_GUI_ACTIVE spans)."""
     if not os.path.exists(HEAD_TRAFFIC_FILE):
         return None
     with open(HEAD_TRAFFIC_FILE) as f:
         tr = json.load(f)
     if tr.get("kernel_digest") != kernel_digest(HEAD_SOURCES) or tr.get("shape") != [M, H, V]:
         return None
-    return tr.get("bytes_per_launch")
+    return tr
 
 
 def lora_workload(args):
