@@ -383,6 +383,11 @@ __device__ __forceinline__ long long row_offset(const StepArgs &a, int c, int k)
     return (long long)c * a.ldc + (long long)k * a.ld;
 }
 
+// An item of at most this many tiles gathers its tile records in LDS and
+// stores them with one instruction at its end (one lane per record) instead
+// of one store per tile.
+constexpr int kBatchTiles = kWave;
+
 struct Shared {
     int ticket;
     float refs[kWavesPerGroup];
@@ -392,6 +397,7 @@ struct Shared {
     float vals2[kWavesPerGroup];
     int idxs2[kWavesPerGroup];
     SeqInfo info;
+    uint64_t trec[kBatchTiles];   // an item's tile records, stored together at its end
 };
 
 // Decision for sequence c from its merged verify rows (wavefront 0 of the
@@ -617,12 +623,20 @@ __device__ __forceinline__ void qn_item(const StepArgs &a, int c, int k, int seg
 
     if (MODE == kSample) {
         TileRec *tr = a.ws.tiles + (size_t)rowid * a.tiles_row;
+        const bool batch = te - tb <= kBatchTiles;
         LaneSoftmax sm;
         stream_row<T, VEC>(row, tb, te, a.V, wave, lane, [&](const TileRaw<T> &r, int tile) {
             const float s = sm.add<T>(r, a.k2);
             const float ts = wave_sum(s);
-            if (lane == 0) st_pair(&tr[tile], pack2(sm.ref, ts));
+            if (lane == 0) {
+                if (batch) sh.trec[tile - tb] = pack2(sm.ref, ts);
+                else st_pair(&tr[tile], pack2(sm.ref, ts));
+            }
         });
+        if (batch) {
+            __syncthreads();
+            if (wave == 0 && lane < te - tb) st_pair(&tr[tb + lane], sh.trec[lane]);
+        }
         if (!arrive(counter(a.ws.row_cnt, rowid), (uint32_t)a.Sq)) return;
         if (wave != 0) return;
 
@@ -929,6 +943,7 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
         // Q is one-hot at x_j: the residual is P with x_j removed
         const int tb = seg * a.tpsr;
         const int te = min(a.tiles_row, tb + a.tpsr);
+        const bool batch = te - tb <= kBatchTiles;
         stream_row<T, VEC>(prow, tb, te, a.V, wave, lane, [&](const TileRaw<T> &rp, int tile) {
             float lr = 0.0f, lp = 0.0f;
 #pragma unroll
@@ -946,11 +961,19 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
             }
             const float sr = wave_sum(lr);
             const float spp = wave_sum(lp);
-            if (lane == 0) st_pair(&rt[tile], pack2(sr, spp));
+            if (lane == 0) {
+                if (batch) sh.trec[tile - tb] = pack2(sr, spp);
+                else st_pair(&rt[tile], pack2(sr, spp));
+            }
         });
+        if (batch) {
+            __syncthreads();
+            if (wave == 0 && lane < te - tb) st_pair(&rt[tb + lane], sh.trec[lane]);
+        }
     } else if (j < L) {
         const int tb = seg * a.tpsr;
         const int te = min(a.tiles_row, tb + a.tpsr);
+        const bool batch = te - tb <= kBatchTiles;
         const ResidForm rf = resid_form(inf, a.k2);
         stream_rows2<T, VEC>(prow, qrow, tb, te, a.V, wave, lane,
                              [&](const TileRaw<T> &rp, const TileRaw<T> &rq, int tile) {
@@ -968,8 +991,15 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
             }
             const float sr = wave_sum(lr);
             const float spp = wave_sum(lp);
-            if (lane == 0) st_pair(&rt[tile], pack2(sr, spp));
+            if (lane == 0) {
+                if (batch) sh.trec[tile - tb] = pack2(sr, spp);
+                else st_pair(&rt[tile], pack2(sr, spp));
+            }
         });
+        if (batch) {
+            __syncthreads();
+            if (wave == 0 && lane < te - tb) st_pair(&rt[tb + lane], sh.trec[lane]);
+        }
     }
 
     if (!arrive(counter(a.ws.res_cnt, c), (uint32_t)a.r_blk)) return;
