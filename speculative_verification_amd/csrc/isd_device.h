@@ -571,23 +571,31 @@ __device__ __forceinline__ uint32_t *counter(uint32_t *base, int i) {
 // the launch's epoch, so a flag left over from an earlier launch never
 // releases a wait of this one.
 __device__ __forceinline__ void publish_decision(const StepArgs &a, int c, int j, float u, float cp, float cq,
-                                 double sp, double sq, int xj) {
-    SeqInfo *si = &a.ws.info[c];
+                                 double sp, double sq, int xj, int lane) {
+    // one store instruction: lane w writes word w of the record (the alpha
+    // word is not part of the decision)
+    uint32_t *si = reinterpret_cast<uint32_t *>(&a.ws.info[c]);
     const double rho = sq > 0.0 ? sp / sq : 0.0;
     const float rho_hi = (float)rho;
     const float rho_lo = (float)(rho - (double)rho_hi);
-    st32(reinterpret_cast<uint32_t *>(&si->j), (uint32_t)j);
-    st32(reinterpret_cast<uint32_t *>(&si->u), __float_as_uint(u));
-    st32(reinterpret_cast<uint32_t *>(&si->cp), __float_as_uint(cp));
-    st32(reinterpret_cast<uint32_t *>(&si->cq), __float_as_uint(cq));
-    st32(reinterpret_cast<uint32_t *>(&si->inv_sp), __float_as_uint(sp > 0.0 ? (float)(1.0 / sp) : 0.0f));
-    st32(reinterpret_cast<uint32_t *>(&si->inv_sq), __float_as_uint(sq > 0.0 ? (float)(1.0 / sq) : 0.0f));
-    st32(reinterpret_cast<uint32_t *>(&si->xj), (uint32_t)xj);
-    st32(reinterpret_cast<uint32_t *>(&si->rho_hi), __float_as_uint(rho_hi));
-    st32(reinterpret_cast<uint32_t *>(&si->rho_lo), __float_as_uint(rho_lo));
+    static_assert(sizeof(SeqInfo) == 10 * sizeof(uint32_t), "SeqInfo is ten words");
+    uint32_t w = 0;
+    switch (lane) {
+    case 0: w = (uint32_t)j; break;
+    case 1: w = __float_as_uint(u); break;
+    case 2: w = __float_as_uint(cp); break;
+    case 3: w = __float_as_uint(cq); break;
+    case 4: w = __float_as_uint(sp > 0.0 ? (float)(1.0 / sp) : 0.0f); break;
+    case 5: w = __float_as_uint(sq > 0.0 ? (float)(1.0 / sq) : 0.0f); break;
+    case 7: w = (uint32_t)xj; break;
+    case 8: w = __float_as_uint(rho_hi); break;
+    case 9: w = __float_as_uint(rho_lo); break;
+    default: break;
+    }
+    if (lane < 10 && lane != 6) st32(&si[lane], w);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
-    st32(counter(a.ws.flag, c), a.epoch);
+    if (lane == 0) st32(counter(a.ws.flag, c), a.epoch);
 }
 
 // ---------------------------------------------------------------------------

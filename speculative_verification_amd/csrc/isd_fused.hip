@@ -162,8 +162,8 @@ __global__ __launch_bounds__(kDecideWaves * kWave) void fused_decide_kernel(Step
     const float jcp = __shfl(cp, src), jcq = __shfl(cq, src);
     const double jsp = __shfl(sp, src), jsq = __shfl(sq, src);
     const int jx = __shfl(xk, src);
+    publish_decision(a, c, j, j < L ? a.ur[c * L + j] : 0.0f, jcp, jcq, jsp, jsq, jx, lane);
     if (lane == 0) {
-        publish_decision(a, c, j, j < L ? a.ur[c * L + j] : 0.0f, jcp, jcq, jsp, jsq, jx);
         if (a.alpha) a.alpha[c] = alpha;
         a.accept_len[c] = j;
         a.n_emitted[c] = j + (j < L ? 1 : 0);

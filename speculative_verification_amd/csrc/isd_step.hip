@@ -390,6 +390,7 @@ constexpr int kBatchTiles = kWave;
 
 struct Shared {
     int ticket;
+    int flag_ok;                  // a residual item's wait for its decision ended in time
     float refs[kWavesPerGroup];
     double sums[kWavesPerGroup];
     float vals[kWavesPerGroup];
@@ -461,9 +462,8 @@ __device__ __forceinline__ void decide(const StepArgs &a, int c, int lane) {
             const float jcp = __shfl(cp, src), jcq = __shfl(cq, src);
             const double jsp = __shfl(sp, src), jsq = __shfl(sq, src);
             const int jx = __shfl(xk, src);
-            if (lane == 0)
-                publish_decision(a, c, j, (j < L && a.ur) ? a.ur[c * L + j] : 0.0f, jcp, jcq, jsp,
-                                 jsq, jx);
+            const float ju = (j < L && a.ur) ? a.ur[c * L + j] : 0.0f;
+            publish_decision(a, c, j, ju, jcp, jcq, jsp, jsq, jx, lane);
         }
         if (lane == 0 && a.verify_outputs) {
             a.accept_len[c] = j;
@@ -571,11 +571,13 @@ __device__ __forceinline__ void pq_item(const StepArgs &a, int t, Shared &sh, in
             sh.sums[wave] = ws;
         }
         __syncthreads();
-        if (threadIdx.x == 0) {
+        if (threadIdx.x < 2) {
+            // the record's two words in one store instruction (lanes 0 and 1)
             float ref;
             double sum;
             merge_refsum(sh.refs, sh.sums, kWavesPerGroup, ref, sum);
-            st_seg(&a.ws.seg[rec], ref, sum);
+            st64(reinterpret_cast<uint64_t *>(&a.ws.seg[rec]) + threadIdx.x,
+                 threadIdx.x == 0 ? pack2(ref, 0.0f) : (uint64_t)__double_as_longlong(sum));
         }
     } else {
         float bv = kNegInf;
@@ -870,16 +872,14 @@ __device__ __forceinline__ void res_item(const StepArgs &a, int c, int seg, Shar
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        SeqInfo *si = &a.ws.info[c];
-        sh.info.j = ok ? (int)ld32(reinterpret_cast<uint32_t *>(&si->j)) : a.L;
-        sh.info.u = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->u)));
-        sh.info.cp = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->cp)));
-        sh.info.cq = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->cq)));
-        sh.info.inv_sp = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->inv_sp)));
-        sh.info.inv_sq = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->inv_sq)));
-        sh.info.xj = (int)ld32(reinterpret_cast<uint32_t *>(&si->xj));
-        sh.info.rho_hi = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->rho_hi)));
-        sh.info.rho_lo = __uint_as_float(ld32(reinterpret_cast<uint32_t *>(&si->rho_lo)));
+        sh.flag_ok = ok;
+    }
+    __syncthreads();
+    if (threadIdx.x < 10) {
+        // the decision record, one word per lane in one load instruction
+        const uint32_t w = ld32(reinterpret_cast<const uint32_t *>(&a.ws.info[c]) + threadIdx.x);
+        reinterpret_cast<uint32_t *>(&sh.info)[threadIdx.x] =
+            (threadIdx.x == 0 && !sh.flag_ok) ? (uint32_t)a.L : w;
     }
     __syncthreads();
     const SeqInfo inf = sh.info;
