@@ -31,7 +31,11 @@ std::atomic<int> g_propose_segments{0};
 std::atomic<int> g_resid_segments{0};
 std::atomic<int> g_trunc_segments{0};
 // default decomposition (tiles of 2048 elements per workgroup segment)
-constexpr int kVerifyTilesPerSeg = 38;
+// Verify rows are taken whole up to this many tiles, and cut further only
+// while there are fewer than kMinVerifyItems verify items (so that a small
+// batch still spreads over the chip).
+constexpr int kVerifyTilesPerSeg = 96;
+constexpr int kMinVerifyItems = 512;
 constexpr int kProposeTilesPerSeg = 19;
 constexpr int kResidTilesPerSeg = 8;
 // truncated path: split rows only as far as needed for about this many items
@@ -164,7 +168,12 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
         int S = want > 0 ? want : ceil_div(a.tiles_row, tiles_per_seg_target);
         return max(1, min(S, min(lay.smax, a.tiles_row)));
     };
-    const int Sv = segs(g_segments.load(), kVerifyTilesPerSeg);
+    int Sv = segs(g_segments.load(), kVerifyTilesPerSeg);
+    if (g_segments.load() <= 0) {
+        const long long vrows = (long long)C * ((greedy || s->q_onehot) ? L : 2 * L);
+        if (vrows * Sv < kMinVerifyItems)
+            Sv = segs((int)((kMinVerifyItems + vrows - 1) / vrows), 0);
+    }
     a.tps = ceil_div(a.tiles_row, Sv);
     a.S = ceil_div(a.tiles_row, a.tps);
     const int Sq = segs(g_propose_segments.load(), kProposeTilesPerSeg);
