@@ -35,7 +35,7 @@ std::atomic<int> g_trunc_segments{0};
 // while there are fewer than kMinVerifyItems verify items (so that a small
 // batch still spreads over the chip).
 constexpr int kVerifyTilesPerSeg = 96;
-constexpr int kMinVerifyItems = 512;
+constexpr int kMinVerifyItems = 1024;
 constexpr int kProposeTilesPerSeg = 19;
 constexpr int kResidTilesPerSeg = 8;
 // truncated path: split rows only as far as needed for about this many items
