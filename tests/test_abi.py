@@ -17,6 +17,10 @@ FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced on the host
 @pytest.fixture(scope="module")
 def isd():
     import speculative_verification_amd as m
+    # test_abi_asan.py runs this file again against a build whose host code
+    # carries AddressSanitizer
+    if os.environ.get("ISD_TEST_LIBRARY"):
+        m.isd.LIB_PATH = os.environ["ISD_TEST_LIBRARY"]
     m.lib()
     return m
 
