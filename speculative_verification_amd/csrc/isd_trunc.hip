@@ -231,7 +231,7 @@ __device__ __forceinline__ uint64_t select_segment(const T *__restrict__ row, in
         // ---- 1. stream: each group's best entry into LDS; the column maximum ----
         // A thread's records (lane `lane` of its wavefront's tiles) form a column.
         uint64_t colmax = 0;
-        stream_row<T, VEC, false>(row, cb, ce, V, wave, lane, [&](const TileRaw<T> &r, int tile) {
+        stream_row<T, VEC>(row, cb, ce, V, wave, lane, [&](const TileRaw<T> &r, int tile) {
             // the lane's maximum and its first position (the lowest index
             // among equals: a later entry replaces it only if larger)
             float vmax = elem<T>(r, 0);
