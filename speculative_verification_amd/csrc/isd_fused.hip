@@ -34,53 +34,72 @@ constexpr float kNegInfF = -__builtin_inff();
 // 2^n for an integer-valued float n, saturating far below the fp64 range.
 __device__ __forceinline__ double pow2_i(float n) { return ldexp(1.0, (int)fmaxf(n, -2000.0f)); }
 
-// A row's tile partials as one wavefront holds them: lane l owns the
-// contiguous tiles [l * per, l * per + per), all loaded at once (per <= kPer;
-// rows longer than 64 * kPer tiles are taken in chunks by the callers).
-constexpr int kPer = 24;
+// A row's tile partials are (e, s) float pairs, 8 bytes per 128-column tile.
+// A wavefront takes them kChunk tiles at a time with lane l holding tiles
+// t0 + i * 64 + l, so each load instruction covers 512 consecutive bytes.
+constexpr int kU = 24;
+constexpr int kChunk = kU * kWave;   // 1536 tiles, 196,608 columns
 
-struct RowPartials {
-    float e[kPer];
-    float s[kPer];
+struct Chunk {
+    float e[kU];
+    float s[kU];
 };
 
-__device__ __forceinline__ void load_partials(const float *st, int n, int t0, int per, int lane,
-                                              RowPartials &r) {
+__device__ __forceinline__ void load_chunk(const float *st, int n, int t0, int lane, Chunk &ch) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int t = t0 + lane * per + i;
-        const bool in = i < per && t < n;
-        r.e[i] = in ? st[2 * t] : kNegInfF;
-        r.s[i] = in ? st[2 * t + 1] : 0.0f;
+    for (int i = 0; i < kU; ++i) {
+        const int t = t0 + i * kWave + lane;
+        if (t < n) {
+            const uint64_t w = *reinterpret_cast<const uint64_t *>(st + 2 * t);
+            ch.e[i] = __uint_as_float((uint32_t)w);
+            ch.s[i] = __uint_as_float((uint32_t)(w >> 32));
+        } else {
+            ch.e[i] = kNegInfF;
+            ch.s[i] = 0.0f;
+        }
     }
 }
 
-// Softmax denominator of one row from its n tile partials (one wavefront):
-// ref = max e, sum = sum s * 2^(e - ref) in fp64.
+// Fold a chunk into a lane's running (reference r, fp64 sum acc scaled to r).
+__device__ __forceinline__ void fold_chunk(const Chunk &ch, float &r, double &acc) {
+    float cm = kNegInfF;
+#pragma unroll
+    for (int i = 0; i < kU; ++i) cm = fmaxf(cm, ch.e[i]);
+    if (cm > r) {
+        if (r != kNegInfF) acc *= pow2_i(r - cm);
+        r = cm;
+    }
+#pragma unroll
+    for (int i = 0; i < kU; ++i)
+        if (ch.e[i] != kNegInfF) acc += (double)ch.s[i] * pow2_i(ch.e[i] - r);
+}
+
+// Combine the lanes: ref = max e over the row, sum = sum s * 2^(e - ref).
+__device__ __forceinline__ void finish_stats(float r, double acc, float &ref, double &sum) {
+    const float R = wave_max(r);
+    ref = R;
+    sum = wave_sum_d(r == kNegInfF ? 0.0 : acc * pow2_i(r - R));
+}
+
+// Softmax denominator of one row from its n tile partials (one wavefront).
 __device__ __forceinline__ void merge_row_stats(const float *st, int n, int lane, float &ref,
                                                 double &sum) {
-    const int per = min(kPer, (n + kWave - 1) / kWave);
-    const int span = per * kWave;
     float r = kNegInfF;
     double acc = 0.0;
-    for (int t0 = 0; t0 < n; t0 += span) {
-        RowPartials p;
-        load_partials(st, n, t0, per, lane, p);
-        float cm = kNegInfF;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) cm = fmaxf(cm, p.e[i]);
-        cm = wave_max(cm);
-        if (cm == kNegInfF) continue;
-        if (cm > r) {
-            if (r != kNegInfF) acc *= pow2_i(r - cm);
-            r = cm;
-        }
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (p.e[i] != kNegInfF) acc += (double)p.s[i] * pow2_i(p.e[i] - r);
+    for (int t0 = 0; t0 < n; t0 += kChunk) {
+        Chunk ch;
+        load_chunk(st, n, t0, lane, ch);
+        fold_chunk(ch, r, acc);
     }
-    ref = r;
-    sum = wave_sum_d(acc);
+    finish_stats(r, acc, ref, sum);
+}
+
+// Wavefront-scope ordering of the LDS staging area: writes before reads by
+// other lanes of the same wavefront, and reads before the next overwrite.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ const float *row_stats(const float *base, const StepArgs &a, int c,
@@ -176,45 +195,73 @@ __global__ __launch_bounds__(kDecideWaves * kWave) void fused_decide_kernel(Step
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void fused_propose_kernel(StepArgs a) {
+    // per wavefront, one chunk of partials re-laid out for contiguous runs
+    __shared__ uint64_t s_part[kWavesPerGroup][kChunk];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int rowid = blockIdx.x * kWavesPerGroup + wave;   // c * L + k
     if (rowid >= a.C * a.L) return;
     const int c = rowid / a.L, k = rowid - c * a.L;
     const float *st = row_stats(a.qn_stats, a, c, k);
     const int n = a.n_stiles;
+    uint64_t *part = s_part[wave];
+    Chunk ch;
+    load_chunk(st, n, 0, lane, ch);
     float cr;
     double S;
-    merge_row_stats(st, n, lane, cr, S);
+    {
+        float r = kNegInfF;
+        double acc = 0.0;
+        fold_chunk(ch, r, acc);
+        for (int t0 = kChunk; t0 < n; t0 += kChunk) {
+            Chunk more;
+            load_chunk(st, n, t0, lane, more);
+            fold_chunk(more, r, acc);
+        }
+        finish_stats(r, acc, cr, S);
+    }
     int token = 0;
     double pw = 0.0;
     if (!(S > 0.0)) {
         if (lane == 0) atomicOr(&a.ws.ctl->error, kErrEmptyRow);
     } else {
         const double target = (double)a.up[rowid] * S;
-        // first tile whose running mass exceeds the target; lane l owns a
-        // contiguous run of tiles, so one scan of lane sums finds the lane
-        const int per = min(kPer, (n + kWave - 1) / kWave);
-        const int span = per * kWave;
+        // first tile whose running mass exceeds the target: each chunk goes
+        // through LDS so that lane l owns a contiguous run of tiles, and one
+        // scan of the lane sums finds the lane
         int tile = -1, last_pos = -1;
         double before = 0.0, base = 0.0;
-        for (int t0 = 0; t0 < n && tile < 0; t0 += span) {
-            RowPartials p;
-            load_partials(st, n, t0, per, lane, p);
-            double m[kPer];
+        for (int t0 = 0; t0 < n && tile < 0; t0 += kChunk) {
+            if (t0 > 0) load_chunk(st, n, t0, lane, ch);
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < kU; ++i)
+                part[i * kWave + lane] =
+                    (uint64_t)__float_as_uint(ch.e[i]) | ((uint64_t)__float_as_uint(ch.s[i]) << 32);
+            wave_lds_sync();
+            const int cn = min(kChunk, n - t0);
+            const int per = (cn + kWave - 1) / kWave;
+            double m[kU];
             double ls = 0.0;
             int mine_last = -1;
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                m[i] = p.e[i] == kNegInfF ? 0.0 : (double)p.s[i] * pow2_i(p.e[i] - cr);
+            for (int i = 0; i < kU; ++i) {
+                const int t = lane * per + i;
+                m[i] = 0.0;
+                if (i < per && t < cn) {
+                    const uint64_t w = part[t];
+                    const float e = __uint_as_float((uint32_t)w);
+                    if (e != kNegInfF)
+                        m[i] = (double)__uint_as_float((uint32_t)(w >> 32)) * pow2_i(e - cr);
+                }
                 ls += m[i];
-                if (m[i] > 0.0) mine_last = t0 + lane * per + i;
+                if (m[i] > 0.0) mine_last = t0 + t;
             }
             const double inc = wave_incl_scan_d(ls, lane);
             double run = base + (inc - ls);
             int first = -1;
             double fb = 0.0;
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
+            for (int i = 0; i < kU; ++i) {
                 if (first < 0 && m[i] > 0.0 && run + m[i] > target) {
                     first = i;
                     fb = run;
