@@ -156,11 +156,12 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const uint16_t *__restrict
 // With the head stored k-contiguous per vocabulary row (wt = w^T, packed
 // once), both MFMA operands are 8 consecutive k of one row: every global
 // load and every LDS store is one 16-byte vector, with no transposition.
-// The workgroup owns a 256 x BN output tile (BN = 128 or 256) and keeps a
-// single LDS buffer (55 or 74 KB): the next K step's tiles are held in
-// registers while the current one is multiplied.  At BN = 128 two workgroups
-// share a CU and their barrier phases interleave; at BN = 256 one workgroup
-// of eight wavefronts fills it and moves a third less operand data per flop.
+//
+// Narrow projections (the LoRA call, or any head with fewer than four 256-wide
+// tiles per CU) run on 256 x 128 tiles: four wavefronts, a single 55 KB LDS
+// buffer with the next K step's tiles held in registers while the current one
+// is multiplied, and two workgroups per CU whose barrier phases interleave.
+// Wide heads use the ping-pong kernel further down.
 
 constexpr int kPBM = 256, kPBN = 128, kPBK = 64;
 constexpr int kPLd = kPBK + 8;                              // LDS row length (bf16), padded
@@ -169,31 +170,16 @@ constexpr int kPVecRow = kPBK / 8;                          // 16-byte vectors p
 // The A operand may come in two K segments: columns [0, K1) from h [M, K1]
 // and [K1, K1 + K2) from h2 [M, K2] (K2 = 0: none); wt is [N, K1 + K2].  Both
 // K1 and K2 are multiples of 64, so a K step never straddles the two.
-//
-// With STATS the epilogue also emits, for every output row and every 128-column
-// tile, the softmax partial of the bf16 logits it writes: an integer reference
-// e = ceil(max * k2) and s = sum 2^(x * k2 - e) (k2 = log2(e) / T), stored as
-// two floats at stats[(row * ceil(N / 128) + tile) * 2].  The ISD step can then
-// take its row statistics from these instead of reading the logits back.
-//
-// BN is the tile width: 128 (256 threads, two workgroups per CU) or 256 (512
-// threads, one workgroup per CU, a third less operand traffic per flop).
-template <int BN, bool STATS>
-__global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
+__global__ __launch_bounds__(256, 2) void lm_head_packed_kernel(
     const uint16_t *__restrict__ h, int K1, const uint16_t *__restrict__ h2, int K2,
     const uint16_t *__restrict__ wt, int M, int N, uint16_t *__restrict__ out, int m_tiles,
-    int total, int per_xcd, float k2, float *__restrict__ stats) {
-    static_assert(BN % kPBN == 0, "statistics are per 128-column tile");
-    constexpr int kThr = BN * 2;                       // 4 or 8 wavefronts
+    int total, int per_xcd) {
+    constexpr int BN = kPBN;
+    constexpr int kThr = BN * 2;                       // 4 wavefronts
     constexpr int kWN = BN / 64;                       // wavefronts along N
     constexpr int kAPer = kPBM * kPVecRow / kThr;      // A vectors per thread per step
     constexpr int kBPer = BN * kPVecRow / kThr;        // B vectors per thread per step
-    // operand tiles; with STATS the same memory later stages the whole output
-    // tile ([256][BN + 8] bf16: 68 KB at BN = 128, 135 KB at BN = 256)
-    constexpr int kStageLd = BN + 8;
-    constexpr int kOperands = (kPBM + BN) * kPLd;
-    constexpr int kSmem = STATS && kPBM * kStageLd > kOperands ? kPBM * kStageLd : kOperands;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[(kPBM + BN) * kPLd];
     uint16_t *As = smem;
     uint16_t *Bs = smem + kPBM * kPLd;
 
@@ -279,6 +265,179 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
         __syncthreads();
     }
 
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+            const int col = n0 + wn * 64 + ni * 32 + lane % 32;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * 128 + mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+                if (row < M && col < N) out[(size_t)row * N + col] = bf16_rne(acc[mi][ni][i]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Wide heads: 256 x 256 tiles, two wavefront groups in ping-pong
+// ---------------------------------------------------------------------------
+//
+// Eight wavefronts, two per SIMD, form two groups of four (group g holds
+// wavefronts 4g .. 4g + 3, one per SIMD).  Each wavefront owns a 128 x 64
+// sub-tile: rows 128 g .. + 127, columns 64 (wave % 4) .. + 63, 4 x 2 MFMA
+// 32x32x16 tiles.  The K loop runs in phases that end on a workgroup barrier.
+// In every phase one group reads its fragments from LDS and issues global
+// loads while the other group multiplies (16 MFMAs per wavefront, half a K
+// step of 64); the groups swap at each barrier, group 1 one phase behind, so
+// each SIMD's matrix pipe is fed by one wavefront while its partner waits on
+// memory.  Both groups pass the same number of barriers: group 1 takes one
+// extra before its first phase and group 0 one after its last.
+//
+// Operands go from global memory straight into LDS with global_load_lds_dwordx4
+// (one wavefront instruction fills 1 KiB of LDS; lane i writes its 16 bytes at
+// offset 16 i).  Group 0 moves the h tile, group 1 the head tile.  Two stages
+// of 64 KiB hold K steps j and j + 1: step j + 1's loads are issued in the
+// first phase of step j and waited for at the end of its third (group 0) or
+// fourth (group 1) phase, before either group reads them.  Rows past M or N
+// re-read the last valid row; their results are never stored.
+//
+// LDS rows are 128 bytes (64 k) without padding.  The 16-byte chunk c of tile
+// row r sits in slot c ^ f(r) with f(r) = (r & 6) | ((r ^ (r >> 3)) & 1): the
+// fragment reads (32 consecutive rows, one chunk) then touch every bank once
+// per cycle whether the LDS serves 8 lanes of 16 bytes (32 banks) or 16 lanes
+// (64 banks).  Lane i of a load fetches the chunk that belongs in slot i % 8,
+// so the DMA's linear fill produces that layout.
+//
+// With STATS the epilogue also emits, for every output row and every
+// 128-column tile, the softmax partial of the bf16 logits it writes: an integer
+// reference e = ceil(max * k2) and s = sum 2^(x * k2 - e) (k2 = log2(e) / T),
+// stored as two floats at stats[(row * ceil(N / 128) + tile) * 2].  The ISD
+// step can then take its row statistics from these instead of reading the
+// logits back.  The output tile is staged through the two LDS stages (rows of
+// group g in stage g, 16-byte chunks XOR-swizzled by row), leaves as 16-byte
+// row chunks, and thread t reduces the 128 staged columns of row t % 256 in
+// column tile t / 256 in two passes (max, then the sum of exponentials).
+
+constexpr int kWBM = 256, kWBN = 256, kWBK = 64;
+constexpr int kStage = (kWBM + kWBN) * kWBK * 2;     // 64 KiB: A rows, then B rows
+constexpr int kStageB = kWBM * kWBK * 2;             // byte offset of the B rows
+
+__device__ __forceinline__ int chunk_swz(int r) { return (r & 6) | ((r ^ (r >> 3)) & 1); }
+
+template <bool STATS>
+__global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restrict__ h,
+                                                         const uint16_t *__restrict__ wt, int M,
+                                                         int K, int N, uint16_t *__restrict__ out,
+                                                         int m_tiles, int total, int per_xcd,
+                                                         float k2, float *__restrict__ stats) {
+    // two separate arrays, so that loads into one stage are known not to
+    // alias fragment reads from the other
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStage];
+
+    const int b = blockIdx.x;
+    const int idx = (b % kXcds) * per_xcd + b / kXcds;
+    if (idx >= total) return;
+    const int m0 = (idx % m_tiles) * kWBM;
+    const int n0 = (idx / m_tiles) * kWBN;
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64;
+    const int g = wave / 4;                    // ping-pong group
+    const int wm = g, wn = wave % 4;           // 128 x 64 sub-tile
+
+    // loads: instruction t of this wavefront fills tile rows 64 (wave % 4) + 8 t
+    // .. + 7 of its group's operand; lane i takes row + i / 8, slot i % 8
+    const int lim = g == 0 ? M : N;
+    const int gbase = g == 0 ? m0 : n0;
+    const uint16_t *src = g == 0 ? h : wt;
+    const int ldsoff = g == 0 ? 0 : kStageB;
+    const uint16_t *gp[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int r = (wave % 4) * 64 + 8 * t + lane / 8;
+        const int grow = min(gbase + r, lim - 1);
+        gp[t] = src + (size_t)grow * K + ((lane % 8) ^ chunk_swz(r)) * 8;
+    }
+    auto load_step = [&](uint8_t *stage, int k0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            __builtin_amdgcn_global_load_lds(gp[t] + k0,
+                                             stage + ldsoff + ((wave % 4) * 64 + 8 * t) * 128, 16, 0, 0);
+    };
+
+    // fragments: the lane's rows are base + lane % 32 with base a multiple of
+    // 32, so the slot swizzle depends on lane % 16 only
+    const int sw = chunk_swz(lane & 15);
+    int aoff[4], boff[2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) aoff[mi] = (wm * 128 + mi * 32 + lane % 32) * 128;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) boff[ni] = kStageB + (wn * 64 + ni * 32 + lane % 32) * 128;
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+    bf16x8 af[2][4], bfr[2][2];
+    auto read_frags = [&](const uint8_t *stage, int half) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int co = (((half * 2 + q) * 2 + lane / 32) ^ sw) * 16;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                af[q][mi] = *reinterpret_cast<const bf16x8 *>(stage + aoff[mi] + co);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                bfr[q][ni] = *reinterpret_cast<const bf16x8 *>(stage + boff[ni] + co);
+        }
+    };
+    auto multiply = [&]() {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][mi], bfr[q][ni],
+                                                                         acc[mi][ni], 0, 0, 0);
+    };
+    // a phase boundary: nothing is scheduled across it
+    auto phase_end = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // s_waitcnt operands (gfx9 encoding): lgkmcnt(0) only; vmcnt(0) only;
+    // vmcnt(0) and lgkmcnt(0)
+    constexpr int kWaitLds = 0xC07F, kWaitVm = 0x0F70, kWaitBoth = 0x0070;
+
+    const int n = K / kWBK;
+    load_step(stage0, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
+    phase_end();
+    if (g == 1) phase_end();
+    auto step = [&](uint8_t *cur, uint8_t *nxt, int j) {
+        read_frags(cur, 0);                    // phase 4j (+ g): fragments, next step's loads
+        if (j + 1 < n) load_step(nxt, (j + 1) * kWBK);
+        __builtin_amdgcn_s_waitcnt(kWaitLds);
+        phase_end();
+        multiply();                            // phase 4j + 1 (+ g)
+        phase_end();
+        read_frags(cur, 1);                    // phase 4j + 2 (+ g): step j + 1 has landed
+        __builtin_amdgcn_s_waitcnt(kWaitBoth);
+        phase_end();
+        multiply();                            // phase 4j + 3 (+ g)
+        phase_end();
+    };
+    for (int j = 0; j < n; j += 2) {
+        step(stage0, stage1, j);
+        if (j + 1 < n) step(stage1, stage0, j + 1);
+    }
+    if (g == 0) phase_end();
+
     if constexpr (!STATS) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
@@ -292,54 +451,54 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
                 }
             }
     } else {
-        // The output tile is staged in LDS as bf16 (the K loop ended on a
-        // barrier, so the operand tiles are free) and leaves as 16-byte row
-        // chunks; thread t then reduces the 128 staged columns of row t in two
-        // passes (max, then the sum of 2^(x k2 - e)).
-        uint16_t *tileL = smem;   // [256][kStageLd]
+        // stage the bf16 tile: local row rl of group g at byte rl * 512 of
+        // stage g, its 16-byte chunk c at slot c ^ (rl & 31)
+        uint8_t *mine = g == 0 ? stage0 : stage1;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int rl = wm * 128 + mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+                    const int rl = mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
                     const int cl = wn * 64 + ni * 32 + lane % 32;
-                    tileL[rl * kStageLd + cl] = bf16_rne(acc[mi][ni][i]);
+                    *reinterpret_cast<uint16_t *>(mine + rl * 512 + (((cl >> 3) ^ (rl & 31)) << 4) +
+                                                  (cl & 7) * 2) = bf16_rne(acc[mi][ni][i]);
                 }
         __syncthreads();
-        // the logits leave the staged tile as 16-byte row chunks (a row's 16
-        // chunks are consecutive threads), or element by element at a ragged
-        // edge or when the output rows are not 16-byte aligned
+        auto staged = [&](int r, int c8) -> const uint8_t * {   // tile row r, chunk c8
+            const uint8_t *s = r < 128 ? stage0 : stage1;
+            const int rl = r & 127;
+            return s + rl * 512 + ((c8 ^ (rl & 31)) << 4);
+        };
+        // the logits leave as 16-byte row chunks (a row's 32 chunks are
+        // consecutive threads), or element by element at a ragged edge or when
+        // the output rows are not 16-byte aligned
         const bool vec_out = (N % 8) == 0 && ((uintptr_t)out % 16) == 0;
 #pragma unroll 4
-        for (int q = tid; q < kPBM * (BN / 8); q += kThr) {
-            const int rl = q / (BN / 8), c8 = (q % (BN / 8)) * 8;
-            const int grow = m0 + rl, gcol = n0 + c8;
-            if (grow >= M) continue;
-            const uint16_t *sp = &tileL[rl * kStageLd + c8];
+        for (int q = tid; q < kWBM * (kWBN / 8); q += 512) {
+            const int r = q / (kWBN / 8), c8 = q % (kWBN / 8);
+            const int grow = m0 + r, gcol = n0 + c8 * 8;
+            if (grow >= M || gcol >= N) continue;
+            const uint8_t *sp = staged(r, c8);
             uint16_t *dp = out + (size_t)grow * N + gcol;
             if (vec_out && gcol + 8 <= N) {
                 *reinterpret_cast<uint4 *>(dp) = *reinterpret_cast<const uint4 *>(sp);
             } else {
-                for (int e = 0; e < 8 && gcol + e < N; ++e) dp[e] = sp[e];
+                const uint16_t *se = reinterpret_cast<const uint16_t *>(sp);
+                for (int e = 0; e < 8 && gcol + e < N; ++e) dp[e] = se[e];
             }
         }
-    }
-    if constexpr (STATS) {
-        // thread tid reduces 128 columns of row tid % 256: 128-column tile
-        // tid / 256 of the workgroup's BN columns
-        static_assert(kThr == kPBM * (BN / kPBN), "one thread per row and 128-column tile");
-        const uint16_t *tileL = smem;
-        const int rl = tid % kPBM, sub = tid / kPBM;
-        const int row = m0 + rl;
-        const int c0 = n0 + sub * kPBN;
-        const uint16_t *src = &tileL[rl * kStageLd + sub * kPBN];
+        // thread tid reduces 128 columns of tile row tid % 256: 128-column
+        // tile tid / 256 of the workgroup's 256 columns
+        const int r = tid % kWBM, sub = tid / kWBM;
+        const int row = m0 + r;
+        const int c0 = n0 + sub * 128;
         const float neg = -__builtin_inff();
         float m = neg;
 #pragma unroll
-        for (int q8 = 0; q8 < kPBN / 8; ++q8) {
-            const uint4 w4 = *reinterpret_cast<const uint4 *>(src + q8 * 8);
+        for (int q8 = 0; q8 < 16; ++q8) {
+            const uint4 w4 = *reinterpret_cast<const uint4 *>(staged(r, sub * 16 + q8));
             const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -352,8 +511,8 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
         float sum = 0.0f;
         if (ref != neg) {
 #pragma unroll
-            for (int q8 = 0; q8 < kPBN / 8; ++q8) {
-                const uint4 w4 = *reinterpret_cast<const uint4 *>(src + q8 * 8);
+            for (int q8 = 0; q8 < 16; ++q8) {
+                const uint4 w4 = *reinterpret_cast<const uint4 *>(staged(r, sub * 16 + q8));
                 const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -365,7 +524,7 @@ __global__ __launch_bounds__(BN * 2, 256 / BN) void lm_head_packed_kernel(
             }
         }
         if (row < M && c0 < N) {
-            const size_t at = ((size_t)row * ((N + kPBN - 1) / kPBN) + c0 / kPBN) * 2;
+            const size_t at = ((size_t)row * ((N + 127) / 128) + c0 / 128) * 2;
             stats[at] = ref;
             stats[at + 1] = sum;
         }
@@ -573,23 +732,34 @@ hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, in
 
 namespace {
 
-// Tile widths: the LM head (N = 151936) and its statistics variant run on
-// 256-wide tiles, one workgroup per CU; the LoRA projection and other narrow
-// projections (N = 24576) on 128-wide ones, two workgroups per CU.
-constexpr int kHeadBN = 256;
-constexpr int kLoraBN = 128;
+// Wide heads (at least four 256-wide tiles per CU, as the LM head's 2376) run
+// on the ping-pong kernel; narrower projections (N = 24576: 384 such tiles,
+// 1.5 rounds over the CUs) balance better on the 128-wide tiles of the
+// two-segment kernel.
+constexpr int kWideTilesMin = 4 * 256;
 
-template <int BN, bool STATS>
 hipError_t launch_packed(const uint16_t *h, int K1, const uint16_t *h2, int K2, const uint16_t *wt,
-                         int M, int N, uint16_t *out, float k2, float *stats, hipStream_t stream) {
+                         int M, int N, uint16_t *out, hipStream_t stream) {
     const int m_tiles = (M + kPBM - 1) / kPBM;
-    const int n_tiles = (N + BN - 1) / BN;
+    const int n_tiles = (N + kPBN - 1) / kPBN;
     const long long total = (long long)m_tiles * n_tiles;
     if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
     const int per_xcd = (int)((total + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((lm_head_packed_kernel<BN, STATS>), dim3((unsigned)(per_xcd * kXcds)),
-                       dim3(BN * 2), 0, stream, h, K1, h2, K2, wt, M, N, out, m_tiles, (int)total,
-                       per_xcd, k2, stats);
+    hipLaunchKernelGGL(lm_head_packed_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0,
+                       stream, h, K1, h2, K2, wt, M, N, out, m_tiles, (int)total, per_xcd);
+    return hipGetLastError();
+}
+
+template <bool STATS>
+hipError_t launch_pp(const uint16_t *h, const uint16_t *wt, int M, int K, int N, uint16_t *out,
+                     float k2, float *stats, hipStream_t stream) {
+    const int m_tiles = (M + kWBM - 1) / kWBM;
+    const int n_tiles = (N + kWBN - 1) / kWBN;
+    const long long total = (long long)m_tiles * n_tiles;
+    if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
+    const int per_xcd = (int)((total + kXcds - 1) / kXcds);
+    hipLaunchKernelGGL((lm_head_pp_kernel<STATS>), dim3((unsigned)(per_xcd * kXcds)), dim3(512), 0,
+                       stream, h, wt, M, K, N, out, m_tiles, (int)total, per_xcd, k2, stats);
     return hipGetLastError();
 }
 
@@ -597,13 +767,10 @@ hipError_t launch_packed(const uint16_t *h, int K1, const uint16_t *h2, int K2, 
 
 hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
                                  uint16_t *out, hipStream_t stream) {
-    // 256-wide tiles when there are at least four per CU (the LM head: 1337 us
-    // against 1434 us on 128-wide tiles); narrower projections balance better
-    // on 128-wide ones (N = 24576: 230 us against 243 us)
-    const long long wide_tiles = (long long)((M + kPBM - 1) / kPBM) * ((N + kHeadBN - 1) / kHeadBN);
-    if (wide_tiles >= 4 * 256)
-        return launch_packed<kHeadBN, false>(h, K, nullptr, 0, wt, M, N, out, 0.0f, nullptr, stream);
-    return launch_packed<kLoraBN, false>(h, K, nullptr, 0, wt, M, N, out, 0.0f, nullptr, stream);
+    const long long wide_tiles = (long long)((M + kWBM - 1) / kWBM) * ((N + kWBN - 1) / kWBN);
+    if (wide_tiles >= kWideTilesMin)
+        return launch_pp<false>(h, wt, M, K, N, out, 0.0f, nullptr, stream);
+    return launch_packed(h, K, nullptr, 0, wt, M, N, out, stream);
 }
 
 hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t *wcat,
@@ -627,7 +794,7 @@ hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_packed<kLoraBN, false>(x, K, t, r, wcat, M, N, out, 0.0f, nullptr, stream);
+    return launch_packed(x, K, t, r, wcat, M, N, out, stream);
 }
 
 hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStream_t stream) {
@@ -638,7 +805,7 @@ hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStre
 
 hipError_t launch_lm_head_stats(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
                                 float k2, uint16_t *out, float *stats, hipStream_t stream) {
-    return launch_packed<kHeadBN, true>(h, K, nullptr, 0, wt, M, N, out, k2, stats, stream);
+    return launch_pp<true>(h, wt, M, K, N, out, k2, stats, stream);
 }
 
 }  // namespace isd
