@@ -35,11 +35,21 @@ constexpr int kAPerThread = kBM * kBK / 8 / kThreadsG;  // A vectors each thread
 constexpr int kBVecRow = kBN / 8;                       // 16-byte vectors per w row per step
 constexpr int kBPerThread = kBK * kBN / 8 / kThreadsG;  // w vectors each thread moves per step
 
+// fp32 -> bf16, round to nearest even, in integer arithmetic (a NaN keeps its
+// payload, made quiet)
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+// The same rounding in one v_cvt_pk_bf16_f32 (equal for every finite value and
+// infinity; a NaN comes out as the canonical quiet NaN).  The wide kernel's
+// epilogue converts 128 values per lane, so the instruction count matters
+// there.
+__device__ __forceinline__ uint16_t bf16_cvt(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __global__ __launch_bounds__(256) void lm_head_kernel(const uint16_t *__restrict__ h,
@@ -314,15 +324,37 @@ __global__ __launch_bounds__(256, 2) void lm_head_packed_kernel(
 // stored as two floats at stats[(row * ceil(N / 128) + tile) * 2].  The ISD
 // step can then take its row statistics from these instead of reading the
 // logits back.  The output tile is staged through the two LDS stages (rows of
-// group g in stage g, 16-byte chunks XOR-swizzled by row), leaves as 16-byte
-// row chunks, and thread t reduces the 128 staged columns of row t % 256 in
-// column tile t / 256 in two passes (max, then the sum of exponentials).
+// group g in stage g, 16-byte chunks XOR-swizzled by row).  Then each row of
+// 16 lanes takes one (row, 128-column tile) at a time: every lane reads one
+// 16-byte chunk of it once, stores it to the logits and reduces it, and the
+// 16 lanes combine their maxima, then their sums, with DPP exchanges.
 
 constexpr int kWBM = 256, kWBN = 256, kWBK = 64;
 constexpr int kStage = (kWBM + kWBN) * kWBK * 2;     // 64 KiB: A rows, then B rows
 constexpr int kStageB = kWBM * kWBK * 2;             // byte offset of the B rows
 
 __device__ __forceinline__ int chunk_swz(int r) { return (r & 6) | ((r ^ (r >> 3)) & 1); }
+
+// All-reduce over each row of 16 lanes: quad_perm [1,0,3,2] and [2,3,0,1]
+// within quads, then row_half_mirror (lane i <-> 7 - i) and row_mirror
+// (i <-> 15 - i); every lane ends with the same value (the pairs combine in
+// either order, and max and + are commutative).
+template <int CTRL>
+__device__ __forceinline__ float dpp16(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp16<0xB1>(v));
+    v = fmaxf(v, dpp16<0x4E>(v));
+    v = fmaxf(v, dpp16<0x141>(v));
+    return fmaxf(v, dpp16<0x140>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp16<0xB1>(v);
+    v += dpp16<0x4E>(v);
+    v += dpp16<0x141>(v);
+    return v + dpp16<0x140>(v);
+}
 
 template <bool STATS>
 __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restrict__ h,
@@ -447,7 +479,7 @@ __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restr
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int row = m0 + wm * 128 + mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
-                    if (row < M && col < N) out[(size_t)row * N + col] = bf16_rne(acc[mi][ni][i]);
+                    if (row < M && col < N) out[(size_t)row * N + col] = bf16_cvt(acc[mi][ni][i]);
                 }
             }
     } else {
@@ -463,7 +495,7 @@ __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restr
                     const int rl = mi * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
                     const int cl = wn * 64 + ni * 32 + lane % 32;
                     *reinterpret_cast<uint16_t *>(mine + rl * 512 + (((cl >> 3) ^ (rl & 31)) << 4) +
-                                                  (cl & 7) * 2) = bf16_rne(acc[mi][ni][i]);
+                                                  (cl & 7) * 2) = bf16_cvt(acc[mi][ni][i]);
                 }
         __syncthreads();
         auto staged = [&](int r, int c8) -> const uint8_t * {   // tile row r, chunk c8
@@ -471,62 +503,54 @@ __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restr
             const int rl = r & 127;
             return s + rl * 512 + ((c8 ^ (rl & 31)) << 4);
         };
-        // the logits leave as 16-byte row chunks (a row's 32 chunks are
-        // consecutive threads), or element by element at a ragged edge or when
-        // the output rows are not 16-byte aligned
+        // round j: lanes 16 q .. 16 q + 15 of wavefront w take pair
+        // 32 j + 4 w + q, i.e. tile row (pair / 2) and column tile (pair % 2);
+        // lane 16 q + i holds its 16-byte chunk i
         const bool vec_out = (N % 8) == 0 && ((uintptr_t)out % 16) == 0;
-#pragma unroll 4
-        for (int q = tid; q < kWBM * (kWBN / 8); q += 512) {
-            const int r = q / (kWBN / 8), c8 = q % (kWBN / 8);
-            const int grow = m0 + r, gcol = n0 + c8 * 8;
-            if (grow >= M || gcol >= N) continue;
-            const uint8_t *sp = staged(r, c8);
-            uint16_t *dp = out + (size_t)grow * N + gcol;
-            if (vec_out && gcol + 8 <= N) {
-                *reinterpret_cast<uint4 *>(dp) = *reinterpret_cast<const uint4 *>(sp);
-            } else {
-                const uint16_t *se = reinterpret_cast<const uint16_t *>(sp);
-                for (int e = 0; e < 8 && gcol + e < N; ++e) dp[e] = se[e];
-            }
-        }
-        // thread tid reduces 128 columns of tile row tid % 256: 128-column
-        // tile tid / 256 of the workgroup's 256 columns
-        const int r = tid % kWBM, sub = tid / kWBM;
-        const int row = m0 + r;
-        const int c0 = n0 + sub * 128;
+        const int nt = (N + 127) / 128;
+        const int sl = lane % 16;
         const float neg = -__builtin_inff();
-        float m = neg;
-#pragma unroll
-        for (int q8 = 0; q8 < 16; ++q8) {
-            const uint4 w4 = *reinterpret_cast<const uint4 *>(staged(r, sub * 16 + q8));
-            const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = c0 + q8 * 8 + 2 * e;
-                if (c < N) m = fmaxf(m, __uint_as_float(w[e] << 16));
-                if (c + 1 < N) m = fmaxf(m, __uint_as_float(w[e] & 0xFFFF0000u));
-            }
-        }
-        const float ref = m == neg ? neg : ceilf(m * k2);
-        float sum = 0.0f;
-        if (ref != neg) {
-#pragma unroll
-            for (int q8 = 0; q8 < 16; ++q8) {
-                const uint4 w4 = *reinterpret_cast<const uint4 *>(staged(r, sub * 16 + q8));
-                const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = c0 + q8 * 8 + 2 * e;
-                    if (c < N) sum += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(w[e] << 16), k2, -ref));
-                    if (c + 1 < N)
-                        sum += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(w[e] & 0xFFFF0000u), k2, -ref));
+#pragma unroll 2
+        for (int j = 0; j < 16; ++j) {
+            const int pair = 32 * j + 4 * wave + lane / 16;
+            const int r = pair / 2, sub = pair % 2;
+            const int grow = m0 + r, c0 = n0 + sub * 128, gcol = c0 + sl * 8;
+            const uint4 w4 = *reinterpret_cast<const uint4 *>(staged(r, sub * 16 + sl));
+            if (grow < M && gcol < N) {
+                uint16_t *dp = out + (size_t)grow * N + gcol;
+                if (vec_out && gcol + 8 <= N) {
+                    *reinterpret_cast<uint4 *>(dp) = w4;
+                } else {
+                    const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+                    for (int e = 0; e < 8 && gcol + e < N; ++e)
+                        dp[e] = (uint16_t)(wd[e / 2] >> (16 * (e % 2)));
                 }
             }
-        }
-        if (row < M && c0 < N) {
-            const size_t at = ((size_t)row * ((N + 127) / 128) + c0 / 128) * 2;
-            stats[at] = ref;
-            stats[at + 1] = sum;
+            const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = __uint_as_float(w[e] << 16);
+                x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            }
+            float m = neg;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (gcol + e < N) m = fmaxf(m, x[e]);
+            m = row16_max(m);
+            const float ref = m == neg ? neg : ceilf(m * k2);
+            float sum = 0.0f;
+            if (ref != neg) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (gcol + e < N) sum += __builtin_amdgcn_exp2f(fmaf(x[e], k2, -ref));
+            }
+            sum = row16_sum(sum);
+            if (sl == 0 && grow < M && c0 < N) {
+                const size_t at = ((size_t)grow * nt + c0 / 128) * 2;
+                stats[at] = ref;
+                stats[at + 1] = sum;
+            }
         }
     }
 }
