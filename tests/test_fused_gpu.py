@@ -139,6 +139,25 @@ def test_stats_and_fused_step_midsize(isd, T):
     log(f"fused midsize T={T}: {st}")
 
 
+@pytest.mark.parametrize("M,N", [(64, 20003), (300, 1029)])
+def test_stats_ragged_width_and_rows(isd, M, N):
+    """The statistics GEMM where N is not a multiple of 8 (element stores of the
+    logits, a last 128-column tile of 35 or 5 columns) and, at M = 300, a ragged
+    last row tile: the logits equal the exact product's bf16 bits and those of the
+    packed head, and every (row, tile) partial matches the fp64 definition."""
+    import torch
+    K = 256
+    d = gen_exact_head(M, K, N, seed=21)
+    h, wt = _dev(d["h"]), _dev(d["wt"])
+    logits, stats = isd.lm_head_stats(h, wt, 0.8)
+    base = isd.lm_head_packed(h, wt)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(logits), _bits(base)), "statistics epilogue changed the logits"
+    assert np.array_equal(_bits(logits), _oracle_logits(d["h"], d["wt"], np.arange(M)))
+    _check_stats(_bits(logits), stats.cpu().numpy(), 0.8)
+    log(f"statistics GEMM M={M} N={N}: logits exact, {stats.shape[1]} tiles per row checked")
+
+
 def test_fused_step_serving_shape(isd):
     """The serving shape: C=64, L=8, V=151936 from an H=4096 head.  Every
     sequence of both paths (statistics and plain) against the oracle under
