@@ -167,11 +167,11 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const uint16_t *__restrict
 // once), both MFMA operands are 8 consecutive k of one row: every global
 // load and every LDS store is one 16-byte vector, with no transposition.
 //
-// Narrow projections (the LoRA call, or any head with fewer than four 256-wide
-// tiles per CU) run on 256 x 128 tiles: four wavefronts, a single 55 KB LDS
-// buffer with the next K step's tiles held in registers while the current one
-// is multiplied, and two workgroups per CU whose barrier phases interleave.
-// Wide heads use the ping-pong kernel further down.
+// Small projections (fewer 256-wide tiles than CUs) run on 256 x 128 tiles:
+// four wavefronts, a single 55 KB LDS buffer with the next K step's tiles held
+// in registers while the current one is multiplied, and two workgroups per CU
+// whose barrier phases interleave.  Larger ones use the ping-pong kernel
+// further down.
 
 constexpr int kPBM = 256, kPBN = 128, kPBK = 64;
 constexpr int kPLd = kPBK + 8;                              // LDS row length (bf16), padded
@@ -356,12 +356,15 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v + dpp16<0x140>(v);
 }
 
-template <bool STATS>
+// With SEG2 the A operand has a second K segment, as in the 128-wide kernel:
+// columns [K, K + K2) come from h2 [M, K2], and wt is [N, K + K2].
+template <bool STATS, bool SEG2>
 __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restrict__ h,
                                                          const uint16_t *__restrict__ wt, int M,
                                                          int K, int N, uint16_t *__restrict__ out,
                                                          int m_tiles, int total, int per_xcd,
-                                                         float k2, float *__restrict__ stats) {
+                                                         float k2, float *__restrict__ stats,
+                                                         const uint16_t *__restrict__ h2, int K2) {
     // two separate arrays, so that loads into one stage are known not to
     // alias fragment reads from the other
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStage];
@@ -379,6 +382,7 @@ __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restr
 
     // loads: instruction t of this wavefront fills tile rows 64 (wave % 4) + 8 t
     // .. + 7 of its group's operand; lane i takes row + i / 8, slot i % 8
+    const int Kt = SEG2 ? K + K2 : K;          // row length of wt, extent of the K loop
     const int lim = g == 0 ? M : N;
     const int gbase = g == 0 ? m0 : n0;
     const uint16_t *src = g == 0 ? h : wt;
@@ -388,9 +392,22 @@ __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restr
     for (int t = 0; t < 8; ++t) {
         const int r = (wave % 4) * 64 + 8 * t + lane / 8;
         const int grow = min(gbase + r, lim - 1);
-        gp[t] = src + (size_t)grow * K + ((lane % 8) ^ chunk_swz(r)) * 8;
+        gp[t] = src + (size_t)grow * (g == 0 ? K : Kt) + ((lane % 8) ^ chunk_swz(r)) * 8;
     }
     auto load_step = [&](uint8_t *stage, int k0) {
+        if constexpr (SEG2) {
+            if (g == 0 && k0 >= K) {           // A columns from h2: rare, addresses made here
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int r = (wave % 4) * 64 + 8 * t + lane / 8;
+                    const int grow = min(m0 + r, M - 1);
+                    __builtin_amdgcn_global_load_lds(
+                        h2 + (size_t)grow * K2 + ((lane % 8) ^ chunk_swz(r)) * 8 + (k0 - K),
+                        stage + ((wave % 4) * 64 + 8 * t) * 128, 16, 0, 0);
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < 8; ++t)
             __builtin_amdgcn_global_load_lds(gp[t] + k0,
@@ -446,7 +463,7 @@ __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restr
     // vmcnt(0) and lgkmcnt(0)
     constexpr int kWaitLds = 0xC07F, kWaitVm = 0x0F70, kWaitBoth = 0x0070;
 
-    const int n = K / kWBK;
+    const int n = Kt / kWBK;
     load_step(stage0, 0);
     __builtin_amdgcn_s_waitcnt(kWaitVm);
     phase_end();
@@ -756,11 +773,10 @@ hipError_t launch_lm_head(const uint16_t *h, const uint16_t *w, int M, int K, in
 
 namespace {
 
-// Wide heads (at least four 256-wide tiles per CU, as the LM head's 2376) run
-// on the ping-pong kernel; narrower projections (N = 24576: 384 such tiles,
-// 1.5 rounds over the CUs) balance better on the 128-wide tiles of the
-// two-segment kernel.
-constexpr int kWideTilesMin = 4 * 256;
+// Projections with at least one 256-wide tile per CU (the LM head's 2376, the
+// MLP projection's 384) run on the ping-pong kernel; smaller ones, which
+// would leave CUs idle, on the 128-wide tiles of the single-group kernel.
+constexpr int kWideTilesMin = 256;
 
 hipError_t launch_packed(const uint16_t *h, int K1, const uint16_t *h2, int K2, const uint16_t *wt,
                          int M, int N, uint16_t *out, hipStream_t stream) {
@@ -774,26 +790,30 @@ hipError_t launch_packed(const uint16_t *h, int K1, const uint16_t *h2, int K2, 
     return hipGetLastError();
 }
 
-template <bool STATS>
-hipError_t launch_pp(const uint16_t *h, const uint16_t *wt, int M, int K, int N, uint16_t *out,
-                     float k2, float *stats, hipStream_t stream) {
+// h2 / K2: the second A segment (nullptr / 0 for none)
+template <bool STATS, bool SEG2>
+hipError_t launch_pp(const uint16_t *h, int K, const uint16_t *h2, int K2, const uint16_t *wt, int M,
+                     int N, uint16_t *out, float k2, float *stats, hipStream_t stream) {
     const int m_tiles = (M + kWBM - 1) / kWBM;
     const int n_tiles = (N + kWBN - 1) / kWBN;
     const long long total = (long long)m_tiles * n_tiles;
     if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
     const int per_xcd = (int)((total + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((lm_head_pp_kernel<STATS>), dim3((unsigned)(per_xcd * kXcds)), dim3(512), 0,
-                       stream, h, wt, M, K, N, out, m_tiles, (int)total, per_xcd, k2, stats);
+    hipLaunchKernelGGL((lm_head_pp_kernel<STATS, SEG2>), dim3((unsigned)(per_xcd * kXcds)), dim3(512),
+                       0, stream, h, wt, M, K, N, out, m_tiles, (int)total, per_xcd, k2, stats, h2, K2);
     return hipGetLastError();
+}
+
+long long wide_tiles(int M, int N) {
+    return (long long)((M + kWBM - 1) / kWBM) * ((N + kWBN - 1) / kWBN);
 }
 
 }  // namespace
 
 hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
                                  uint16_t *out, hipStream_t stream) {
-    const long long wide_tiles = (long long)((M + kWBM - 1) / kWBM) * ((N + kWBN - 1) / kWBN);
-    if (wide_tiles >= kWideTilesMin)
-        return launch_pp<false>(h, wt, M, K, N, out, 0.0f, nullptr, stream);
+    if (wide_tiles(M, N) >= kWideTilesMin)
+        return launch_pp<false, false>(h, K, nullptr, 0, wt, M, N, out, 0.0f, nullptr, stream);
     return launch_packed(h, K, nullptr, 0, wt, M, N, out, stream);
 }
 
@@ -818,6 +838,8 @@ hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (wide_tiles(M, N) >= kWideTilesMin)
+        return launch_pp<false, true>(x, K, t, r, wcat, M, N, out, 0.0f, nullptr, stream);
     return launch_packed(x, K, t, r, wcat, M, N, out, stream);
 }
 
@@ -829,7 +851,7 @@ hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStre
 
 hipError_t launch_lm_head_stats(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
                                 float k2, uint16_t *out, float *stats, hipStream_t stream) {
-    return launch_pp<true>(h, wt, M, K, N, out, k2, stats, stream);
+    return launch_pp<true, false>(h, K, nullptr, 0, wt, M, N, out, k2, stats, stream);
 }
 
 }  // namespace isd

@@ -123,15 +123,15 @@ def test_lm_head_packed_full_shape_sampled_rows(isd):
         f"exact-rounded fraction {frac:.5f}")
 
 
-@pytest.mark.parametrize("M,N", [(1024, 65280), (1024, 65536), (1000, 65544), (1000, 65541)])
+@pytest.mark.parametrize("M,N", [(1024, 16128), (1024, 16384), (1000, 16392), (1000, 16389)])
 def test_lm_head_packed_tile_width_threshold(isd, M, N):
-    """1024 rows give four 256-row tiles; N = 65280 makes 1020 tiles of 256 columns
-    (the packed head then runs on the 128-wide two-segment kernel), N = 65536 exactly
-    1024 (the 256-wide ping-pong kernel), and M = 1000 with N = 65544 or 65541 takes the
-    wide kernel with a ragged last row tile and a ragged last column tile.  Every case
-    must hold the oracle's bound on sampled rows and, where the unpacked kernel accepts
-    the shape (N a multiple of 8), agree bit for bit with it: it accumulates in the same
-    K order."""
+    """1024 rows give four 256-row tiles; N = 16128 makes 252 tiles of 256 columns,
+    fewer than the CUs (the packed head then runs on the 128-wide kernel), N = 16384
+    exactly 256 (the 256-wide ping-pong kernel), and M = 1000 with N = 16392 or 16389
+    takes the wide kernel with a ragged last row tile and a ragged last column tile.
+    Every case must hold the oracle's bound on sampled rows and, where the unpacked
+    kernel accepts the shape (N a multiple of 8), agree bit for bit with it: it
+    accumulates in the same K order."""
     import torch
     K = 512
     rng = np.random.default_rng(N)

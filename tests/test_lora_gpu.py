@@ -118,10 +118,36 @@ def test_lora_split_shrink_ragged(isd):
     log(f"lora split shrink: worst h err/bound {worst:.3f}, t err/bound {t_worst:.3f}")
 
 
+def test_lora_wide_tiles_ragged(isd):
+    """At least one 256 x 256 output tile per CU (4 x 65 here) takes the
+    ping-pong kernel with its second K segment: 1000 rows (a ragged last row
+    tile), N = 16389 (a ragged, odd last column tile), K = 256, r = 128.
+    Sampled rows meet the bound, and every clean row equals the base
+    projection bit for bit."""
+    import torch
+    cfg = dict(LORA_CONFIGS["mid"], C=100, L=10, N=16389, K=256, r=128)
+    d = gen_lora(cfg, seed=7)
+    mask = d["mask"]
+    x, a = _dev(d["x"]), _dev(d["a"])
+    wcat = isd.lora_pack(_dev(d["w"]), _dev(d["b"]))
+    h, t = isd.lora_gemm(x, a, wcat, torch.from_numpy(mask).cuda())
+    base = isd.lm_head_packed(x, _dev(d["w"]))
+    torch.cuda.synchronize()
+    hb, tb = _host(h), _host(t)
+    rows = np.unique(np.concatenate([np.arange(0, 1000, 37), [255, 256, 511, 512, 767, 768, 998, 999]]))
+    worst, t_worst = _check(d, hb, tb, rows, mask)
+    clean = mask == 0
+    assert clean.any() and (~clean).any()
+    np.testing.assert_array_equal(hb[clean], _host(base)[clean])
+    log(f"lora wide tiles 1000 x 256 x 16389: worst h err/bound {worst:.3f}, "
+        f"t err/bound {t_worst:.3f}, {int(clean.sum())} clean rows equal the base projection")
+
+
 def test_lora_full_shape_sampled_rows(isd):
     """The MLP gate/up projection of an 8B model at the serving batch:
-    M = 1024, K = 4096, N = 24576, r = 128; every adapter activation and
-    the full output rows of a clean and a mask position of several sequences."""
+    M = 1024, K = 4096, N = 24576, r = 128; every adapter activation, the
+    full output rows of a clean and a mask position of several sequences,
+    and every clean row against the base projection, bit for bit."""
     import torch
     cfg = LORA_CONFIGS["mlp_up"]
     d = gen_lora(cfg, seed=0)
@@ -129,8 +155,11 @@ def test_lora_full_shape_sampled_rows(isd):
     x, a = _dev(d["x"]), _dev(d["a"])
     wcat = isd.lora_pack(_dev(d["w"]), _dev(d["b"]))
     h, t = isd.lora_gemm(x, a, wcat, torch.from_numpy(mask).cuda())
+    base = isd.lm_head_packed(x, _dev(d["w"]))
     torch.cuda.synchronize()
     hb, tb = _host(h), _host(t)
+    clean = mask == 0
+    np.testing.assert_array_equal(hb[clean], _host(base)[clean])
     rows = np.array([0, 7, 8, 15, 500, 511, 1016, 1023])
     worst, t_worst = _check(d, hb, tb, rows, mask)
     # all adapter activations
