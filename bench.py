@@ -297,6 +297,8 @@ def lm_head_workload(args):
     nt = (V + isd.isd.STATS_TILE - 1) // isd.isd.STATS_TILE
     stats = [torch.empty((M, nt, 2), dtype=torch.float32, device=dev) for _ in range(2)]
     xs = [torch.zeros((C, L), dtype=torch.int32, device=dev) for _ in range(2)]
+    # the plain GEMM's workspace: the tiles of its last partial round are halved along K
+    gws = isd.gemm_workspace(M, H, V)
     torch.cuda.synchronize()
     print(f"# W [{H}, {V}] and hidden states ready, {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
@@ -313,7 +315,7 @@ def lm_head_workload(args):
         if args.fused:
             isd.lm_head_stats(h, Wt, T, out=logits[i % 2], stats=stats[i % 2])
         else:
-            isd.lm_head_packed(h, Wt, out=logits[i % 2])
+            isd.lm_head_packed(h, Wt, out=logits[i % 2], workspace=gws)
 
     def verify_propose(i):
         p, qn = views(i)
@@ -372,6 +374,7 @@ def lm_head_workload(args):
         config=dict(workload=f"LM head + ISD step: h [{M}, {H}] x W [{H}, {V}] bf16, then "
                              f"C={C}, L={L} verify/propose", C=C, L=L, V=V, H=H,
                     head_layout="W packed once (untimed) to k-contiguous [V, H]",
+                    k_split_workspace_bytes=0 if (args.fused or gws is None) else gws.numel(),
                     step_input="LM-head tile statistics" if args.fused else "logits"),
         roofline=dict(bound="mfma", achieved=round(gemm_tflops, 1), peak=2500.0,
                       unit="TFLOP/s", frac=round(gemm_tflops / 2500.0, 4),
@@ -429,6 +432,8 @@ def lora_workload(args):
     N, r = w.shape[0], a.shape[0]
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     t = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    # the GEMM's workspace: the tiles of its last partial round are halved along K
+    ws = isd.gemm_workspace(M, K, N)
     stream = torch.cuda.current_stream()
 
     def timed(fn):
@@ -445,8 +450,8 @@ def lora_workload(args):
         return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t0) * 1e3 / args.steps
 
     read_probe()
-    base_ms, _ = timed(lambda: isd.lm_head_packed(x, w, out=out))
-    lora_ms, wall_ms = timed(lambda: isd.lora_gemm(x, a, wcat, mask, out=out, t=t))
+    base_ms, _ = timed(lambda: isd.lm_head_packed(x, w, out=out, workspace=ws))
+    lora_ms, wall_ms = timed(lambda: isd.lora_gemm(x, a, wcat, mask, out=out, t=t, workspace=ws))
     gated = int((d["mask"] != 0).sum())
     flops = 2.0 * M * K * N + 2.0 * gated * r * (K + N)
     tflops = flops / (lora_ms * 1e-3) / 1e12
@@ -460,7 +465,8 @@ def lora_workload(args):
         roofline=dict(bound="mfma", achieved=round(tflops, 1), peak=2500.0, unit="TFLOP/s",
                       frac=round(tflops / 2500.0, 4), traffic=None),
         kernel_us_avg=round(lora_ms * 1e3, 2), base_projection_us=round(base_ms * 1e3, 2),
-        adapter_overhead=round(lora_ms / base_ms - 1.0, 4))), flush=True)
+        adapter_overhead=round(lora_ms / base_ms - 1.0, 4),
+        k_split_workspace_bytes=0 if ws is None else ws.numel())), flush=True)
 
 
 def step_workload(args):

@@ -281,9 +281,20 @@ isd_status_t isd_lm_head(const void *h, const void *w, int32_t M, int32_t K, int
 /* The LM head on a pre-packed head: logits[M, N] = h[M, K] @ wt[N, K]^T,
  * where wt = w^T is k-contiguous per vocabulary row (isd_lm_head_pack).  Same
  * arithmetic and rounding as isd_lm_head; K % 64 == 0; h and wt 16-byte
- * aligned.  No workspace is used (pass NULL, 0). */
+ * aligned.  The workspace is optional (NULL, 0: none): given at least
+ * isd_gemm_workspace_bytes(M, K, N) bytes, 256-byte aligned and zero-filled
+ * before its first use, the output tiles of a last partial round over the
+ * CUs are computed as two halves along K that meet in it (each call leaves
+ * its counters zero again; calls that share one workspace must not overlap).
+ * Those tiles then sum two fp32 partial products, so they can differ from the
+ * unsplit result by the fp32 rounding of that sum; the split is deterministic. */
 isd_status_t isd_lm_head_packed(const void *h, const void *wt, int32_t M, int32_t K, int32_t N,
                                 void *logits, void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of the optional workspace of isd_lm_head_packed and isd_lora_gemm
+ * for an output of M x N and a (first) K segment of K; 0 when the K split
+ * does not apply to the shape (the workspace is then not used). */
+size_t isd_gemm_workspace_bytes(int32_t M, int32_t K, int32_t N);
 
 /* One-time packing of a head w[K, N] (bf16, row-major) into wt[N, K]
  * (caller-allocated, 16-byte aligned): a bit-exact transpose. */
@@ -397,6 +408,12 @@ isd_status_t isd_step_fused(const isd_shape_t *s, const void *p_logits, const vo
  *                      aligned, r is a multiple of 128 and it can hold
  *                      ceil(K / 256) * M * r floats, it first holds the
  *                      shrink's partial sums (split over K)
+ *   workspace, ws_bytes  optional, as for isd_lm_head_packed: with at least
+ *                      isd_gemm_workspace_bytes(M, K, N) bytes the GEMM
+ *                      halves the tiles of its last partial round along K
+ *                      (the halves split at the same K step as the base
+ *                      projection's, so clean rows still equal it bit for
+ *                      bit when both are given a workspace)
  * K and r must be multiples of 64.  Two or three launches on `stream` (the
  * shrink, in one kernel or as partial sums and their sum, then one GEMM over
  * the concatenated K); no host synchronisation, no allocation, so the call
@@ -404,7 +421,7 @@ isd_status_t isd_step_fused(const isd_shape_t *s, const void *p_logits, const vo
  * for bad sizes or pointers, ISD_ERR_DEVICE if a launch fails. */
 isd_status_t isd_lora_gemm(const void *x, const void *a, const void *wcat, const int32_t *mask,
                            int32_t M, int32_t K, int32_t N, int32_t r, void *t, void *out,
-                           void *stream);
+                           void *workspace, size_t ws_bytes, void *stream);
 
 /* wcat [N, K + r] = (W [N, K] | B [N, r]), row by row (two 2-D device copies on
  * `stream`, done once per adapter).  All bf16, 2-byte aligned. */

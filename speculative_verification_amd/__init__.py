@@ -19,6 +19,7 @@ from .isd import (  # noqa: F401
     check_device_error,
     decode_commit,
     decode_masks,
+    gemm_workspace,
     lib,
     lm_head,
     lm_head_pack,

@@ -618,18 +618,23 @@ isd_status_t isd_lm_head_pack(const void *w, int32_t K, int32_t N, void *wt, voi
     return ISD_OK;
 }
 
+size_t isd_gemm_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+    if (M < 1 || N < 1 || K < 64 || K % 64) return 0;
+    return gemm_workspace_bytes(M, K, N);
+}
+
 isd_status_t isd_lm_head_packed(const void *h, const void *wt, int32_t M, int32_t K, int32_t N,
                                 void *logits, void *workspace, size_t ws_bytes, void *stream) {
-    (void)workspace;
-    (void)ws_bytes;
     ISD_TRY(check_ptr(h, "h", 16));
     ISD_TRY(check_ptr(wt, "wt", 16));
     ISD_TRY(check_ptr(logits, "logits", 2));
+    if (workspace) ISD_TRY(check_ptr(workspace, "workspace", 256));
     if (M < 1 || N < 1 || K < 1) return fail(ISD_ERR_ARG, "M, K, N must be >= 1");
     if (K % 64) return fail(ISD_ERR_ARG, "K must be a multiple of 64 (got %d)", (int)K);
     const hipError_t e = launch_lm_head_packed(static_cast<const uint16_t *>(h),
                                                static_cast<const uint16_t *>(wt), M, K, N,
-                                               static_cast<uint16_t *>(logits), (hipStream_t)stream);
+                                               static_cast<uint16_t *>(logits), workspace,
+                                               workspace ? ws_bytes : 0, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "lm_head launch failed: %s", hipGetErrorString(e));
     return ISD_OK;
 }
@@ -725,20 +730,21 @@ isd_status_t isd_lora_pack(const void *w, const void *b, int32_t N, int32_t K, i
 
 isd_status_t isd_lora_gemm(const void *x, const void *a, const void *wcat, const int32_t *mask,
                            int32_t M, int32_t K, int32_t N, int32_t r, void *t, void *out,
-                           void *stream) {
+                           void *workspace, size_t ws_bytes, void *stream) {
     ISD_TRY(check_ptr(x, "x", 16));
     ISD_TRY(check_ptr(a, "a", 16));
     ISD_TRY(check_ptr(wcat, "wcat", 16));
     ISD_TRY(check_ptr(t, "t", 16));
     ISD_TRY(check_ptr(out, "out", 2));
     if (mask) ISD_TRY(check_ptr(mask, "mask", 4));
+    if (workspace) ISD_TRY(check_ptr(workspace, "workspace", 256));
     if (M < 1 || N < 1 || K < 1 || r < 1) return fail(ISD_ERR_ARG, "M, K, N, r must be >= 1");
     if (K % 64) return fail(ISD_ERR_ARG, "K must be a multiple of 64 (got %d)", (int)K);
     if (r % 64) return fail(ISD_ERR_ARG, "r must be a multiple of 64 (got %d)", (int)r);
     const hipError_t e = launch_lora_gemm(
         static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(a),
         static_cast<const uint16_t *>(wcat), mask, M, K, N, r, static_cast<uint16_t *>(t),
-        static_cast<uint16_t *>(out), (hipStream_t)stream);
+        static_cast<uint16_t *>(out), workspace, workspace ? ws_bytes : 0, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "lora launch failed: %s", hipGetErrorString(e));
     return ISD_OK;
 }

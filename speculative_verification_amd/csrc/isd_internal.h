@@ -180,9 +180,13 @@ hipError_t launch_decode_commit(int C, int L, int32_t *state, const int32_t *acc
                                 const int32_t *anchor, int32_t *history, int64_t hist_cap,
                                 int64_t *tokens, int64_t *forwards, hipStream_t stream);
 
-// LM-head GEMM on a pre-packed head wt = w^T [N, K], and the packing.
+// LM-head GEMM on a pre-packed head wt = w^T [N, K], and the packing.  With a
+// workspace of gemm_workspace_bytes(M, K, N) bytes (zero-filled once; each
+// launch leaves its counters zero) the tiles of a last partial round are
+// halved along K; 0 bytes: that split does not apply to the shape.
+size_t gemm_workspace_bytes(int M, int K, int N);
 hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
-                                 uint16_t *out, hipStream_t stream);
+                                 uint16_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStream_t stream);
 
 // The packed LM-head GEMM that also writes per-(row, 128-column tile) softmax
@@ -195,7 +199,7 @@ hipError_t launch_lm_head_stats(const uint16_t *h, const uint16_t *wt, int M, in
 // with wcat = (w | b) [N, K + r].
 hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t *wcat,
                             const int32_t *mask, int M, int K, int N, int r, uint16_t *t,
-                            uint16_t *out, hipStream_t stream);
+                            uint16_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 // Streaming-read probe over n_tiles 2048-element bf16 tiles (4 KiB each),
 // tiles_per_group consecutive tiles per workgroup.

@@ -358,21 +358,51 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 // With SEG2 the A operand has a second K segment, as in the 128-wide kernel:
 // columns [K, K + K2) come from h2 [M, K2], and wt is [N, K + K2].
-template <bool STATS, bool SEG2>
+//
+// With SPLIT the tiles past the last whole round over the CUs are cut in two
+// along K, so that the last round is half as long: workgroups 0 .. n_full - 1
+// take whole tiles n_full .. (the first n_full), the rest take the K steps
+// [0, ks) or [ks, n) of one remaining tile.  Each half stores its fp32 tile
+// in the workspace (agent-scope atomic stores, coherent across the XCDs) and
+// counts itself on the tile's counter; the second to arrive adds the other
+// half's tile to its own (fp32 addition is commutative, so the result does
+// not depend on which half comes last), stores the output and resets the
+// counter.  No half waits for the other.
+struct SplitArgs {
+    int n_full;                // whole tiles (a multiple of 8)
+    int ks;                    // K steps of the first half
+    float *part;               // [tiles - n_full][2][256 * 256] fp32 halves
+    uint32_t *cnt;             // [tiles - n_full] counters, 128 bytes apart, zero between launches
+};
+
+template <bool STATS, bool SEG2, bool SPLIT>
 __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restrict__ h,
                                                          const uint16_t *__restrict__ wt, int M,
                                                          int K, int N, uint16_t *__restrict__ out,
                                                          int m_tiles, int total, int per_xcd,
                                                          float k2, float *__restrict__ stats,
-                                                         const uint16_t *__restrict__ h2, int K2) {
+                                                         const uint16_t *__restrict__ h2, int K2,
+                                                         SplitArgs sp) {
     // two separate arrays, so that loads into one stage are known not to
     // alias fragment reads from the other
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStage];
 
     const int b = blockIdx.x;
-    const int idx = (b % kXcds) * per_xcd + b / kXcds;
-    if (idx >= total) return;
+    int idx, half = -1;
+    if constexpr (SPLIT) {
+        if (b < sp.n_full) {
+            idx = (b % kXcds) * (sp.n_full / kXcds) + b / kXcds;
+        } else {                               // the two halves of a tile share an XCD
+            const int u = b - sp.n_full, nu = (int)gridDim.x - sp.n_full;
+            const int q = (u % kXcds) * (nu / kXcds) + u / kXcds;
+            idx = sp.n_full + q / 2;
+            half = q % 2;
+        }
+    } else {
+        idx = (b % kXcds) * per_xcd + b / kXcds;
+        if (idx >= total) return;
+    }
     const int m0 = (idx % m_tiles) * kWBM;
     const int n0 = (idx / m_tiles) * kWBN;
     const int tid = threadIdx.x;
@@ -463,14 +493,19 @@ __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restr
     // vmcnt(0) and lgkmcnt(0)
     constexpr int kWaitLds = 0xC07F, kWaitVm = 0x0F70, kWaitBoth = 0x0070;
 
-    const int n = Kt / kWBK;
-    load_step(stage0, 0);
+    // K steps [j0, j1) of the tile
+    int j0 = 0, j1 = Kt / kWBK;
+    if constexpr (SPLIT) {
+        if (half == 0) j1 = sp.ks;
+        if (half == 1) j0 = sp.ks;
+    }
+    load_step(stage0, j0 * kWBK);
     __builtin_amdgcn_s_waitcnt(kWaitVm);
     phase_end();
     if (g == 1) phase_end();
     auto step = [&](uint8_t *cur, uint8_t *nxt, int j) {
         read_frags(cur, 0);                    // phase 4j (+ g): fragments, next step's loads
-        if (j + 1 < n) load_step(nxt, (j + 1) * kWBK);
+        if (j + 1 < j1) load_step(nxt, (j + 1) * kWBK);
         __builtin_amdgcn_s_waitcnt(kWaitLds);
         phase_end();
         multiply();                            // phase 4j + 1 (+ g)
@@ -481,11 +516,59 @@ __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restr
         multiply();                            // phase 4j + 3 (+ g)
         phase_end();
     };
-    for (int j = 0; j < n; j += 2) {
+    for (int j = j0; j < j1; j += 2) {
         step(stage0, stage1, j);
-        if (j + 1 < n) step(stage1, stage0, j + 1);
+        if (j + 1 < j1) step(stage1, stage0, j + 1);
     }
     if (g == 0) phase_end();
+
+    if constexpr (SPLIT) {
+        if (half >= 0) {
+            // this half's tile, wavefront-major: 64-bit word ((wave * 8 + mi * 2 + ni) * 8
+            // + i / 2) * 64 + lane holds elements i, i + 1 of accumulator (mi, ni)
+            const int si = idx - sp.n_full;
+            uint64_t *mine = reinterpret_cast<uint64_t *>(sp.part + ((size_t)si * 2 + half) * (kWBM * kWBN));
+            const uint64_t *other =
+                reinterpret_cast<const uint64_t *>(sp.part + ((size_t)si * 2 + (1 - half)) * (kWBM * kWBN));
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                    for (int i = 0; i < 16; i += 2) {
+                        const uint64_t w = (uint64_t)__float_as_uint(acc[mi][ni][i]) |
+                                           ((uint64_t)__float_as_uint(acc[mi][ni][i + 1]) << 32);
+                        __hip_atomic_store(&mine[((wave * 8 + mi * 2 + ni) * 8 + i / 2) * 64 + lane], w,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+            // every wavefront's stores complete, then one count per half
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            uint32_t *cnt = sp.cnt + (size_t)si * kCounterStride;
+            volatile uint32_t *flag = reinterpret_cast<volatile uint32_t *>(stage0);
+            if (tid == 0) {
+                const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (prev == 1) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *flag = prev;
+            }
+            __syncthreads();
+            if (*flag != 1) return;            // the first half: the other one finishes the tile
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                    for (int i = 0; i < 16; i += 2) {
+                        const uint64_t w = __hip_atomic_load(
+                            const_cast<uint64_t *>(&other[((wave * 8 + mi * 2 + ni) * 8 + i / 2) * 64 + lane]),
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        acc[mi][ni][i] += __uint_as_float((uint32_t)w);
+                        acc[mi][ni][i + 1] += __uint_as_float((uint32_t)(w >> 32));
+                    }
+        }
+    }
 
     if constexpr (!STATS) {
 #pragma unroll
@@ -791,16 +874,18 @@ hipError_t launch_packed(const uint16_t *h, int K1, const uint16_t *h2, int K2, 
 }
 
 // h2 / K2: the second A segment (nullptr / 0 for none)
-template <bool STATS, bool SEG2>
+template <bool STATS, bool SEG2, bool SPLIT = false>
 hipError_t launch_pp(const uint16_t *h, int K, const uint16_t *h2, int K2, const uint16_t *wt, int M,
-                     int N, uint16_t *out, float k2, float *stats, hipStream_t stream) {
+                     int N, uint16_t *out, float k2, float *stats, hipStream_t stream,
+                     SplitArgs sp = SplitArgs{0, 0, nullptr, nullptr}, int n_split = 0) {
     const int m_tiles = (M + kWBM - 1) / kWBM;
     const int n_tiles = (N + kWBN - 1) / kWBN;
     const long long total = (long long)m_tiles * n_tiles;
     if (total >= (1LL << 31) / kXcds) return hipErrorInvalidValue;
     const int per_xcd = (int)((total + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((lm_head_pp_kernel<STATS, SEG2>), dim3((unsigned)(per_xcd * kXcds)), dim3(512),
-                       0, stream, h, wt, M, K, N, out, m_tiles, (int)total, per_xcd, k2, stats, h2, K2);
+    const unsigned grid = SPLIT ? (unsigned)(sp.n_full + 2 * n_split) : (unsigned)(per_xcd * kXcds);
+    hipLaunchKernelGGL((lm_head_pp_kernel<STATS, SEG2, SPLIT>), dim3(grid), dim3(512), 0, stream, h, wt,
+                       M, K, N, out, m_tiles, (int)total, per_xcd, k2, stats, h2, K2, sp);
     return hipGetLastError();
 }
 
@@ -808,18 +893,58 @@ long long wide_tiles(int M, int N) {
     return (long long)((M + kWBM - 1) / kWBM) * ((N + kWBN - 1) / kWBN);
 }
 
+// The K split of the last partial round: it applies when the tiles past the
+// whole rounds over the CUs fill at most half a round (their halves then fill
+// at most one), their number is a multiple of 4 (the halves spread evenly over
+// the XCDs), and the first K segment has at least two steps.  The workspace
+// holds one 128-byte counter per split tile, then its two fp32 halves.
+constexpr int kCUs = 256;
+
+struct SplitPlan {
+    int n_full, n_split, ks;
+    size_t bytes;
+};
+
+SplitPlan split_plan(int M, int K1, int N) {
+    SplitPlan p{0, 0, 0, 0};
+    const long long tiles = wide_tiles(M, N);
+    const long long rem = tiles % kCUs;
+    if (tiles < kCUs || rem == 0 || 2 * rem > kCUs || rem % 4 != 0 || K1 / kWBK < 2) return p;
+    p.n_full = (int)(tiles - rem);
+    p.n_split = (int)rem;
+    p.ks = K1 / kWBK / 2;
+    p.bytes = (size_t)rem * kCounterStride * sizeof(uint32_t) + (size_t)rem * 2 * kWBM * kWBN * sizeof(float);
+    return p;
+}
+
+// The ping-pong GEMM, split when the plan applies and the workspace is large enough.
+template <bool SEG2>
+hipError_t launch_pp_maybe_split(const uint16_t *h, int K, const uint16_t *h2, int K2, const uint16_t *wt,
+                                 int M, int N, uint16_t *out, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    const SplitPlan p = split_plan(M, K, N);
+    if (p.n_split == 0 || ws == nullptr || ws_bytes < p.bytes)
+        return launch_pp<false, SEG2>(h, K, h2, K2, wt, M, N, out, 0.0f, nullptr, stream);
+    uint32_t *cnt = static_cast<uint32_t *>(ws);
+    float *part = reinterpret_cast<float *>(cnt + (size_t)p.n_split * kCounterStride);
+    return launch_pp<false, SEG2, true>(h, K, h2, K2, wt, M, N, out, 0.0f, nullptr, stream,
+                                        SplitArgs{p.n_full, p.ks, part, cnt}, p.n_split);
+}
+
 }  // namespace
 
+size_t gemm_workspace_bytes(int M, int K, int N) { return split_plan(M, K, N).bytes; }
+
 hipError_t launch_lm_head_packed(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
-                                 uint16_t *out, hipStream_t stream) {
+                                 uint16_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
     if (wide_tiles(M, N) >= kWideTilesMin)
-        return launch_pp<false, false>(h, K, nullptr, 0, wt, M, N, out, 0.0f, nullptr, stream);
+        return launch_pp_maybe_split<false>(h, K, nullptr, 0, wt, M, N, out, ws, ws_bytes, stream);
     return launch_packed(h, K, nullptr, 0, wt, M, N, out, stream);
 }
 
 hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t *wcat,
                             const int32_t *mask, int M, int K, int N, int r, uint16_t *t,
-                            uint16_t *out, hipStream_t stream) {
+                            uint16_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
     // the split-K shrink when the output buffer can hold its fp32 partials
     const int slices = (K + kSpSlice - 1) / kSpSlice;
     const bool split = r % kSpCh == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0 &&
@@ -839,7 +964,7 @@ hipError_t launch_lora_gemm(const uint16_t *x, const uint16_t *a, const uint16_t
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (wide_tiles(M, N) >= kWideTilesMin)
-        return launch_pp<false, true>(x, K, t, r, wcat, M, N, out, 0.0f, nullptr, stream);
+        return launch_pp_maybe_split<true>(x, K, t, r, wcat, M, N, out, ws, ws_bytes, stream);
     return launch_packed(x, K, t, r, wcat, M, N, out, stream);
 }
 

@@ -62,7 +62,9 @@ _SIGS = {
     "isd_lm_head_stats": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp, _vp]),
     "isd_step_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 10 + [_i64, _i64] +
                        [_vp] * 8 + [_vp, _sz, _vp]),
-    "isd_lora_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "isd_lora_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
+                                     _vp]),
+    "isd_gemm_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "isd_read_probe": (ctypes.c_int, [_vp, _sz, _i32, _vp, _vp]),
     "isd_step_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 16 + [_vp]),
     "isd_last_error": (ctypes.c_char_p, []),
@@ -450,8 +452,25 @@ def lm_head_pack(w):
     return wt
 
 
-def lm_head_packed(h, wt, out=None):
-    """logits [M, N] = h [M, K] @ wt [N, K]^T (bf16, fp32 accumulation on MFMA)."""
+def gemm_workspace(M: int, K: int, N: int, device="cuda"):
+    """A zero-filled workspace for lm_head_packed / lora_gemm on an M x N output
+    with a (first) K segment of K, or None when the K split does not apply."""
+    n = lib().isd_gemm_workspace_bytes(M, K, N)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    return _ptr(ws), ws.numel()
+
+
+def lm_head_packed(h, wt, out=None, workspace=None):
+    """logits [M, N] = h [M, K] @ wt [N, K]^T (bf16, fp32 accumulation on MFMA).
+    `workspace` (from gemm_workspace) lets the GEMM halve its last partial round
+    along K."""
     if h.dtype != torch.bfloat16 or wt.dtype != torch.bfloat16:
         raise ValueError("lm_head_packed takes bf16 tensors")
     if not (h.is_contiguous() and wt.is_contiguous()):
@@ -462,7 +481,7 @@ def lm_head_packed(h, wt, out=None):
         raise ValueError("inner dimensions differ")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=h.device)
-    _check(lib().isd_lm_head_packed(_ptr(h), _ptr(wt), M, K, N, _ptr(out), None, 0, _stream()))
+    _check(lib().isd_lm_head_packed(_ptr(h), _ptr(wt), M, K, N, _ptr(out), *_ws(workspace), _stream()))
     return out
 
 
@@ -512,8 +531,10 @@ def lora_pack(w: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
 
 
 def lora_gemm(x: torch.Tensor, a: torch.Tensor, wcat: torch.Tensor, mask=None, *, out=None,
-              t=None):
-    """h = x W^T + [mask] (x A^T) B^T with wcat = lora_pack(W, B); returns (h, t)."""
+              t=None, workspace=None):
+    """h = x W^T + [mask] (x A^T) B^T with wcat = lora_pack(W, B); returns (h, t).
+    `workspace` (from gemm_workspace(M, K, N)) lets the GEMM halve its last
+    partial round along K."""
     for name, v in (("x", x), ("a", a), ("wcat", wcat)):
         if v.dtype != torch.bfloat16 or not v.is_contiguous():
             raise ValueError(f"{name} must be contiguous bf16")
@@ -527,7 +548,7 @@ def lora_gemm(x: torch.Tensor, a: torch.Tensor, wcat: torch.Tensor, mask=None, *
     out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
     t = torch.empty((M, r), dtype=torch.bfloat16, device=x.device) if t is None else t
     _check(lib().isd_lora_gemm(_ptr(x), _ptr(a), _ptr(wcat), _ptr(mask), M, K, N, r, _ptr(t),
-                               _ptr(out), _stream()))
+                               _ptr(out), *_ws(workspace), _stream()))
     return out, t
 
 

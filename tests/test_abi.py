@@ -124,6 +124,36 @@ def test_propose_alpha_step_validation(isd):
     assert "qnext_logits" in lib.isd_last_error().decode()
 
 
+def test_gemm_workspace_bytes(isd):
+    """The K split of the ping-pong GEMM's last partial round (256 CUs): it
+    applies when the 256 x 256 tiles past the whole rounds fill at most half a
+    round and number a multiple of 4; the workspace holds a 128-byte counter
+    and two fp32 256 x 256 halves per split tile."""
+    f = isd.lib().isd_gemm_workspace_bytes
+    per_tile = 128 + 2 * 256 * 256 * 4
+    assert f(1024, 4096, 24576) == 128 * per_tile     # 384 tiles: 256 whole, 128 split
+    assert f(1000, 256, 24389) == 128 * per_tile      # ragged rows and columns, same tiles
+    assert f(1024, 4096, 151936) == 72 * per_tile     # 2376 tiles: 72 past nine rounds
+    assert f(1024, 4096, 16384) == 0                  # exactly one round
+    assert f(1024, 4096, 16640) == 4 * per_tile       # 260 tiles
+    assert f(1024, 4096, 16448) == 4 * per_tile       # 260 tiles, the last one ragged
+    assert f(1024, 4096, 8192) == 0                   # fewer tiles than CUs
+    assert f(768, 4096, 22016) == 0                   # 258 tiles: 2 past the round
+    assert f(1024, 4096, 26624) == 0                  # 416 tiles: 160 past, over half a round
+    assert f(1024, 64, 24576) == 0                    # one K step cannot be halved
+    assert f(0, 4096, 24576) == 0 and f(1024, 100, 24576) == 0
+
+
+def test_gemm_workspace_alignment_is_checked(isd):
+    lib = isd.lib()
+    odd = ctypes.c_void_p(0x10080)                    # 128-byte, not 256-byte, aligned
+    assert lib.isd_lm_head_packed(FAKE, FAKE, 1024, 4096, 24576, FAKE, odd, 1 << 30, None) == 1
+    assert "workspace" in lib.isd_last_error().decode()
+    assert lib.isd_lora_gemm(FAKE, FAKE, FAKE, None, 1024, 4096, 24576, 128, FAKE, FAKE, odd, 1 << 30,
+                             None) == 1
+    assert "workspace" in lib.isd_last_error().decode()
+
+
 def test_lm_head_validation(isd):
     lib = isd.lib()
     assert lib.isd_lm_head(FAKE, FAKE, 16, 100, 64, FAKE, None, 0, None) == 1

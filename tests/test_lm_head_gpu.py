@@ -152,3 +152,44 @@ def test_lm_head_packed_tile_width_threshold(isd, M, N):
         assert np.array_equal(gp, gu), "packed and unpacked heads differ"
     log(f"lm_head_packed M={M} K={K} N={N}: worst err/bound {worst:.3f}, "
         f"exact-rounded fraction {frac:.5f}" + (", equal to the unpacked kernel" if N % 8 == 0 else ""))
+
+
+@pytest.mark.parametrize("M,K,N", [(1024, 512, 24576), (1000, 256, 24389), (1024, 256, 16640)])
+def test_lm_head_packed_k_split(isd, M, K, N):
+    """With a workspace, the 256 x 256 tiles past the whole rounds over the CUs
+    are computed as two halves along K that meet in it: 128 of 384 tiles, 128
+    of 384 with ragged rows and columns, 4 of 260.  Sampled rows (all columns,
+    so every split tile is checked) hold the oracle's bound; the tiles of the
+    whole rounds equal the call without a workspace bit for bit; a second call
+    on the same workspace repeats the bits and leaves its counters zero."""
+    import torch
+    rng = np.random.default_rng(N + K)
+    h_bits = f32_to_bf16_bits(rng.normal(0, 1, (M, K)).astype(np.float32))
+    w_bits = f32_to_bf16_bits(rng.normal(0, 0.02, (K, N)).astype(np.float32))
+    h_dev = _dev_bf16(h_bits)
+    wt = isd.lm_head_pack(_dev_bf16(w_bits))
+    ws = isd.gemm_workspace(M, K, N)
+    assert ws is not None
+    per_tile = 128 + 2 * 256 * 256 * 4
+    n_split = ws.numel() // per_tile
+    assert ws.numel() == n_split * per_tile and n_split > 0
+    plain = isd.lm_head_packed(h_dev, wt)
+    split = isd.lm_head_packed(h_dev, wt, workspace=ws)
+    again = isd.lm_head_packed(h_dev, wt, workspace=ws)
+    torch.cuda.synchronize()
+    gp = plain.view(torch.int16).cpu().numpy().view(np.uint16)
+    gs = split.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(gs, again.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert int(ws[: n_split * 128].view(torch.int32).abs().sum()) == 0, "counters not returned to zero"
+    m_tiles = (M + 255) // 256
+    n_tiles = (N + 255) // 256
+    n_full = m_tiles * n_tiles - n_split
+    tile = (np.arange(M)[:, None] // 256) + (np.arange(N)[None, :] // 256) * m_tiles
+    whole = tile < n_full
+    assert np.array_equal(gs[whole], gp[whole]), "tiles of the whole rounds changed"
+    rows = np.array([0, 1, 255, 256, 511, 767, M - 2, M - 1])
+    worst, frac = _check(gs, h_bits, w_bits, rows)
+    differ = int(np.sum(gs[~whole] != gp[~whole]))
+    log(f"lm_head_packed K split M={M} K={K} N={N}: {n_split} split tiles, worst err/bound "
+        f"{worst:.3f}, exact-rounded fraction {frac:.5f}, {differ} of {int((~whole).sum())} split "
+        f"outputs differ from the unsplit call")

@@ -118,20 +118,24 @@ def test_lora_split_shrink_ragged(isd):
     log(f"lora split shrink: worst h err/bound {worst:.3f}, t err/bound {t_worst:.3f}")
 
 
-def test_lora_wide_tiles_ragged(isd):
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "k-split"])
+def test_lora_wide_tiles_ragged(isd, split):
     """At least one 256 x 256 output tile per CU (4 x 65 here) takes the
     ping-pong kernel with its second K segment: 1000 rows (a ragged last row
-    tile), N = 16389 (a ragged, odd last column tile), K = 256, r = 128.
+    tile), N = 16389 (a ragged, odd last column tile), K = 256, r = 128; with
+    a workspace, the 4 tiles past the first round are halved along K.
     Sampled rows meet the bound, and every clean row equals the base
-    projection bit for bit."""
+    projection (given the same workspace) bit for bit."""
     import torch
     cfg = dict(LORA_CONFIGS["mid"], C=100, L=10, N=16389, K=256, r=128)
     d = gen_lora(cfg, seed=7)
     mask = d["mask"]
     x, a = _dev(d["x"]), _dev(d["a"])
     wcat = isd.lora_pack(_dev(d["w"]), _dev(d["b"]))
-    h, t = isd.lora_gemm(x, a, wcat, torch.from_numpy(mask).cuda())
-    base = isd.lm_head_packed(x, _dev(d["w"]))
+    ws = isd.gemm_workspace(x.shape[0], cfg["K"], cfg["N"]) if split else None
+    assert (ws is not None) == split
+    h, t = isd.lora_gemm(x, a, wcat, torch.from_numpy(mask).cuda(), workspace=ws)
+    base = isd.lm_head_packed(x, _dev(d["w"]), workspace=ws)
     torch.cuda.synchronize()
     hb, tb = _host(h), _host(t)
     rows = np.unique(np.concatenate([np.arange(0, 1000, 37), [255, 256, 511, 512, 767, 768, 998, 999]]))
@@ -139,7 +143,7 @@ def test_lora_wide_tiles_ragged(isd):
     clean = mask == 0
     assert clean.any() and (~clean).any()
     np.testing.assert_array_equal(hb[clean], _host(base)[clean])
-    log(f"lora wide tiles 1000 x 256 x 16389: worst h err/bound {worst:.3f}, "
+    log(f"lora wide tiles 1000 x 256 x 16389 (split {split}): worst h err/bound {worst:.3f}, "
         f"t err/bound {t_worst:.3f}, {int(clean.sum())} clean rows equal the base projection")
 
 
@@ -147,7 +151,8 @@ def test_lora_full_shape_sampled_rows(isd):
     """The MLP gate/up projection of an 8B model at the serving batch:
     M = 1024, K = 4096, N = 24576, r = 128; every adapter activation, the
     full output rows of a clean and a mask position of several sequences,
-    and every clean row against the base projection, bit for bit."""
+    and every clean row against the base projection, bit for bit; then the
+    same with the K-split workspace."""
     import torch
     cfg = LORA_CONFIGS["mlp_up"]
     d = gen_lora(cfg, seed=0)
@@ -160,6 +165,17 @@ def test_lora_full_shape_sampled_rows(isd):
     hb, tb = _host(h), _host(t)
     clean = mask == 0
     np.testing.assert_array_equal(hb[clean], _host(base)[clean])
+    # the same with a workspace: the 128 tiles past the first round (columns
+    # 16384 on) are halved along K; the others keep their bits
+    ws = isd.gemm_workspace(*d["x"].shape, cfg["N"])
+    hs, ts = isd.lora_gemm(x, a, wcat, torch.from_numpy(mask).cuda(), workspace=ws)
+    bs = isd.lm_head_packed(x, _dev(d["w"]), workspace=ws)
+    torch.cuda.synchronize()
+    hsb = _host(hs)
+    np.testing.assert_array_equal(_host(ts), tb)
+    np.testing.assert_array_equal(hsb[clean], _host(bs)[clean])
+    np.testing.assert_array_equal(hsb[:, :16384], hb[:, :16384])
+    split_worst, _ = _check(d, hsb, tb, np.array([3, 12, 700, 1019]), mask)
     rows = np.array([0, 7, 8, 15, 500, 511, 1016, 1023])
     worst, t_worst = _check(d, hb, tb, rows, mask)
     # all adapter activations
@@ -171,4 +187,5 @@ def test_lora_full_shape_sampled_rows(isd):
     bound = _half_ulp(xa) + cfg["K"] * 2.0 ** -24 * (np.abs(_f64(d["x"])) @ np.abs(_f64(d["a"])).T)
     assert np.max((np.abs(tg - xa) / bound)[gate[:, 0]]) <= 1.0
     log(f"lora full shape rows {rows.tolist()}: worst h err/bound {worst:.3f}, "
-        f"t err/bound {t_worst:.3f} ({all_rows.size} rows of t checked)")
+        f"t err/bound {t_worst:.3f} ({all_rows.size} rows of t checked); with the K split "
+        f"{split_worst:.3f}")
