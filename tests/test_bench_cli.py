@@ -34,3 +34,16 @@ def test_traffic_record_fields():
         tr["write_kib_per_dispatch"] * 1024 * tr["write_scale"]
     assert abs(b - tr["bytes_per_launch"]) <= 1024
     assert tr["bytes_per_launch"] >= tr["algorithmic_bytes_per_launch"]
+
+
+def test_counter_records_match_the_kernel_sources():
+    """bench.py reports counter-derived traffic only while the sources a record
+    was taken from are unchanged; both committed records must be current."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    with open(b.TRAFFIC_FILE) as f:
+        assert json.load(f)["kernel_digest"] == b.kernel_digest()
+    with open(b.HEAD_TRAFFIC_FILE) as f:
+        assert json.load(f)["kernel_digest"] == b.kernel_digest(b.HEAD_SOURCES)
