@@ -22,8 +22,8 @@ Reported:
              (the tiny workload reports microseconds per step instead)
   roofline   the step kernel against the HBM peak: algorithmic bytes per
              launch (every logit read once: 3*C*L*V*2 B) over the kernel's
-             average duration (two events on its stream around the K
-             back-to-back launches); `traffic` is the HBM bytes per launch
+             average duration (events on its stream around launches 2..K,
+             which run back to back); `traffic` is the HBM bytes per launch
              from rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated on a plain copy,
              when profiles/ holds counters for the current kernel source
   read_probe the probe's read rate and the step's fraction of it
@@ -532,33 +532,46 @@ def step_workload(args):
         call.bind_out(o)
         tails.append(call._tail)
 
+    # every step's input views, made before any timing: binding a step then
+    # only swaps pointers
+    step_inputs = [(dev_sets[i % nsets]["p"], dev_sets[i % nsets]["q"], dev_sets[i % nsets]["x"],
+                    uni[i, 0], uni[i, 1], dev_sets[i % nsets]["qn"], uni[i, 2]) for i in range(total)]
+
     def bind(i):
-        t = dev_sets[i % nsets]
-        call.bind(t["p"], t["q"], t["x"], uni[i, 0], uni[i, 1], t["qn"], uni[i, 2])
+        call.bind(*step_inputs[i])
 
     stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
     call.bind_out(outputs())
     for i in range(args.warmup):
         bind(i)
-        call()
+        call(sh)
     torch.cuda.synchronize()
     isd.check_device_error(call.ws)
 
-    # two events on the launch stream bracket the K back-to-back launches
+    # Events on the launch stream time the launches back to back.  The first
+    # event follows the first launch: an event recorded before it would fire
+    # at once and count the host's time to issue that launch as kernel time
+    # (about 25 us, a microsecond per step over 20 steps).  So the kernel
+    # average spans launches 2..K; the wall clock spans all K.
+    ev_first = torch.cuda.Event(enable_timing=True)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
+    ev_first.record(stream)
     for n in range(args.steps):
         bind(args.warmup + n)
         call._tail = tails[n]
-        call()
+        call(sh)
+        if n == 0:
+            ev0.record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     isd.check_device_error(call.ws)
-    kernel_avg_ms = ev0.elapsed_time(ev1) / args.steps
+    kernel_avg_ms = (ev0.elapsed_time(ev1) / (args.steps - 1) if args.steps > 1
+                     else ev_first.elapsed_time(ev1))
 
     gpu = {k: np.stack([o[k].cpu().numpy() for o in timed_out]) for k in timed_out[0]}
     ms_per_step = wall * 1e3 / args.steps
