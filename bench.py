@@ -297,7 +297,7 @@ def lm_head_workload(args):
     nt = (V + isd.isd.STATS_TILE - 1) // isd.isd.STATS_TILE
     stats = [torch.empty((M, nt, 2), dtype=torch.float32, device=dev) for _ in range(2)]
     xs = [torch.zeros((C, L), dtype=torch.int32, device=dev) for _ in range(2)]
-    # the plain GEMM's workspace: the tiles of its last partial round are halved along K
+    # the GEMM's workspace: the tiles of its last partial round are halved along K
     gws = isd.gemm_workspace(M, H, V)
     torch.cuda.synchronize()
     print(f"# W [{H}, {V}] and hidden states ready, {time.perf_counter() - t_gen:.1f} s",
@@ -313,7 +313,7 @@ def lm_head_workload(args):
 
     def head(h, i):
         if args.fused:
-            isd.lm_head_stats(h, Wt, T, out=logits[i % 2], stats=stats[i % 2])
+            isd.lm_head_stats(h, Wt, T, out=logits[i % 2], stats=stats[i % 2], workspace=gws)
         else:
             isd.lm_head_packed(h, Wt, out=logits[i % 2], workspace=gws)
 
@@ -374,7 +374,7 @@ def lm_head_workload(args):
         config=dict(workload=f"LM head + ISD step: h [{M}, {H}] x W [{H}, {V}] bf16, then "
                              f"C={C}, L={L} verify/propose", C=C, L=L, V=V, H=H,
                     head_layout="W packed once (untimed) to k-contiguous [V, H]",
-                    k_split_workspace_bytes=0 if (args.fused or gws is None) else gws.numel(),
+                    k_split_workspace_bytes=0 if gws is None else gws.numel(),
                     step_input="LM-head tile statistics" if args.fused else "logits"),
         roofline=dict(bound="mfma", achieved=round(gemm_tflops, 1), peak=2500.0,
                       unit="TFLOP/s", frac=round(gemm_tflops / 2500.0, 4),

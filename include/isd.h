@@ -367,9 +367,12 @@ isd_status_t isd_set_tuning(int32_t segments, int32_t propose_segments, int32_t 
  * integer (fp32), -inf for a tile past N.  stats: fp32, 8-byte aligned,
  * M * ceil(N / 128) * 2 values.  An extend forward's rows (per sequence L
  * anchor rows then L mask rows) give both the p and the qn statistics of a
- * step; the q statistics are the previous step's qn statistics. */
+ * step; the q statistics are the previous step's qn statistics.  workspace,
+ * ws_bytes: optional, as for isd_lm_head_packed (the same K split, so the
+ * logits equal isd_lm_head_packed's given a workspace too). */
 isd_status_t isd_lm_head_stats(const void *h, const void *wt, int32_t M, int32_t K, int32_t N,
-                               float temperature, void *logits, float *stats, void *stream);
+                               float temperature, void *logits, float *stats, void *workspace,
+                               size_t ws_bytes, void *stream);
 
 /* isd_step fed by those statistics (sample mode, no top-k): the softmax
  * denominators and the proposal draws come from the tile partials, and the

@@ -573,11 +573,13 @@ isd_status_t isd_step_fused(const isd_shape_t *s, const void *p_logits, const vo
 }
 
 isd_status_t isd_lm_head_stats(const void *h, const void *wt, int32_t M, int32_t K, int32_t N,
-                               float temperature, void *logits, float *stats, void *stream) {
+                               float temperature, void *logits, float *stats, void *workspace,
+                               size_t ws_bytes, void *stream) {
     ISD_TRY(check_ptr(h, "h", 16));
     ISD_TRY(check_ptr(wt, "wt", 16));
     ISD_TRY(check_ptr(logits, "logits", 2));
     ISD_TRY(check_ptr(stats, "stats", 8));
+    if (workspace) ISD_TRY(check_ptr(workspace, "workspace", 256));
     if (M < 1 || N < 1 || K < 1) return fail(ISD_ERR_ARG, "M, K, N must be >= 1");
     if (K % 64) return fail(ISD_ERR_ARG, "K must be a multiple of 64 (got %d)", (int)K);
     if (!(isfinite(temperature) && temperature > 0.0f))
@@ -585,8 +587,8 @@ isd_status_t isd_lm_head_stats(const void *h, const void *wt, int32_t M, int32_t
     const float k2 = (float)(1.4426950408889634 / (double)temperature);
     const hipError_t e = launch_lm_head_stats(static_cast<const uint16_t *>(h),
                                               static_cast<const uint16_t *>(wt), M, K, N, k2,
-                                              static_cast<uint16_t *>(logits), stats,
-                                              (hipStream_t)stream);
+                                              static_cast<uint16_t *>(logits), stats, workspace,
+                                              workspace ? ws_bytes : 0, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "lm_head launch failed: %s", hipGetErrorString(e));
     return ISD_OK;
 }

@@ -193,7 +193,8 @@ hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStre
 // partials (ref, sum) of its bf16 logits; k2 = log2(e) / T.
 constexpr int kStatsTile = 128;
 hipError_t launch_lm_head_stats(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
-                                float k2, uint16_t *out, float *stats, hipStream_t stream);
+                                float k2, uint16_t *out, float *stats, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 // Segment-gated LoRA projection: t = gate * (x a^T), then out = (x | t) wcat^T
 // with wcat = (w | b) [N, K + r].

@@ -359,15 +359,15 @@ __device__ __forceinline__ float row16_sum(float v) {
 // With SEG2 the A operand has a second K segment, as in the 128-wide kernel:
 // columns [K, K + K2) come from h2 [M, K2], and wt is [N, K + K2].
 //
-// With SPLIT the tiles past the last whole round over the CUs are cut in two
+// With SPLIT (with or without STATS) the tiles past the last whole round over the CUs are cut in two
 // along K, so that the last round is half as long: workgroups 0 .. n_full - 1
 // take whole tiles n_full .. (the first n_full), the rest take the K steps
 // [0, ks) or [ks, n) of one remaining tile.  Each half stores its fp32 tile
 // in the workspace (agent-scope atomic stores, coherent across the XCDs) and
 // counts itself on the tile's counter; the second to arrive adds the other
 // half's tile to its own (fp32 addition is commutative, so the result does
-// not depend on which half comes last), stores the output and resets the
-// counter.  No half waits for the other.
+// not depend on which half comes last), stores the output (and, with STATS,
+// its partials) and resets the counter.  No half waits for the other.
 struct SplitArgs {
     int n_full;                // whole tiles (a multiple of 8)
     int ks;                    // K steps of the first half
@@ -553,7 +553,9 @@ __global__ __launch_bounds__(512) void lm_head_pp_kernel(const uint16_t *__restr
                 *flag = prev;
             }
             __syncthreads();
-            if (*flag != 1) return;            // the first half: the other one finishes the tile
+            const uint32_t arrived = *flag;
+            __syncthreads();                   // every wavefront has the word before LDS is reused
+            if (arrived != 1) return;          // the first half: the other one finishes the tile
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
@@ -975,8 +977,15 @@ hipError_t launch_pack_wt(const uint16_t *w, uint16_t *wt, int K, int N, hipStre
 }
 
 hipError_t launch_lm_head_stats(const uint16_t *h, const uint16_t *wt, int M, int K, int N,
-                                float k2, uint16_t *out, float *stats, hipStream_t stream) {
-    return launch_pp<true, false>(h, K, nullptr, 0, wt, M, N, out, k2, stats, stream);
+                                float k2, uint16_t *out, float *stats, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    const SplitPlan p = split_plan(M, K, N);
+    if (p.n_split == 0 || ws == nullptr || ws_bytes < p.bytes)
+        return launch_pp<true, false>(h, K, nullptr, 0, wt, M, N, out, k2, stats, stream);
+    uint32_t *cnt = static_cast<uint32_t *>(ws);
+    float *part = reinterpret_cast<float *>(cnt + (size_t)p.n_split * kCounterStride);
+    return launch_pp<true, false, true>(h, K, nullptr, 0, wt, M, N, out, k2, stats, stream,
+                                        SplitArgs{p.n_full, p.ks, part, cnt}, p.n_split);
 }
 
 }  // namespace isd

@@ -59,7 +59,8 @@ _SIGS = {
     "isd_set_tuning": (ctypes.c_int, [_i32, _i32, _i32, _i64]),
     "isd_set_trunc_tuning": (ctypes.c_int, [_i32]),
     "isd_lora_pack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
-    "isd_lm_head_stats": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp, _vp]),
+    "isd_lm_head_stats": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp, _vp,
+                                         _sz, _vp]),
     "isd_step_fused": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 10 + [_i64, _i64] +
                        [_vp] * 8 + [_vp, _sz, _vp]),
     "isd_lora_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
@@ -555,9 +556,10 @@ def lora_gemm(x: torch.Tensor, a: torch.Tensor, wcat: torch.Tensor, mask=None, *
 STATS_TILE = 128
 
 
-def lm_head_stats(h, wt, temperature=1.0, out=None, stats=None):
+def lm_head_stats(h, wt, temperature=1.0, out=None, stats=None, workspace=None):
     """logits [M, N] = h @ wt^T like lm_head_packed, plus the softmax partials
-    of every (row, 128-column tile): stats [M, ceil(N / 128), 2] fp32 (e, s)."""
+    of every (row, 128-column tile): stats [M, ceil(N / 128), 2] fp32 (e, s).
+    `workspace` (from gemm_workspace) as for lm_head_packed."""
     if h.dtype != torch.bfloat16 or wt.dtype != torch.bfloat16:
         raise ValueError("lm_head_stats takes bf16 tensors")
     if not (h.is_contiguous() and wt.is_contiguous()):
@@ -570,7 +572,7 @@ def lm_head_stats(h, wt, temperature=1.0, out=None, stats=None):
     out = torch.empty((M, N), dtype=torch.bfloat16, device=h.device) if out is None else out
     stats = torch.empty((M, nt, 2), dtype=torch.float32, device=h.device) if stats is None else stats
     _check(lib().isd_lm_head_stats(_ptr(h), _ptr(wt), M, K, N, float(temperature), _ptr(out),
-                                   _ptr(stats), _stream()))
+                                   _ptr(stats), *_ws(workspace), _stream()))
     return out, stats
 
 

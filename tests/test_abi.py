@@ -275,9 +275,15 @@ def test_fused_and_stats_validation(isd):
     trunc = _shape(isd)
     trunc.top_k = 8
     assert lib.isd_step_fused(ctypes.byref(trunc), *args) == 2
-    assert lib.isd_lm_head_stats(FAKE, FAKE, 8, 100, 64, ctypes.c_float(1.0), FAKE, FAKE, None) == 1
-    assert lib.isd_lm_head_stats(FAKE, FAKE, 8, 128, 64, ctypes.c_float(0.0), FAKE, FAKE, None) == 1
+    assert lib.isd_lm_head_stats(FAKE, FAKE, 8, 100, 64, ctypes.c_float(1.0), FAKE, FAKE, None, 0,
+                                 None) == 1
+    assert lib.isd_lm_head_stats(FAKE, FAKE, 8, 128, 64, ctypes.c_float(0.0), FAKE, FAKE, None, 0,
+                                 None) == 1
     assert "temperature" in lib.isd_last_error().decode()
+    odd = ctypes.c_void_p(0x10080)
+    assert lib.isd_lm_head_stats(FAKE, FAKE, 1024, 4096, 24576, ctypes.c_float(1.0), FAKE, FAKE, odd,
+                                 1 << 30, None) == 1
+    assert "workspace" in lib.isd_last_error().decode()
 
 
 @pytest.mark.parametrize("nbytes,tpg,msg", [

@@ -177,3 +177,33 @@ def test_fused_step_variants(isd, variant):
     Gumbel-max correction on the statistics path."""
     fused, plain, ref, st, _ = _run(isd, 4, 8, 256, 20000, 1.0, seed=9, **variant)
     log(f"fused {variant}: {st}")
+
+
+@pytest.mark.parametrize("M,N", [(1000, 16389), (1024, 24576)])
+def test_stats_k_split(isd, M, N):
+    """The statistics GEMM with the GEMM workspace: the 256 x 256 tiles past the
+    whole rounds over the CUs (4 of 260 with ragged rows and columns, 128 of 384)
+    run as two halves of K, and the second half to arrive writes the logits and
+    the partials.  The logits equal the exact product's bf16 bits and the packed
+    head's with the same workspace, every partial matches the fp64 definition,
+    a second call repeats the bits, and the counters return to zero."""
+    import torch
+    K = 256
+    d = gen_exact_head(M, K, N, seed=23)
+    h, wt = _dev(d["h"]), _dev(d["wt"])
+    ws = isd.gemm_workspace(M, K, N)
+    assert ws is not None
+    logits, stats = isd.lm_head_stats(h, wt, 0.8, workspace=ws)
+    logits2, stats2 = isd.lm_head_stats(h, wt, 0.8, workspace=ws)
+    base = isd.lm_head_packed(h, wt, workspace=ws)
+    torch.cuda.synchronize()
+    per_tile = 128 + 2 * 256 * 256 * 4
+    n_split = ws.numel() // per_tile
+    assert int(ws[: n_split * 128].view(torch.int32).abs().sum()) == 0, "counters not returned to zero"
+    assert np.array_equal(_bits(logits), _bits(logits2))
+    assert torch.equal(stats, stats2)
+    assert np.array_equal(_bits(logits), _bits(base)), "statistics epilogue changed the logits"
+    assert np.array_equal(_bits(logits), _oracle_logits(d["h"], d["wt"], np.arange(M)))
+    _check_stats(_bits(logits), stats.cpu().numpy(), 0.8)
+    log(f"statistics GEMM with K split M={M} N={N}: {n_split} split tiles, logits exact, "
+        f"{stats.shape[1]} tiles per row checked")
