@@ -233,9 +233,13 @@ isd_status_t run(const isd_shape_t *s, const Plan &plan, StepArgs a, void *works
 
     const bool vec = vec_ok(s, a.p, a.q, a.qn);
     hipError_t e = hipSuccess;
-    if (plan.fused) e = launch_fused_decide(a, s->dtype, (hipStream_t)stream);
+    // the statistics path: decisions (and proposals, in the same launch when
+    // it fits) before the residual items, which read the decisions
+    const bool front = plan.fused && fused_front_fits(a);
+    if (front) e = launch_fused_front(a, s->dtype, (hipStream_t)stream);
+    else if (plan.fused) e = launch_fused_decide(a, s->dtype, (hipStream_t)stream);
     if (e == hipSuccess) e = launch_step(a, s->dtype, s->mode, vec, (hipStream_t)stream);
-    if (e == hipSuccess && plan.fused) e = launch_fused_propose(a, s->dtype, (hipStream_t)stream);
+    if (e == hipSuccess && plan.fused && !front) e = launch_fused_propose(a, s->dtype, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ISD_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ISD_OK;
 }

@@ -117,16 +117,14 @@ __device__ __forceinline__ long long fused_row_offset(const StepArgs &a, int c, 
 
 constexpr int kDecideWaves = 16;
 
-template <typename T>
-__global__ __launch_bounds__(kDecideWaves * kWave) void fused_decide_kernel(StepArgs a) {
-    __shared__ float s_c[2][kMaxL];
-    __shared__ double s_s[2][kMaxL];
-    const int c = blockIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+// Sequence c's decision, by a whole workgroup of NW wavefronts.
+template <typename T, int NW>
+__device__ __forceinline__ void decide_seq(const StepArgs &a, int c, int wave, int lane,
+                                           float (&s_c)[2][kMaxL], double (&s_s)[2][kMaxL]) {
     const int L = a.L;
     // one wavefront per row: p rows (which = 0), then q rows (which = 1)
     const int rows = a.q_onehot ? L : 2 * L;
-    for (int rr = wave; rr < rows; rr += kDecideWaves) {
+    for (int rr = wave; rr < rows; rr += NW) {
         const int which = rr / L, k = rr - which * L;
         float cr;
         double sr;
@@ -193,17 +191,13 @@ __global__ __launch_bounds__(kDecideWaves * kWave) void fused_decide_kernel(Step
 // Proposals
 // ---------------------------------------------------------------------------
 
+// The proposal of mask row rowid = c * L + k, by one wavefront; part: its
+// chunk of LDS, where partials are re-laid out for contiguous runs.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void fused_propose_kernel(StepArgs a) {
-    // per wavefront, one chunk of partials re-laid out for contiguous runs
-    __shared__ uint64_t s_part[kWavesPerGroup][kChunk];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int rowid = blockIdx.x * kWavesPerGroup + wave;   // c * L + k
-    if (rowid >= a.C * a.L) return;
+__device__ __forceinline__ void propose_row(const StepArgs &a, int rowid, uint64_t *part, int lane) {
     const int c = rowid / a.L, k = rowid - c * a.L;
     const float *st = row_stats(a.qn_stats, a, c, k);
     const int n = a.n_stiles;
-    uint64_t *part = s_part[wave];
     Chunk ch;
     load_chunk(st, n, 0, lane, ch);
     float cr;
@@ -324,7 +318,63 @@ __global__ __launch_bounds__(kThreads) void fused_propose_kernel(StepArgs a) {
     }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kDecideWaves * kWave) void fused_decide_kernel(StepArgs a) {
+    __shared__ float s_c[2][kMaxL];
+    __shared__ double s_s[2][kMaxL];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    decide_seq<T, kDecideWaves>(a, blockIdx.x, wave, lane, s_c, s_s);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fused_propose_kernel(StepArgs a) {
+    __shared__ uint64_t s_part[kWavesPerGroup][kChunk];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int rowid = blockIdx.x * kWavesPerGroup + wave;   // c * L + k
+    if (rowid >= a.C * a.L) return;
+    propose_row<T>(a, rowid, s_part[wave], lane);
+}
+
+// Decisions and proposals in one launch: they read only the LM head's partials
+// and logits, never each other's results.  Workgroups of kFrontWaves
+// wavefronts (two per SIMD, so the proposal code keeps its registers):
+// workgroups 0 .. C - 1 decide a sequence each, the rest give each wavefront
+// one mask row.  Their LDS (96 KB) keeps one workgroup per CU, so the launch
+// is used when all its workgroups fit on the CUs at once.
+constexpr int kFrontWaves = 8;
+constexpr int kFrontMaxGroups = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kFrontWaves * kWave) void fused_front_kernel(StepArgs a) {
+    __shared__ float s_c[2][kMaxL];
+    __shared__ double s_s[2][kMaxL];
+    __shared__ uint64_t s_part[kFrontWaves][kChunk];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    if ((int)blockIdx.x < a.C) {
+        decide_seq<T, kFrontWaves>(a, blockIdx.x, wave, lane, s_c, s_s);
+        return;
+    }
+    const int rowid = ((int)blockIdx.x - a.C) * kFrontWaves + wave;
+    if (rowid >= a.C * a.L) return;
+    propose_row<T>(a, rowid, s_part[wave], lane);
+}
+
+int front_groups(const StepArgs &a) {
+    return a.C + (a.C * a.L + kFrontWaves - 1) / kFrontWaves;
+}
+
 }  // namespace
+
+bool fused_front_fits(const StepArgs &a) { return front_groups(a) <= kFrontMaxGroups; }
+
+hipError_t launch_fused_front(const StepArgs &a, int dtype, hipStream_t stream) {
+    const unsigned g = (unsigned)front_groups(a);
+    if (dtype == kBf16)
+        hipLaunchKernelGGL(fused_front_kernel<uint16_t>, dim3(g), dim3(kFrontWaves * kWave), 0, stream, a);
+    else
+        hipLaunchKernelGGL(fused_front_kernel<float>, dim3(g), dim3(kFrontWaves * kWave), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_fused_decide(const StepArgs &a, int dtype, hipStream_t stream) {
     if (dtype == kBf16)

@@ -168,6 +168,10 @@ hipError_t launch_step(const StepArgs &a, int dtype, int mode, bool vec, hipStre
 // residual items of launch_step), and the proposals (after it).
 hipError_t launch_fused_decide(const StepArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_fused_propose(const StepArgs &a, int dtype, hipStream_t stream);
+// Both in one launch (before the residual items), when its workgroups fit on
+// the CUs at once.
+bool fused_front_fits(const StepArgs &a);
+hipError_t launch_fused_front(const StepArgs &a, int dtype, hipStream_t stream);
 
 // Launches the truncated (top-k / top-p) step kernel for `a` (sample mode).
 hipError_t launch_trunc(const StepArgs &a, int dtype, bool vec, hipStream_t stream);

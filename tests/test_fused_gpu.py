@@ -170,6 +170,14 @@ def test_fused_step_serving_shape(isd):
     log(f"fused serving shape, all 64 sequences against the oracle: {st}")
 
 
+def test_fused_step_separate_launches(isd):
+    """C = 200, L = 8: the decisions and proposals take 200 + 200 workgroups, more
+    than fit on the CUs at once, so they run as two launches around the residual
+    items instead of one.  Every sequence against the oracle."""
+    fused, plain, ref, st, _ = _run(isd, 200, 8, 128, 3000, 0.9, seed=13)
+    log(f"fused C=200 (separate decision and proposal launches): {st}")
+
+
 @pytest.mark.parametrize("variant", [dict(sampler="gumbel"), dict(q_onehot=True, relax=0.5),
                                      dict(q_onehot=True, sampler="gumbel")])
 def test_fused_step_variants(isd, variant):
