@@ -359,9 +359,10 @@ __device__ __forceinline__ float row16_sum(float v) {
 // With SEG2 the A operand has a second K segment, as in the 128-wide kernel:
 // columns [K, K + K2) come from h2 [M, K2], and wt is [N, K + K2].
 //
-// With SPLIT (with or without STATS) the tiles past the last whole round over the CUs are cut in two
-// along K, so that the last round is half as long: workgroups 0 .. n_full - 1
-// take whole tiles n_full .. (the first n_full), the rest take the K steps
+// With SPLIT (with or without STATS) the tiles past the last whole round over
+// the CUs are cut in two along K, so that the last round is half as long:
+// workgroups 0 .. n_full - 1 take the whole tiles 0 .. n_full - 1 (in the same
+// XCD-aware order as without the split), and the rest take the K steps
 // [0, ks) or [ks, n) of one remaining tile.  Each half stores its fp32 tile
 // in the workspace (agent-scope atomic stores, coherent across the XCDs) and
 // counts itself on the tile's counter; the second to arrive adds the other
