@@ -17,8 +17,12 @@
 //           the 128-column tile where the running mass crosses u * S, read
 //           those 128 logits and finish the inverse-CDF draw there.
 //
-// So the step reads the residual rows and a few kilobytes per row instead of
-// all 3 * C * L rows of logits.
+// Decide and propose read only the partials and the logits, never each
+// other's results, so they share one launch ahead of the residual items when
+// its workgroups fit on the CUs at once (fused_front_kernel); otherwise decide
+// runs before the residual items and propose after them.  So the step reads
+// the residual rows and a few kilobytes per row instead of all 3 * C * L rows
+// of logits.
 
 #include "isd_device.h"
 #include "isd_internal.h"
