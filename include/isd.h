@@ -383,8 +383,9 @@ isd_status_t isd_lm_head_stats(const void *h, const void *wt, int32_t M, int32_t
  *   p_stats, q_stats, qn_stats  tile partials of rows (c, k) of p, q, qn at
  *     stats + 2 * (c * stats_ldc + k * stats_ld); stats_ld >= ceil(V / 128),
  *     stats_ldc = 0 means L * stats_ld.  q_stats may be NULL with q_onehot.
- * Three launches on `stream`.  Errors as isd_step, and ISD_ERR_UNSUPPORTED in
- * greedy mode or with top_k. */
+ * Two launches on `stream` (decisions and proposals, then the residual
+ * draws) when C + ceil(C * L / 8) <= 256, else three.  Errors as isd_step,
+ * and ISD_ERR_UNSUPPORTED in greedy mode or with top_k. */
 isd_status_t isd_step_fused(const isd_shape_t *s, const void *p_logits, const void *q_logits,
                             const int32_t *proposals, const float *u_accept, const float *u_resid,
                             const void *qnext_logits, const float *u_propose,
